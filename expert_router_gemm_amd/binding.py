@@ -1,0 +1,192 @@
+"""ctypes binding of libmoe (include/moe.h): argument marshalling only.
+
+Every function has the C name and argument order of the ABI; torch tensors
+are passed as device pointers, ``stream=None`` means torch's current stream.
+A non-OK status raises ``MoEError``.  The library must have been built
+(``python -m expert_router_gemm_amd.build``); there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_F16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F_SHARED = 1
+
+EXPORTED = (
+    "moe_route", "moe_dispatch", "moe_expert_ffn_up", "moe_expert_ffn_down",
+    "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_workspace_bytes",
+    "moe_status_str", "moe_version",
+)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_slots", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("dispatch", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+    def __repr__(self):
+        return "Shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class SlotMap(ctypes.Structure):
+    _fields_ = [("rep_off", ctypes.c_void_p), ("rep_slot", ctypes.c_void_p),
+                ("seed", ctypes.c_uint64)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_router", "bias", "w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"libmoe.so not found at {LIB_PATH}; build it with "
+                "`python -m expert_router_gemm_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_uint64
+        SP = ctypes.POINTER(Shape)
+        L.moe_route.argtypes = [SP, I32, P, P, P, P, P, P, P, P, SZ, P]
+        L.moe_dispatch.argtypes = [SP, I32, P, P, ctypes.POINTER(SlotMap), P, P, P, P, P, P, P, SZ, P]
+        L.moe_expert_ffn_up.argtypes = [SP, I32, I32, P, I32, P, I32, P, P, P, P, P]
+        L.moe_expert_ffn_down.argtypes = [SP, I32, I32, P, P, P, P, P]
+        L.moe_expert_ffn.argtypes = [SP, I32, I32, P, I32, P, I32, P, P, P, P, P, P, SZ, P]
+        L.moe_combine.argtypes = [SP, I32, P, P, P, P, P, P, P]
+        L.moe_layer_forward.argtypes = [SP, ctypes.POINTER(Weights), ctypes.POINTER(SlotMap),
+                                        I32, P, P, P, SZ, P]
+        L.moe_workspace_bytes.argtypes = [SP, I32]
+        L.moe_workspace_bytes.restype = SZ
+        L.moe_status_str.argtypes = [ctypes.c_int]
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_version.restype = ctypes.c_char_p
+        for fn in EXPORTED:
+            if fn not in ("moe_workspace_bytes", "moe_status_str", "moe_version"):
+                getattr(L, fn).restype = ctypes.c_int
+        _ = U64
+        _lib = L
+    return _lib
+
+
+def status_str(st: int) -> str:
+    return lib().moe_status_str(int(st)).decode()
+
+
+def version() -> str:
+    return lib().moe_version().decode()
+
+
+def _p(t) -> Optional[int]:
+    """Device pointer of a tensor (or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise MoEError(fn, st)
+
+
+def make_shape(*, hidden, inter, n_experts, top_k, n_slots, n_shared=0, act=MOE_F16,
+               dispatch=None, shared=False) -> Shape:
+    return Shape(hidden, inter, n_experts, top_k, n_slots, n_shared, act,
+                 act if dispatch is None else dispatch, MOE_F_SHARED if shared else 0)
+
+
+def moe_workspace_bytes(shape: Shape, T: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(shape), T))
+
+
+def moe_route(shape, T, h, w_router, bias, topk_idx, topk_w, shared_gate, logits, ws, stream=None):
+    _check("moe_route", lib().moe_route(
+        ctypes.byref(shape), T, _p(h), _p(w_router), _p(bias), _p(topk_idx), _p(topk_w),
+        _p(shared_gate), _p(logits), _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_dispatch(shape, T, h, topk_idx, slot_map: SlotMap, x_perm, x_scale, counts, offsets,
+                 perm_src, inv_pos, ws, stream=None):
+    _check("moe_dispatch", lib().moe_dispatch(
+        ctypes.byref(shape), T, _p(h), _p(topk_idx), ctypes.byref(slot_map), _p(x_perm),
+        _p(x_scale), _p(counts), _p(offsets), _p(perm_src), _p(inv_pos), _p(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def moe_expert_ffn_up(shape, n_groups, cap_rows, x, x_dtype, x_scale, x_broadcast, offsets,
+                      w_gate, w_up, hm, stream=None):
+    _check("moe_expert_ffn_up", lib().moe_expert_ffn_up(
+        ctypes.byref(shape), n_groups, cap_rows, _p(x), x_dtype, _p(x_scale), int(x_broadcast),
+        _p(offsets), _p(w_gate), _p(w_up), _p(hm), _stream(stream)))
+
+
+def moe_expert_ffn_down(shape, n_groups, cap_rows, hm, offsets, w_down, y, stream=None):
+    _check("moe_expert_ffn_down", lib().moe_expert_ffn_down(
+        ctypes.byref(shape), n_groups, cap_rows, _p(hm), _p(offsets), _p(w_down), _p(y),
+        _stream(stream)))
+
+
+def moe_expert_ffn(shape, n_groups, cap_rows, x, x_dtype, x_scale, x_broadcast, offsets,
+                   w_gate, w_up, w_down, y, ws, stream=None):
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        ctypes.byref(shape), n_groups, cap_rows, _p(x), x_dtype, _p(x_scale), int(x_broadcast),
+        _p(offsets), _p(w_gate), _p(w_up), _p(w_down), _p(y), _p(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def moe_combine(shape, T, y, inv_pos, topk_w, shared_y, shared_gate, out, stream=None):
+    _check("moe_combine", lib().moe_combine(
+        ctypes.byref(shape), T, _p(y), _p(inv_pos), _p(topk_w), _p(shared_y), _p(shared_gate),
+        _p(out), _stream(stream)))
+
+
+def moe_layer_forward(shape, weights: Weights, slot_map: SlotMap, T, h, out, ws, stream=None):
+    _check("moe_layer_forward", lib().moe_layer_forward(
+        ctypes.byref(shape), ctypes.byref(weights), ctypes.byref(slot_map), T, _p(h), _p(out),
+        _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def make_weights(*, w_router, bias=None, w_gate, w_up, w_down, sh_gate=None, sh_up=None,
+                 sh_down=None) -> Weights:
+    return Weights(*(_p(t) for t in (w_router, bias, w_gate, w_up, w_down, sh_gate, sh_up,
+                                     sh_down)))
+
+
+def make_slot_map(rep_off, rep_slot, seed: int) -> SlotMap:
+    return SlotMap(_p(rep_off), _p(rep_slot), seed)

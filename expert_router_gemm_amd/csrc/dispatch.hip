@@ -1,0 +1,227 @@
+// dispatch.hip -- Step 2 on one GPU: permute local (token, k) pairs into
+// per-slot contiguous groups, optionally quantising rows to OCP E4M3.
+//
+// The expert-parallelism blog page (section 2.2, Step 2) sends each token's
+// hidden row to the GPUs that own its experts; with one GPU holding this
+// rank's share, the send becomes a stable permutation: rows grouped by local
+// slot, token order inside a group, nothing dropped.  Slots come from the
+// contiguous placement of section 2.1 and, for redundant experts, a random
+// replica (section 6.3) chosen by a counter hash so the result is exact.
+// Section 2.3 notes FP8 halves the dispatched bytes: with x_dtype = FP8 each
+// row is stored as E4M3 codes with one fp32 scale.
+//
+// Three kernels, all deterministic (no order-dependent atomics):
+//  1. rank:    one wave per 64-token chunk.  Each (token, k) sets its lane bit
+//              in a per-slot 64-bit LDS mask (an OR, so arrival order cannot
+//              matter); the pair's rank inside the chunk is the popcount of
+//              the mask bits of lower lanes, the chunk's count the popcount.
+//  2. scan:    per slot, exclusive scan over chunks; then an exclusive scan
+//              over slots gives offsets.  chunk_counts becomes chunk_base.
+//  3. scatter: one wave per pair: row = chunk_base + rank; writes inv_pos,
+//              perm_src and copies (or quantises) the 14 KB hidden row with
+//              16-byte lane accesses.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// SplitMix64 output function (Steele, Lea and Flood, OOPSLA 2014).
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+    x += 0x9E3779B97F4A7C15ull;
+    x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+    x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+    return x ^ (x >> 31);
+}
+
+__device__ __forceinline__ int slot_of(const DispatchArgs &a, int t, int k) {
+    const int e = a.topk_idx[(size_t)t * a.K + k];
+    if (e < 0 || e >= a.E) return -1;
+    const int lo = a.rep_off[e];
+    const int n = a.rep_off[e + 1] - lo;
+    if (n <= 0) return -1;
+    int r = 0;
+    if (n > 1) r = (int)(splitmix64(a.seed ^ ((uint64_t)t * (uint64_t)a.K + (uint64_t)k)) % (uint64_t)n);
+    const int s = a.rep_slot[lo + r];
+    return (s >= 0 && s < a.S) ? s : -1;
+}
+
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchArgs a) {
+    extern __shared__ unsigned long long masks[];  // [4][S]
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const int chunk = blockIdx.x * 4 + wave;
+    const int C = (a.T + 63) / 64;
+    unsigned long long *m = masks + (size_t)wave * a.S;
+    for (int s = lane; s < a.S; s += 64) m[s] = 0ull;
+    __syncthreads();
+    const int t = chunk * 64 + lane;
+    const unsigned long long bit = 1ull << lane;
+    if (t < a.T)
+        for (int k = 0; k < a.K; ++k) {
+            const int s = slot_of(a, t, k);
+            if (s >= 0) atomicOr(&m[s], bit);
+        }
+    __syncthreads();
+    if (t < a.T)
+        for (int k = 0; k < a.K; ++k) {
+            const int s = slot_of(a, t, k);
+            int code = -1;
+            if (s >= 0) code = s * 64 + __popcll(m[s] & (bit - 1ull));
+            a.pair_code[(size_t)t * a.K + k] = code;
+        }
+    if (chunk < C)
+        for (int s = lane; s < a.S; s += 64) a.chunk_counts[(size_t)chunk * a.S + s] = __popcll(m[s]);
+}
+
+// Single block of 1024 threads; S <= 1024.
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(DispatchArgs a) {
+    __shared__ int buf[2][1024];
+    const int C = (a.T + 63) / 64;
+    const int s = threadIdx.x;
+    // 1. per slot: exclusive scan over chunks (in place) and the slot total
+    int tot = 0;
+    if (s < a.S) {
+        int c = 0;
+        for (; c + 8 <= C; c += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = a.chunk_counts[(size_t)(c + u) * a.S + s];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                a.chunk_counts[(size_t)(c + u) * a.S + s] = tot;
+                tot += v[u];
+            }
+        }
+        for (; c < C; ++c) {
+            const int v = a.chunk_counts[(size_t)c * a.S + s];
+            a.chunk_counts[(size_t)c * a.S + s] = tot;
+            tot += v;
+        }
+        a.counts[s] = tot;
+    }
+    // 2. exclusive scan of the totals over slots (Hillis-Steele in LDS)
+    int cur = 0;
+    buf[0][s] = tot;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int v = buf[cur][s] + (s >= o ? buf[cur][s - o] : 0);
+        buf[cur ^ 1][s] = v;
+        cur ^= 1;
+        __syncthreads();
+    }
+    const int incl = buf[cur][s];
+    if (s < a.S) {
+        const int off = incl - tot;
+        a.offsets[s] = off;
+        for (int c = 0; c < C; ++c) a.chunk_counts[(size_t)c * a.S + s] += off;
+        if (s == a.S - 1) a.offsets[a.S] = incl;
+    }
+}
+
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+    // |v| <= 448.  OCP E4M3: bias 7, 3 mantissa bits, subnormals below 2^-6.
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t sign = (b >> 24) & 0x80u;
+    const uint32_t a = b & 0x7fffffffu;
+    if (a < 0x3c800000u) {  // |v| < 2^-6: multiples of 2^-9, RNE
+        const float q = __uint_as_float(a) * 512.0f;
+        return sign | (uint32_t)__builtin_rintf(q);
+    }
+    // keep exponent and top 3 mantissa bits, round the low 20 bits to nearest even
+    uint32_t q = a >> 20;
+    const uint32_t rem = a & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) q += 1u;
+    return sign | (q - ((127u - 7u) << 3));
+}
+
+template <typename T, int XM>
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(DispatchArgs a) {
+    const size_t p = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (p >= (size_t)a.T * a.K) return;
+    const int lane = lane_id();
+    const int code = __builtin_amdgcn_readfirstlane(a.pair_code[p]);
+    if (code < 0) {
+        if (lane == 0) a.inv_pos[p] = -1;
+        return;
+    }
+    const int t = (int)(p / a.K);
+    const int s = code >> 6, rank = code & 63;
+    const int row = __builtin_amdgcn_readfirstlane(a.chunk_counts[(size_t)(t >> 6) * a.S + s] + rank);
+    if (lane == 0) {
+        a.inv_pos[p] = row;
+        a.perm_src[row] = (int32_t)p;
+    }
+    constexpr int EL = Frag<T>::kElems;
+    const T *src = reinterpret_cast<const T *>(a.h) + (size_t)t * a.H;
+    if (XM != DT_FP8) {
+        T *dst = reinterpret_cast<T *>(a.x_perm) + (size_t)row * a.H;
+        for (int i = lane * EL; i < a.H; i += 64 * EL)
+            *reinterpret_cast<typename Frag<T>::vec *>(dst + i) = load16(src + i);
+        return;
+    }
+    // FP8: per-row amax -> scale, then codes
+    float amax = 0.0f;
+    for (int i = lane * EL; i < a.H; i += 64 * EL) {
+        const typename Frag<T>::vec v = load16(src + i);
+#pragma unroll
+        for (int j = 0; j < EL; ++j) amax = fmaxf(amax, fabsf((float)v[j]));
+    }
+    amax = wave_max(amax);
+    uint8_t *dst = reinterpret_cast<uint8_t *>(a.x_perm) + (size_t)row * a.H;
+    if (amax == 0.0f) {
+        for (int i = lane * EL; i < a.H; i += 64 * EL)
+            *reinterpret_cast<u32x2 *>(dst + i) = u32x2{0u, 0u};
+        if (lane == 0) a.x_scale[row] = 0.0f;
+        return;
+    }
+    const float inv = __fdiv_rn(448.0f, amax);
+    if (lane == 0) a.x_scale[row] = __fdiv_rn(amax, 448.0f);
+    for (int i = lane * EL; i < a.H; i += 64 * EL) {
+        const typename Frag<T>::vec v = load16(src + i);
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < EL; ++j) {
+            float q = __fmul_rn((float)v[j], inv);
+            q = fminf(fmaxf(q, -448.0f), 448.0f);
+            w[j >> 2] |= e4m3_rne(q) << (8 * (j & 3));
+        }
+        *reinterpret_cast<u32x2 *>(dst + i) = u32x2{w[0], w[1]};
+    }
+}
+
+}  // namespace
+
+size_t dispatch_scratch_bytes(int T, int K, int S) {
+    const size_t C = (size_t)(T + 63) / 64;
+    size_t a = ((size_t)T * K * 4 + 255) & ~(size_t)255;
+    a += ((C * (size_t)S * 4) + 255) & ~(size_t)255;
+    return a;
+}
+
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
+    if (a.T < 0) return hipErrorInvalidValue;
+    const int C = (a.T + 63) / 64;
+    hipError_t e;
+    if (C > 0) {
+        hipLaunchKernelGGL(dispatch_rank_kernel, dim3((C + 3) / 4), dim3(256),
+                           (size_t)4 * a.S * sizeof(unsigned long long), s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // with T = 0 the scan alone writes all-zero counts and offsets
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.T == 0) return hipSuccess;
+    const size_t pairs = (size_t)a.T * a.K;
+    dim3 grid((unsigned)((pairs + 3) / 4));
+    if (a.dtype == DT_F32)
+        hipLaunchKernelGGL((dispatch_scatter_kernel<float, DT_F32>), grid, dim3(256), 0, s, a);
+    else if (a.x_dtype == DT_FP8)
+        hipLaunchKernelGGL((dispatch_scatter_kernel<f16, DT_FP8>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((dispatch_scatter_kernel<f16, DT_F16>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

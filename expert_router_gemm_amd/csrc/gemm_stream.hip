@@ -1,0 +1,219 @@
+// gemm_stream.hip -- grouped "weight-stream" GEMM on MFMA for small row counts.
+//
+// Serves the router linear (Step 1 of the expert-parallelism blog page,
+// section 2.2) and both halves of the SwiGLU expert FFN (Step 3) when each
+// group (expert slot) holds few rows, i.e. decode.  There the work is bound by
+// reading every touched weight byte once from HBM (the decode-is-memory-bound
+// analysis of the PPIO essay on EP), so the kernel streams weights straight
+// from HBM into registers and never stages them in LDS:
+//
+//   out[r][n] = epilogue( sum_k W[g][n][k] * x[r][k] )   for rows r of group g
+//
+// Work decomposition
+//   blockIdx.x  64 output features (4 waves x 16 features each)
+//   blockIdx.y  group g (expert slot)
+//   blockIdx.z  first row block; row blocks of 64 rows are strided by gridDim.z
+// Each wave owns 16 features and runs the whole K loop for them, so no
+// cross-wave reduction is needed.  The 64 rows of a row block are processed
+// in MT = 1, 2 or 4 tiles of 16, chosen from the rows actually present, so
+// one pass over the weights serves every row of a decode-sized group.
+//
+// MFMA mapping (v_mfma_f32_16x16x32_f16, or 4x v_mfma_f32_16x16x4_f32 for
+// fp32): A = 16 weight rows (features), B = x^T (16 rows = tokens).  Lane l
+// reads 16 contiguous bytes of weight row l%16 and of token row l%16 at the
+// same K offset, so a wave instruction covers 16 rows x 64 bytes and two
+// consecutive K chunks cover whole 128-byte lines.  Loads are double
+// buffered in registers, U chunks per buffer, to keep several KB per wave in
+// flight against HBM latency.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+// Epilogues
+enum : int { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_LOGITS = 2 };
+
+template <typename TW, int XM>
+struct XFrag {  // raw x fragment as loaded (same dtype as W)
+    typedef typename Frag<TW>::vec raw;
+    __device__ static __forceinline__ raw load(const void *base, size_t elem) {
+        return load16(reinterpret_cast<const TW *>(base) + elem);
+    }
+    __device__ static __forceinline__ typename Frag<TW>::vec cvt(const raw &v) { return v; }
+};
+template <>
+struct XFrag<f16, DT_FP8> {  // 8 fp8 codes, decoded to fp16 * 2^-8
+    typedef u32x2 raw;
+    __device__ static __forceinline__ raw load(const void *base, size_t elem) {
+        return *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint8_t *>(base) + elem);
+    }
+    __device__ static __forceinline__ f16x8 cvt(const raw &v) { return e4m3x8_to_f16x8_scaled(v); }
+};
+
+template <typename TW, int XM, int NM, int EPI, int MT, int U>
+__device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, int rstart,
+                                            int r0, int r1) {
+    typedef typename Frag<TW>::vec V;
+    typedef XFrag<TW, XM> XF;
+    typedef typename XF::raw XR;
+    constexpr int EL = Frag<TW>::kElems;  // elements per lane fragment
+    constexpr int CK = 4 * EL;            // K covered by one fragment step
+    const int lane = lane_id();
+    const int lr = lane & 15, lg = lane >> 4;
+    const int K = a.K;
+    const int NC = K / CK;
+
+    // weight rows (clamped: rows past N are read but never stored)
+    const TW *wp[NM];
+    {
+        int wrow = f0 + lr;
+        if (wrow > a.N - 1) wrow = a.N - 1;
+        const size_t off = (size_t)g * a.w_group_stride + (size_t)wrow * K + (size_t)lg * EL;
+        wp[0] = reinterpret_cast<const TW *>(a.w0) + off;
+        if (NM > 1) wp[NM - 1] = reinterpret_cast<const TW *>(a.w1) + off;
+    }
+    // token rows (clamped to the group's last row; extra columns are dropped)
+    size_t xo[MT];
+    int rows[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        int r = rstart + t * 16 + lr;
+        rows[t] = r;
+        int rc = r < r1 ? r : r1 - 1;
+        int xr = a.x_broadcast ? rc - r0 : rc;
+        xo[t] = (size_t)xr * K + (size_t)lg * EL;
+    }
+
+    f32x4 acc[NM][MT];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    V wa[U][NM], wb[U][NM];
+    XR xa[U][MT], xb[U][MT];
+
+#define MOE_LOAD(WBUF, XBUF, c)                                                  \
+    _Pragma("unroll") for (int u = 0; u < U; ++u) {                              \
+        _Pragma("unroll") for (int m = 0; m < NM; ++m) WBUF[u][m] =              \
+            load16(wp[m] + (size_t)((c) + u) * CK);                              \
+        _Pragma("unroll") for (int t = 0; t < MT; ++t) XBUF[u][t] =              \
+            XF::load(a.x, xo[t] + (size_t)((c) + u) * CK);                       \
+    }
+#define MOE_COMPUTE(WBUF, XBUF)                                                  \
+    _Pragma("unroll") for (int u = 0; u < U; ++u) {                              \
+        _Pragma("unroll") for (int t = 0; t < MT; ++t) {                         \
+            V xv = XF::cvt(XBUF[u][t]);                                          \
+            _Pragma("unroll") for (int m = 0; m < NM; ++m) acc[m][t] =           \
+                mfma16(WBUF[u][m], xv, acc[m][t]);                               \
+        }                                                                        \
+    }
+
+    MOE_LOAD(wa, xa, 0);
+    for (int c = 0; c < NC; c += 2 * U) {
+        MOE_LOAD(wb, xb, c + U);
+        MOE_COMPUTE(wa, xa);
+        if (c + 2 * U < NC) {
+            MOE_LOAD(wa, xa, c + 2 * U);
+        }
+        MOE_COMPUTE(wb, xb);
+    }
+#undef MOE_LOAD
+#undef MOE_COMPUTE
+
+    // epilogue: lane holds features f0 + 4*lg + j (j = 0..3) of token rows[t]
+    const int fb = f0 + 4 * lg;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const int r = rows[t];
+        if (r >= r1) continue;
+        float sc = 1.0f;
+        if (XM == DT_FP8) sc = a.x_scale[r] * 256.0f;  // undo the 2^-8 of the decode
+        if (EPI == EPI_LOGITS) {
+            float *o = reinterpret_cast<float *>(a.out) + (size_t)r * a.out_ld;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int f = fb + j;
+                if (f < a.N) o[f] = acc[0][t][j] + (a.bias && f < a.n_bias ? a.bias[f] : 0.0f);
+            }
+        } else {
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (EPI == EPI_SWIGLU) {
+                    const float ga = acc[0][t][j] * sc, ub = acc[NM - 1][t][j] * sc;
+                    v[j] = siluf_(ga) * ub;
+                } else {
+                    v[j] = acc[0][t][j] * sc;
+                }
+            }
+            TW *o = reinterpret_cast<TW *>(a.out) + (size_t)r * a.out_ld + fb;
+            if (sizeof(TW) == 2) {
+                f16x4 h4 = {to_f16(v[0]), to_f16(v[1]), to_f16(v[2]), to_f16(v[3])};
+                *reinterpret_cast<f16x4 *>(o) = h4;
+            } else {
+                *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
+            }
+        }
+    }
+}
+
+template <typename TW, int XM, int NM, int EPI, int U>
+__global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
+    const int wave = threadIdx.x >> 6;
+    const int f0 = blockIdx.x * 64 + wave * 16;
+    if (f0 >= a.N) return;
+    const int g = blockIdx.y;
+    int r0, r1;
+    if (a.offsets) {
+        r0 = a.offsets[g];
+        r1 = a.offsets[g + 1];
+    } else {
+        r0 = g * a.rows_per_group;
+        r1 = r0 + a.rows_per_group;
+    }
+    for (int rb = blockIdx.z; r0 + rb * 64 < r1; rb += gridDim.z) {
+        const int rs = r0 + rb * 64;
+        const int n = r1 - rs;
+        if (n <= 16)
+            stream_pass<TW, XM, NM, EPI, 1, U>(a, g, f0, rs, r0, r1);
+        else if (n <= 32)
+            stream_pass<TW, XM, NM, EPI, 2, U>(a, g, f0, rs, r0, r1);
+        else
+            stream_pass<TW, XM, NM, EPI, 4, (U > 2 ? 2 : U)>(a, g, f0, rs, r0, r1);
+    }
+}
+
+template <typename TW, int XM, int NM, int EPI>
+hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t s) {
+    dim3 grid((a.N + 63) / 64, n_groups, zblocks);
+    constexpr int CK = 4 * Frag<TW>::kElems;
+    const int NC = a.K / CK;
+    if (NC % 8 == 0)
+        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NM, EPI, 4>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NM, EPI, 2>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int mode,
+                              int n_groups, int zblocks, hipStream_t s) {
+    if (n_groups <= 0 || zblocks <= 0) return hipSuccess;
+    if (dtype == DT_F16) {
+        if (mode == STREAM_SWIGLU) {
+            if (x_dtype == DT_FP8) return launch_t<f16, DT_FP8, 2, EPI_SWIGLU>(a, n_groups, zblocks, s);
+            return launch_t<f16, DT_F16, 2, EPI_SWIGLU>(a, n_groups, zblocks, s);
+        }
+        if (mode == STREAM_STORE) return launch_t<f16, DT_F16, 1, EPI_STORE>(a, n_groups, zblocks, s);
+        return launch_t<f16, DT_F16, 1, EPI_LOGITS>(a, n_groups, zblocks, s);
+    }
+    if (mode == STREAM_SWIGLU) return launch_t<float, DT_F32, 2, EPI_SWIGLU>(a, n_groups, zblocks, s);
+    if (mode == STREAM_STORE) return launch_t<float, DT_F32, 1, EPI_STORE>(a, n_groups, zblocks, s);
+    return launch_t<float, DT_F32, 1, EPI_LOGITS>(a, n_groups, zblocks, s);
+}
+
+}  // namespace moe

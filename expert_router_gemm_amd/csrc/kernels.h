@@ -1,0 +1,73 @@
+// kernels.h -- internal launch interface between moe_api.cpp and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- GEMMs
+enum : int { STREAM_STORE = 0, STREAM_SWIGLU = 1, STREAM_LOGITS = 2 };
+
+struct StreamArgs {
+    const void *x;          // [rows][K] activations (dtype, or fp8 codes)
+    const float *x_scale;   // fp8 rows: per-row scale
+    int x_broadcast;        // x row = r - group start (shared experts)
+    const int32_t *offsets; // [G+1] group row ranges, or NULL: uniform groups
+    int rows_per_group;     // uniform groups: group g = rows [g*rpg, (g+1)*rpg)
+    const void *w0;         // [G][N][K]: gate (SWIGLU) or the only matrix
+    const void *w1;         // [G][N][K]: up (SWIGLU only)
+    size_t w_group_stride;  // elements from one group's matrix to the next
+    void *out;              // [rows][out_ld]
+    int out_ld;
+    const float *bias;      // LOGITS: fp32 bias for columns < n_bias
+    int n_bias;
+    int N, K;
+};
+
+// dtype: DT_F16 / DT_F32 (weights and output); x_dtype: dtype or DT_FP8.
+// Grid: ceil(N/64) x n_groups x zblocks; see gemm_stream.hip.
+hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int mode,
+                              int n_groups, int zblocks, hipStream_t s);
+
+// ---------------------------------------------------------------- routing
+// logits [T][ld] fp32 (E expert columns, then the shared-gate column if
+// has_gate) -> topk_idx/topk_w [T][K], shared_gate [T], logits_out [T][E].
+hipError_t launch_topk(const float *logits, int ld, int T, int E, int K, int has_gate,
+                       int32_t *topk_idx, float *topk_w, float *shared_gate,
+                       float *logits_out, hipStream_t s);
+
+// ---------------------------------------------------------------- dispatch
+struct DispatchArgs {
+    int T, K, E, S, H;
+    int dtype;              // of h
+    int x_dtype;            // of x_perm (dtype or DT_FP8)
+    const void *h;
+    const int32_t *topk_idx;
+    const int32_t *rep_off;
+    const int32_t *rep_slot;
+    uint64_t seed;
+    void *x_perm;
+    float *x_scale;
+    int32_t *counts, *offsets, *perm_src, *inv_pos;
+    // scratch
+    int32_t *pair_code;     // [T*K]
+    int32_t *chunk_counts;  // [C][S], C = ceil(T/64)
+};
+size_t dispatch_scratch_bytes(int T, int K, int S);
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- combine
+struct CombineArgs {
+    int T, K, H, n_shared, dtype;
+    const void *y;
+    const int32_t *inv_pos;
+    const float *topk_w;
+    const void *shared_y;   // [n_shared][T][H] or NULL
+    const float *shared_gate;
+    void *out;
+};
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,451 @@
+// moe_api.cpp -- the C ABI declared in include/moe.h: host-side validation,
+// workspace layout and the launch sequence of the layer.  No allocation, no
+// synchronisation, no global state.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+#define MOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace moe;
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxSlots = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxShared = 16;
+constexpr int64_t kMaxTokens = 1 << 20;
+
+inline size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline int act_bytes(const moe_shape &s) { return s.act == MOE_F32 ? 4 : 2; }
+inline int has_gate(const moe_shape &s) { return (s.flags & MOE_F_SHARED) ? 1 : 0; }
+
+moe_status check_shape(const moe_shape *s) {
+    if (!s) return MOE_ERR_INVALID_ARG;
+    if (s->flags & ~MOE_F_SHARED) return MOE_ERR_INVALID_ARG;
+    if (s->hidden <= 0 || s->inter <= 0 || s->hidden % 128 || s->inter % 128) return MOE_ERR_SHAPE;
+    if (s->n_experts < 1 || s->n_experts > kMaxExperts) return MOE_ERR_SHAPE;
+    if (s->top_k < 1 || s->top_k > kMaxTopK || s->top_k > s->n_experts) return MOE_ERR_SHAPE;
+    if (s->n_slots < 1 || s->n_slots > kMaxSlots) return MOE_ERR_SHAPE;
+    if (s->n_shared < 0 || s->n_shared > kMaxShared) return MOE_ERR_SHAPE;
+    if ((s->flags & MOE_F_SHARED) && s->n_shared < 1) return MOE_ERR_SHAPE;
+    if (s->act != MOE_F32 && s->act != MOE_F16) return MOE_ERR_DTYPE;
+    if (s->dispatch != s->act && !(s->dispatch == MOE_FP8_E4M3 && s->act == MOE_F16)) return MOE_ERR_DTYPE;
+    return MOE_OK;
+}
+
+moe_status check_T(int32_t T) { return (T < 0 || T > kMaxTokens) ? MOE_ERR_SHAPE : MOE_OK; }
+
+moe_status need(const void *p) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    return aligned16(p) ? MOE_OK : MOE_ERR_ALIGN;
+}
+moe_status need_opt(const void *p) { return (p && !aligned16(p)) ? MOE_ERR_ALIGN : MOE_OK; }
+moe_status need4(const void *p) {  // int32/fp32 vectors: 4-byte alignment
+    if (!p) return MOE_ERR_INVALID_ARG;
+    return ((uintptr_t)p & 3u) ? MOE_ERR_ALIGN : MOE_OK;
+}
+moe_status need4_opt(const void *p) { return (p && ((uintptr_t)p & 3u)) ? MOE_ERR_ALIGN : MOE_OK; }
+
+#define TRY(x)                                      \
+    do {                                            \
+        moe_status _st = (x);                       \
+        if (_st != MOE_OK) return _st;              \
+    } while (0)
+#define LAUNCH(x)                                   \
+    do {                                            \
+        if ((x) != hipSuccess) return MOE_ERR_LAUNCH; \
+    } while (0)
+
+moe_status device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_NO_DEVICE;
+    return MOE_OK;
+}
+
+// Workspace carving for moe_layer_forward (every piece 256-byte aligned).
+struct Layout {
+    size_t logits, topk_idx, topk_w, shared_gate, counts, offsets, perm_src, inv_pos;
+    size_t x_perm, x_scale, hm, y, shared_y, disp, total;
+};
+
+Layout layout(const moe_shape &s, int T) {
+    Layout L;
+    const size_t TK = (size_t)T * s.top_k;
+    const size_t isz = act_bytes(s);
+    const size_t xsz = s.dispatch == MOE_FP8_E4M3 ? 1 : isz;
+    const size_t nsh = has_gate(s) ? (size_t)s.n_shared : 0;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o += up256(bytes);
+        return at;
+    };
+    L.logits = take((size_t)T * (s.n_experts + 1) * 4);
+    L.topk_idx = take(TK * 4);
+    L.topk_w = take(TK * 4);
+    L.shared_gate = take((size_t)T * 4);
+    L.counts = take((size_t)s.n_slots * 4);
+    L.offsets = take((size_t)(s.n_slots + 1) * 4);
+    L.perm_src = take(TK * 4);
+    L.inv_pos = take(TK * 4);
+    L.x_perm = take(TK * s.hidden * xsz);
+    L.x_scale = take(TK * 4);
+    const size_t hm_rows = TK > nsh * T ? TK : nsh * T;
+    L.hm = take(hm_rows * s.inter * isz);
+    L.y = take(TK * s.hidden * isz);
+    L.shared_y = take(nsh * T * s.hidden * isz);
+    L.disp = take(dispatch_scratch_bytes(T, s.top_k, s.n_slots));
+    L.total = o;
+    return L;
+}
+
+template <typename P>
+inline P at(void *ws, size_t off) {
+    return reinterpret_cast<P>(reinterpret_cast<char *>(ws) + off);
+}
+
+int ffn_zblocks(int cap_rows, int n_groups) {
+    if (n_groups <= 0) return 1;
+    long per = ((long)cap_rows + n_groups - 1) / n_groups;
+    long z = (per + 63) / 64;
+    if (z < 1) z = 1;
+    if (z > 16) z = 16;
+    return (int)z;
+}
+
+// ------------------------------------------------------------ stage impls
+
+hipError_t route_impl(const moe_shape &s, int T, const void *h, const void *w_router,
+                      const float *bias, int32_t *topk_idx, float *topk_w, float *shared_gate,
+                      float *logits_user, float *logits_buf, hipStream_t st) {
+    const int gate = has_gate(s);
+    const int N = s.n_experts + gate;
+    StreamArgs a{};
+    a.x = h;
+    a.x_broadcast = 0;
+    a.offsets = nullptr;
+    a.rows_per_group = T;
+    a.w0 = w_router;
+    a.w1 = nullptr;
+    a.w_group_stride = 0;
+    a.out = logits_buf;
+    a.out_ld = N;
+    a.bias = bias;
+    a.n_bias = s.n_experts;
+    a.N = N;
+    a.K = s.hidden;
+    const int zb = (T + 63) / 64 < 65535 ? (T + 63) / 64 : 65535;  // rows stride by gridDim.z
+    hipError_t e = launch_stream_gemm(a, s.act, s.act, STREAM_LOGITS, 1, zb, st);
+    if (e != hipSuccess) return e;
+    return launch_topk(logits_buf, N, T, s.n_experts, s.top_k, gate, topk_idx, topk_w,
+                       shared_gate, logits_user, st);
+}
+
+hipError_t dispatch_impl(const moe_shape &s, int T, const void *h, const int32_t *topk_idx,
+                         const moe_slot_map &m, void *x_perm, float *x_scale, int32_t *counts,
+                         int32_t *offsets, int32_t *perm_src, int32_t *inv_pos, void *scratch,
+                         hipStream_t st) {
+    DispatchArgs d{};
+    d.T = T;
+    d.K = s.top_k;
+    d.E = s.n_experts;
+    d.S = s.n_slots;
+    d.H = s.hidden;
+    d.dtype = s.act;
+    d.x_dtype = s.dispatch;
+    d.h = h;
+    d.topk_idx = topk_idx;
+    d.rep_off = m.rep_off;
+    d.rep_slot = m.rep_slot;
+    d.seed = m.seed;
+    d.x_perm = x_perm;
+    d.x_scale = x_scale;
+    d.counts = counts;
+    d.offsets = offsets;
+    d.perm_src = perm_src;
+    d.inv_pos = inv_pos;
+    d.pair_code = reinterpret_cast<int32_t *>(scratch);
+    d.chunk_counts = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(scratch) +
+                                                 up256((size_t)T * s.top_k * 4));
+    return launch_dispatch(d, st);
+}
+
+hipError_t ffn_up_impl(const moe_shape &s, int n_groups, int zblocks, const void *x, int x_dtype,
+                       const float *x_scale, int x_broadcast, const int32_t *offsets,
+                       int rows_per_group, const void *w_gate, const void *w_up, void *hm,
+                       hipStream_t st) {
+    StreamArgs a{};
+    a.x = x;
+    a.x_scale = x_scale;
+    a.x_broadcast = x_broadcast;
+    a.offsets = offsets;
+    a.rows_per_group = rows_per_group;
+    a.w0 = w_gate;
+    a.w1 = w_up;
+    a.w_group_stride = (size_t)s.inter * s.hidden;
+    a.out = hm;
+    a.out_ld = s.inter;
+    a.N = s.inter;
+    a.K = s.hidden;
+    return launch_stream_gemm(a, s.act, x_dtype, STREAM_SWIGLU, n_groups, zblocks, st);
+}
+
+hipError_t ffn_down_impl(const moe_shape &s, int n_groups, int zblocks, const void *hm,
+                         const int32_t *offsets, int rows_per_group, const void *w_down, void *y,
+                         hipStream_t st) {
+    StreamArgs a{};
+    a.x = hm;
+    a.offsets = offsets;
+    a.rows_per_group = rows_per_group;
+    a.w0 = w_down;
+    a.w_group_stride = (size_t)s.hidden * s.inter;
+    a.out = y;
+    a.out_ld = s.hidden;
+    a.N = s.hidden;
+    a.K = s.inter;
+    return launch_stream_gemm(a, s.act, s.act, STREAM_STORE, n_groups, zblocks, st);
+}
+
+hipError_t combine_impl(const moe_shape &s, int T, const void *y, const int32_t *inv_pos,
+                        const float *topk_w, const void *shared_y, const float *shared_gate,
+                        void *out, hipStream_t st) {
+    CombineArgs c{};
+    c.T = T;
+    c.K = s.top_k;
+    c.H = s.hidden;
+    c.n_shared = shared_y ? s.n_shared : 0;
+    c.dtype = s.act;
+    c.y = y;
+    c.inv_pos = inv_pos;
+    c.topk_w = topk_w;
+    c.shared_y = shared_y;
+    c.shared_gate = shared_gate;
+    c.out = out;
+    return launch_combine(c, st);
+}
+
+moe_status check_ffn_common(const moe_shape *shape, int32_t n_groups, int32_t cap_rows) {
+    TRY(check_shape(shape));
+    if (n_groups < 1 || n_groups > 65535) return MOE_ERR_SHAPE;
+    if (cap_rows < 0 || (int64_t)cap_rows > kMaxTokens * kMaxTopK) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- ABI
+
+MOE_EXPORT const char *moe_status_str(moe_status st) {
+    switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_NO_DEVICE: return "MOE_ERR_NO_DEVICE";
+    case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH";
+    case MOE_ERR_NOT_IMPLEMENTED: return "MOE_ERR_NOT_IMPLEMENTED";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+MOE_EXPORT const char *moe_version(void) { return "0.1.0"; }
+
+MOE_EXPORT size_t moe_workspace_bytes(const moe_shape *shape, int32_t T) {
+    if (check_shape(shape) != MOE_OK || check_T(T) != MOE_OK) return 0;
+    return layout(*shape, T).total;
+}
+
+MOE_EXPORT moe_status moe_route(const moe_shape *shape, int32_t T, const void *h,
+                                const void *w_router, const float *bias, int32_t *topk_idx,
+                                float *topk_w, float *shared_gate, float *logits, void *ws,
+                                size_t ws_bytes, void *stream) {
+    TRY(check_shape(shape));
+    TRY(check_T(T));
+    if (T == 0) return MOE_OK;  // no token: nothing to route
+    TRY(need(h));
+    TRY(need(w_router));
+    TRY(need4_opt(bias));
+    TRY(need4(topk_idx));
+    TRY(need4(topk_w));
+    TRY(need4_opt(shared_gate));
+    TRY(need4_opt(logits));
+    if (has_gate(*shape) && !shared_gate) return MOE_ERR_INVALID_ARG;
+    const size_t req = up256((size_t)T * (shape->n_experts + 1) * 4);
+    if (!ws || ws_bytes < req) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    TRY(device_ok());
+    LAUNCH(route_impl(*shape, T, h, w_router, bias, topk_idx, topk_w, shared_gate, logits,
+                      reinterpret_cast<float *>(ws), (hipStream_t)stream));
+    return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_dispatch(const moe_shape *shape, int32_t T, const void *h,
+                                   const int32_t *topk_idx, const moe_slot_map *map,
+                                   void *x_perm, float *x_scale, int32_t *counts,
+                                   int32_t *offsets, int32_t *perm_src, int32_t *inv_pos,
+                                   void *ws, size_t ws_bytes, void *stream) {
+    TRY(check_shape(shape));
+    TRY(check_T(T));
+    if (!map) return MOE_ERR_INVALID_ARG;
+    TRY(need4(counts));
+    TRY(need4(offsets));
+    if (T > 0) {  // with no token only counts and offsets are written
+        TRY(need(h));
+        TRY(need4(topk_idx));
+        TRY(need4(map->rep_off));
+        TRY(need4(map->rep_slot));
+        TRY(need(x_perm));
+        if (shape->dispatch == MOE_FP8_E4M3) TRY(need4(x_scale));
+        TRY(need4(perm_src));
+        TRY(need4(inv_pos));
+    }
+    const size_t req = dispatch_scratch_bytes(T, shape->top_k, shape->n_slots);
+    if (!ws || ws_bytes < req) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    TRY(device_ok());
+    LAUNCH(dispatch_impl(*shape, T, h, topk_idx, *map, x_perm, x_scale, counts, offsets,
+                         perm_src, inv_pos, ws, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_expert_ffn_up(const moe_shape *shape, int32_t n_groups,
+                                        int32_t cap_rows, const void *x, int32_t x_dtype,
+                                        const float *x_scale, int32_t x_broadcast,
+                                        const int32_t *offsets, const void *w_gate,
+                                        const void *w_up, void *hm, void *stream) {
+    TRY(check_ffn_common(shape, n_groups, cap_rows));
+    if (x_dtype != shape->act && !(x_dtype == MOE_FP8_E4M3 && shape->act == MOE_F16))
+        return MOE_ERR_DTYPE;
+    TRY(need(x));
+    if (x_dtype == MOE_FP8_E4M3) TRY(need4(x_scale));
+    TRY(need4(offsets));
+    TRY(need(w_gate));
+    TRY(need(w_up));
+    TRY(need(hm));
+    if (cap_rows == 0) return MOE_OK;
+    TRY(device_ok());
+    LAUNCH(ffn_up_impl(*shape, n_groups, ffn_zblocks(cap_rows, n_groups), x, x_dtype, x_scale,
+                       x_broadcast ? 1 : 0, offsets, 0, w_gate, w_up, hm, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_expert_ffn_down(const moe_shape *shape, int32_t n_groups,
+                                          int32_t cap_rows, const void *hm,
+                                          const int32_t *offsets, const void *w_down, void *y,
+                                          void *stream) {
+    TRY(check_ffn_common(shape, n_groups, cap_rows));
+    TRY(need(hm));
+    TRY(need4(offsets));
+    TRY(need(w_down));
+    TRY(need(y));
+    if (cap_rows == 0) return MOE_OK;
+    TRY(device_ok());
+    LAUNCH(ffn_down_impl(*shape, n_groups, ffn_zblocks(cap_rows, n_groups), hm, offsets, 0,
+                         w_down, y, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_expert_ffn(const moe_shape *shape, int32_t n_groups, int32_t cap_rows,
+                                     const void *x, int32_t x_dtype, const float *x_scale,
+                                     int32_t x_broadcast, const int32_t *offsets,
+                                     const void *w_gate, const void *w_up, const void *w_down,
+                                     void *y, void *ws, size_t ws_bytes, void *stream) {
+    TRY(check_ffn_common(shape, n_groups, cap_rows));
+    const size_t req = up256((size_t)cap_rows * shape->inter * act_bytes(*shape));
+    if (cap_rows > 0 && (!ws || ws_bytes < req)) return MOE_ERR_WORKSPACE;
+    if (cap_rows > 0 && !aligned16(ws)) return MOE_ERR_ALIGN;
+    TRY(need(w_down));
+    TRY(need(y));
+    moe_status st = moe_expert_ffn_up(shape, n_groups, cap_rows, x, x_dtype, x_scale,
+                                      x_broadcast, offsets, w_gate, w_up, ws, stream);
+    if (st != MOE_OK) return st;
+    return moe_expert_ffn_down(shape, n_groups, cap_rows, ws, offsets, w_down, y, stream);
+}
+
+MOE_EXPORT moe_status moe_combine(const moe_shape *shape, int32_t T, const void *y,
+                                  const int32_t *inv_pos, const float *topk_w,
+                                  const void *shared_y, const float *shared_gate, void *out,
+                                  void *stream) {
+    TRY(check_shape(shape));
+    TRY(check_T(T));
+    if (T == 0) return MOE_OK;
+    TRY(need(y));
+    TRY(need4(inv_pos));
+    TRY(need4(topk_w));
+    TRY(need_opt(shared_y));
+    if (shared_y) TRY(need4(shared_gate));
+    TRY(need(out));
+    TRY(device_ok());
+    LAUNCH(combine_impl(*shape, T, y, inv_pos, topk_w, shared_y, shared_gate, out,
+                        (hipStream_t)stream));
+    return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_layer_forward(const moe_shape *shape, const moe_weights *w,
+                                        const moe_slot_map *map, int32_t T, const void *h,
+                                        void *out, void *ws, size_t ws_bytes, void *stream) {
+    TRY(check_shape(shape));
+    TRY(check_T(T));
+    if (!w || !map) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;  // no token: empty output
+    const moe_shape &s = *shape;
+    TRY(need(h));
+    TRY(need(out));
+    TRY(need(w->w_router));
+    TRY(need4_opt(w->bias));
+    TRY(need(w->w_gate));
+    TRY(need(w->w_up));
+    TRY(need(w->w_down));
+    TRY(need4(map->rep_off));
+    TRY(need4(map->rep_slot));
+    const int gate = has_gate(s);
+    if (gate) {
+        TRY(need(w->sh_gate));
+        TRY(need(w->sh_up));
+        TRY(need(w->sh_down));
+    }
+    const Layout L = layout(s, T);
+    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    TRY(device_ok());
+    hipStream_t st = (hipStream_t)stream;
+
+    int32_t *topk_idx = at<int32_t *>(ws, L.topk_idx);
+    float *topk_w = at<float *>(ws, L.topk_w);
+    float *sgate = at<float *>(ws, L.shared_gate);
+    int32_t *offsets = at<int32_t *>(ws, L.offsets);
+    int32_t *inv_pos = at<int32_t *>(ws, L.inv_pos);
+    float *x_scale = at<float *>(ws, L.x_scale);
+    const int cap = T * s.top_k;
+
+    LAUNCH(route_impl(s, T, h, w->w_router, w->bias, topk_idx, topk_w, gate ? sgate : nullptr,
+                      nullptr, at<float *>(ws, L.logits), st));
+    LAUNCH(dispatch_impl(s, T, h, topk_idx, *map, at<void *>(ws, L.x_perm), x_scale,
+                         at<int32_t *>(ws, L.counts), offsets, at<int32_t *>(ws, L.perm_src),
+                         inv_pos, at<void *>(ws, L.disp), st));
+    const int z = ffn_zblocks(cap, s.n_slots);
+    LAUNCH(ffn_up_impl(s, s.n_slots, z, at<void *>(ws, L.x_perm), s.dispatch, x_scale, 0, offsets,
+                       0, w->w_gate, w->w_up, at<void *>(ws, L.hm), st));
+    LAUNCH(ffn_down_impl(s, s.n_slots, z, at<void *>(ws, L.hm), offsets, 0, w->w_down,
+                         at<void *>(ws, L.y), st));
+    void *shared_y = nullptr;
+    if (gate) {
+        shared_y = at<void *>(ws, L.shared_y);
+        const int zs = (T + 63) / 64 < 65535 ? (T + 63) / 64 : 65535;
+        LAUNCH(ffn_up_impl(s, s.n_shared, zs, h, s.act, nullptr, 1, nullptr, T, w->sh_gate,
+                           w->sh_up, at<void *>(ws, L.hm), st));
+        LAUNCH(ffn_down_impl(s, s.n_shared, zs, at<void *>(ws, L.hm), nullptr, T, w->sh_down,
+                             shared_y, st));
+    }
+    LAUNCH(combine_impl(s, T, at<void *>(ws, L.y), inv_pos, topk_w, shared_y, sgate, out, st));
+    return MOE_OK;
+}

@@ -1,0 +1,203 @@
+/*
+ * moe.h -- C ABI of libmoe: one DeepSeek-V3-style MoE layer on one MI355X.
+ *
+ * The operations follow the five-step token journey of the expert-parallelism
+ * blog page (yveltals, "专家并行（EP）", section 2.2):
+ *   Step 1  router linear + top-K            -> moe_route
+ *   Step 2  dispatch to the experts' owners  -> moe_dispatch (an on-device
+ *           permutation into per-slot contiguous groups: one GPU holds this
+ *           rank's share of the experts, so nothing crosses a link)
+ *   Step 3  expert FFN                       -> moe_expert_ffn
+ *                                               (= moe_expert_ffn_up + _down)
+ *   Step 4  combine (return the outputs)     -> moe_combine
+ *   Step 5  gate-weighted sum + shared term     (same call)
+ *   all of it                                -> moe_layer_forward
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE memory unless marked (host).  The caller allocates
+ *     and owns every buffer; the library never allocates, frees or
+ *     synchronises, and keeps no state between calls (thread-safe).
+ *   - Matrices are row-major and "out-major": a weight that maps an input of
+ *     length n to m outputs is stored [m][n], i.e. the transpose of the
+ *     page's [in, out] math shapes (router [7168, 256], gate/up
+ *     [7168, 2048], down [2048, 7168]).  Every row starts 16-byte aligned.
+ *   - dtype: MOE_F16 (fp16 activations and weights, fp32 accumulation,
+ *     fp16 outputs) or MOE_F32 (fp32 throughout).  Dispatched rows may be
+ *     MOE_FP8_E4M3 with one fp32 scale per row (F16 layers only).
+ *   - stream: a hipStream_t; NULL is the default stream.  Every call only
+ *     enqueues work on it and returns; outputs are valid once the stream
+ *     reaches that point.
+ *   - Return value: a synchronous status from host-side validation (shapes,
+ *     NULL pointers, alignment, dtype combinations, workspace size), or
+ *     MOE_ERR_LAUNCH if a kernel launch was rejected.  Nothing is enqueued
+ *     when validation fails.  Faults inside kernels surface at the caller's
+ *     next synchronisation of the stream.  No C++ exception crosses the ABI.
+ *   - Limits: hidden and inter positive multiples of 128;
+ *     1 <= top_k <= min(E, 16); E <= 1024; 1 <= S <= 1024; n_shared <= 16;
+ *     0 <= T <= 2^20 (T = 0 is valid: no token, nothing routed).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,     /* NULL pointer / bad flag */
+    MOE_ERR_SHAPE = 2,           /* dims outside the limits above */
+    MOE_ERR_DTYPE = 3,           /* unsupported dtype combination */
+    MOE_ERR_ALIGN = 4,           /* pointer not 16-byte aligned */
+    MOE_ERR_WORKSPACE = 5,       /* ws NULL or ws_bytes too small */
+    MOE_ERR_NO_DEVICE = 6,       /* no HIP device usable */
+    MOE_ERR_LAUNCH = 7,          /* a kernel launch failed */
+    MOE_ERR_NOT_IMPLEMENTED = 8
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_F16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* moe_shape.flags */
+#define MOE_F_SHARED 1u /* layer has shared experts: add their gated sum */
+
+/* Layer description (host struct). */
+typedef struct {
+    int32_t hidden;    /* H: 7168 for DeepSeek-V3 (section 2.2, Step 1) */
+    int32_t inter;     /* I: 2048 (section 一: gate/up [7168, 2048]) */
+    int32_t n_experts; /* E: routed experts the router scores (256) */
+    int32_t top_k;     /* K: experts per token (8) */
+    int32_t n_slots;   /* S: expert weight sets resident here (32 for one
+                          rank of EP=8, 33 with a redundant replica, 256 for
+                          the whole layer; sections 2.1 and 6.3) */
+    int32_t n_shared;  /* shared experts (2 in DeepSeek-V3, section 2.1) */
+    int32_t act;       /* moe_dtype of h, weights and outputs: F32 or F16 */
+    int32_t dispatch;  /* moe_dtype of dispatched rows: == act, or FP8_E4M3 */
+    uint32_t flags;    /* MOE_F_SHARED */
+} moe_shape;
+
+/* Expert -> local slot table (device arrays), sections 2.1 and 6.3.
+ * Expert e has n_e = rep_off[e+1] - rep_off[e] replicas, listed in
+ * rep_slot[rep_off[e] .. rep_off[e+1]): a local slot in [0, S) or -1 for a
+ * copy that lives on another GPU.  A pair (t, k) routed to e goes to replica
+ * splitmix64(seed ^ (t*K + k)) mod n_e (SplitMix64 output function, Steele,
+ * Lea and Flood 2014); n_e == 1 needs no hash; n_e == 0 means not here. */
+typedef struct {
+    const int32_t *rep_off;  /* [E + 1] */
+    const int32_t *rep_slot; /* [rep_off[E]] */
+    uint64_t seed;
+} moe_slot_map;
+
+/* Weights of the whole layer (device pointers; dtype = shape.act). */
+typedef struct {
+    const void *w_router; /* [E][H]; with MOE_F_SHARED, [E + 1][H]: row E is
+                             the shared-expert gate vector w_sg */
+    const float *bias;    /* [E] fp32 router logit bias, or NULL */
+    const void *w_gate;   /* [S][I][H] */
+    const void *w_up;     /* [S][I][H] */
+    const void *w_down;   /* [S][H][I] */
+    const void *sh_gate;  /* [n_shared][I][H]  (MOE_F_SHARED only) */
+    const void *sh_up;    /* [n_shared][I][H] */
+    const void *sh_down;  /* [n_shared][H][I] */
+} moe_weights;
+
+/* Step 1 (section 2.2): router linear and top-K.
+ *   logits[t][e] = fp32(sum_i h[t][i] * w_router[e][i]) + bias[e]
+ *   p[t] = softmax over all E logits; the K experts with the largest logits
+ *   (ties: lower id first) are written to topk_idx[t][0..K) in that order
+ *   and their probabilities, not renormalised, to topk_w[t][0..K).
+ *   With MOE_F_SHARED, shared_gate[t] = sigmoid(h[t] . w_router[E]).
+ * h [T][H] (act); topk_idx int32 [T][K]; topk_w fp32 [T][K];
+ * shared_gate fp32 [T] or NULL; logits fp32 [T][E] or NULL (if non-NULL the
+ * raw logits including bias are stored).
+ * Workspace: ws of at least T*(E+1)*4 bytes rounded up to 256 (any
+ * moe_workspace_bytes(shape, T) sized buffer works). */
+moe_status moe_route(const moe_shape *shape, int32_t T, const void *h,
+                     const void *w_router, const float *bias, int32_t *topk_idx,
+                     float *topk_w, float *shared_gate, float *logits, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* Step 2 (section 2.2) on one GPU: permute the local (token, k) pairs into
+ * per-slot contiguous groups.  slot(t, k) comes from `map`; rows are ordered
+ * by (slot, t) ascending; no capacity limit, nothing dropped.
+ *   counts [S]         rows per slot
+ *   offsets [S + 1]    exclusive prefix sum; offsets[S] = local rows P
+ *   perm_src [T*K]     perm_src[row] = t*K + k for row < P (rest untouched)
+ *   inv_pos [T][K]     row of pair (t, k), or -1 if the pair is not local
+ *   x_perm [T*K][H]    x_perm[row] = h[t]; with dispatch = FP8_E4M3 the row
+ *                      is stored as OCP E4M3 codes (uint8) with
+ *                      x_scale[row] = amax/448 and codes
+ *                      E4M3_RNE(clamp(h * (448/amax), -448, 448)) (section
+ *                      2.3: FP8 halves the dispatch payload); x_scale may be
+ *                      NULL otherwise.  Rows >= P are untouched.
+ * Workspace: ws of at least moe_workspace_bytes(shape, T) bytes. */
+moe_status moe_dispatch(const moe_shape *shape, int32_t T, const void *h,
+                        const int32_t *topk_idx, const moe_slot_map *map, void *x_perm,
+                        float *x_scale, int32_t *counts, int32_t *offsets,
+                        int32_t *perm_src, int32_t *inv_pos, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/* Step 3, first half (section 一 gives gate/up [7168, 2048]): for every group
+ * g < n_groups and every row r in [offsets[g], offsets[g+1]):
+ *   hm[r] = silu(w_gate[g] . x_r) * (w_up[g] . x_r),  silu(z) = z*sigmoid(z)
+ * x_r = x[r] normally, or x[r - offsets[g]] when x_broadcast != 0 (every
+ * group reads the same rows: how the shared experts see all tokens).  With
+ * x_dtype FP8_E4M3 the row is decoded and multiplied by x_scale[r].
+ * hm [cap_rows][I] (act).  cap_rows (host) bounds offsets[n_groups]; groups
+ * with no rows read no weights. */
+moe_status moe_expert_ffn_up(const moe_shape *shape, int32_t n_groups, int32_t cap_rows,
+                             const void *x, int32_t x_dtype, const float *x_scale,
+                             int32_t x_broadcast, const int32_t *offsets,
+                             const void *w_gate, const void *w_up, void *hm, void *stream);
+
+/* Step 3, second half (section 6.3's 88 MB per expert = three 7168 x 2048
+ * fp16 matrices, so down is [2048, 7168]):  y[r] = w_down[g] . hm[r].
+ * y [cap_rows][H] (act). */
+moe_status moe_expert_ffn_down(const moe_shape *shape, int32_t n_groups, int32_t cap_rows,
+                               const void *hm, const int32_t *offsets, const void *w_down,
+                               void *y, void *stream);
+
+/* Step 3 whole: up then down, with hm in the workspace. */
+moe_status moe_expert_ffn(const moe_shape *shape, int32_t n_groups, int32_t cap_rows,
+                          const void *x, int32_t x_dtype, const float *x_scale,
+                          int32_t x_broadcast, const int32_t *offsets, const void *w_gate,
+                          const void *w_up, const void *w_down, void *y, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Steps 4 and 5 (section 2.2):
+ *   out[t] = sum_{k = 0..K-1, inv_pos[t][k] >= 0} topk_w[t][k] * y[inv_pos[t][k]]
+ *          + shared_gate[t] * sum_j shared_y[j][t]      (if shared_y != NULL)
+ * summed in k order in fp32, rounded once to act.  A token with no local
+ * pair and no shared term gets exact zeros (a rank's partial output).
+ * y [*][H]; shared_y [n_shared][T][H] or NULL; out [T][H] (act). */
+moe_status moe_combine(const moe_shape *shape, int32_t T, const void *y,
+                       const int32_t *inv_pos, const float *topk_w, const void *shared_y,
+                       const float *shared_gate, void *out, void *stream);
+
+/* Steps 1-5 for T tokens: moe_route, moe_dispatch, moe_expert_ffn on the
+ * routed groups and (MOE_F_SHARED) on the shared experts, moe_combine.
+ * Same kernels and order as the staged calls, so the outputs are bitwise
+ * equal to the staged path.  out [T][H] (act).  Without MOE_F_SHARED the
+ * output is this GPU's partial sum over its local pairs. */
+moe_status moe_layer_forward(const moe_shape *shape, const moe_weights *weights,
+                             const moe_slot_map *map, int32_t T, const void *h, void *out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* (host) Workspace bytes that moe_layer_forward needs for T tokens; also
+ * enough for moe_dispatch and moe_expert_ffn with cap_rows <= T*K (or
+ * n_shared*T for the shared experts).  Returns 0 for an invalid shape. */
+size_t moe_workspace_bytes(const moe_shape *shape, int32_t T);
+
+/* (host) Static string naming a status. */
+const char *moe_status_str(moe_status status);
+
+/* (host) Library version, "major.minor.patch". */
+const char *moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

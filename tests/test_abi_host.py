@@ -1,0 +1,155 @@
+"""Host-side checks of libmoe's C ABI (no kernel is launched here).
+
+* the shared library loads and exports every function include/moe.h declares;
+* host validation returns the documented status codes before touching a
+  device (fake, aligned pointers are enough: nothing is dereferenced);
+* the product's placement tables agree with the oracle's own builder.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("expert_router_gemm_amd")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"libmoe.so does not export {n}"
+    assert set(names) == set(moe.EXPORTED)
+
+
+def test_status_strings_and_version():
+    assert moe.status_str(0) == "MOE_OK"
+    assert moe.status_str(2) == "MOE_ERR_SHAPE"
+    assert moe.status_str(99) == "MOE_ERR_UNKNOWN"
+    assert re.fullmatch(r"\d+\.\d+\.\d+", moe.version())
+
+
+def _shape(**kw):
+    d = dict(hidden=7168, inter=2048, n_experts=256, top_k=8, n_slots=32)
+    d.update(kw)
+    return moe.make_shape(**d)
+
+
+def test_workspace_bytes():
+    s = _shape()
+    w = moe.moe_workspace_bytes(s, 256)
+    T, K, H, I, E = 256, 8, 7168, 2048, 256
+    # at least x_perm, hm and y plus the routing buffers
+    assert w >= T * K * H * 2 * 2 + T * K * I * 2 + T * (E + 1) * 4
+    assert moe.moe_workspace_bytes(s, 0) > 0
+    assert moe.moe_workspace_bytes(_shape(hidden=100), 16) == 0
+    assert moe.moe_workspace_bytes(s, -1) == 0
+    sh = _shape(n_shared=2, shared=True, n_slots=256)
+    assert moe.moe_workspace_bytes(sh, 128) > moe.moe_workspace_bytes(_shape(n_slots=256), 128)
+    f8 = _shape(dispatch=moe.MOE_FP8_E4M3)
+    assert moe.moe_workspace_bytes(f8, 512) < moe.moe_workspace_bytes(_shape(), 512)
+
+
+FAKE = 0x100000  # aligned, never dereferenced: validation fails first
+
+
+def _route(shape, T=16, **ptr):
+    L = moe.lib()
+    p = dict(h=FAKE, w=FAKE, bias=None, idx=FAKE, tw=FAKE, sg=None, lg=None, ws=FAKE)
+    p.update(ptr)
+    return L.moe_route(ctypes.byref(shape), T, p["h"], p["w"], p["bias"], p["idx"], p["tw"],
+                       p["sg"], p["lg"], p["ws"], ptr.get("ws_bytes", 1 << 30), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=7000), 2), (dict(inter=100), 2), (dict(top_k=0), 2), (dict(top_k=17), 2),
+    (dict(n_experts=4, top_k=8), 2), (dict(n_experts=2048), 2), (dict(n_slots=0), 2),
+    (dict(n_slots=2000), 2), (dict(act=7), 3), (dict(act=0, dispatch=2), 3),
+    (dict(shared=True, n_shared=0), 2),
+])
+def test_route_rejects_bad_shapes(kw, status):
+    assert _route(_shape(**kw)) == status
+
+
+def test_route_rejects_bad_pointers_and_workspace():
+    s = _shape()
+    assert _route(s, h=None) == 1
+    assert _route(s, h=FAKE + 2) == 4
+    assert _route(s, idx=FAKE + 2) == 4
+    assert _route(s, ws=None) == 5
+    assert _route(s, ws_bytes=100) == 5
+    assert _route(s, T=-1) == 2
+    assert _route(_shape(n_shared=2, shared=True), sg=None) == 1
+    assert _route(s, T=0, ws=None) == 0  # nothing to do
+
+
+def test_other_entry_points_validate_before_launch():
+    L = moe.lib()
+    s = _shape()
+    sm = moe.SlotMap(FAKE, FAKE, 0)
+    assert L.moe_dispatch(ctypes.byref(s), 16, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+                          FAKE, FAKE, 1 << 30, None) == 1
+    assert L.moe_dispatch(ctypes.byref(s), 16, FAKE, FAKE, ctypes.byref(sm), FAKE, None, FAKE,
+                          FAKE, FAKE, FAKE, FAKE, 10, None) == 5
+    f8 = _shape(dispatch=moe.MOE_FP8_E4M3)
+    assert L.moe_dispatch(ctypes.byref(f8), 16, FAKE, FAKE, ctypes.byref(sm), FAKE, None, FAKE,
+                          FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert L.moe_expert_ffn_up(ctypes.byref(s), 0, 16, FAKE, 1, None, 0, FAKE, FAKE, FAKE, FAKE,
+                               None) == 2
+    assert L.moe_expert_ffn_up(ctypes.byref(s), 4, 16, FAKE, 2, None, 0, FAKE, FAKE, FAKE, FAKE,
+                               None) == 1  # fp8 rows need scales
+    assert L.moe_expert_ffn_up(ctypes.byref(_shape(act=0, dispatch=0)), 4, 16, FAKE, 2, FAKE, 0,
+                               FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert L.moe_expert_ffn_down(ctypes.byref(s), 4, -1, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.moe_expert_ffn(ctypes.byref(s), 4, 16, FAKE, 1, None, 0, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, 8, None) == 5
+    assert L.moe_combine(ctypes.byref(s), 16, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 1
+    w = moe.Weights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)
+    assert L.moe_layer_forward(ctypes.byref(s), ctypes.byref(w), ctypes.byref(sm), 16, FAKE,
+                               FAKE, FAKE, 16, None) == 5
+    sh = _shape(n_shared=2, shared=True)
+    assert L.moe_layer_forward(ctypes.byref(sh), ctypes.byref(w), ctypes.byref(sm), 16, FAKE,
+                               FAKE, FAKE, 1 << 40, None) == 1  # shared weights missing
+
+
+def _gpu_present() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:  # pragma: no cover
+        return False
+
+
+@pytest.mark.skipif(_gpu_present(), reason="a device is present: valid calls would launch")
+def test_valid_call_without_device_reports_no_device():
+    s = _shape()
+    assert _route(s) == 6
+
+
+@pytest.mark.parametrize("E,ep,rank,rep", [(256, 8, 0, None), (256, 8, 3, None), (256, 8, 0, 32),
+                                           (256, 1, 0, None), (16, 1, 0, None), (32, 4, 2, 3)])
+def test_placement_tables_match_oracle(E, ep, rank, rep):
+    a = moe.build_slot_map(E, ep, rank, [rep] if rep is not None else None)
+    b = oracle.placement(E, ep, rank, replica_of=rep)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_drop_replica_matches_oracle_reading():
+    off, slot, _ = moe.build_slot_map(256, 8, 0, [40])
+    off2, slot2 = moe.drop_replica(off, slot, 40, 0)
+    assert off2[-1] == off[-1] - 1
+    assert list(slot2[off2[40]:off2[41]]) == [32]

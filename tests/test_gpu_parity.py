@@ -1,0 +1,326 @@
+"""Parity of the HIP path (through libmoe's C ABI) with the CPU oracle.
+
+Bars:
+  * bit-exact: routing indices (tokens whose sorted top-(K+1) logits have a
+    gap < 1e-5 are excluded and counted), per-slot counts, offsets, the
+    dispatch permutation and inverse, copied rows, fp8 codes and scales;
+  * |gpu - ref| <= 2e-3 + 2e-2 |ref| elementwise on layer outputs;
+  * intermediates with tolerances derived from the arithmetic (see each test).
+Stage tests feed the oracle the GPU's own upstream results, so each stage is
+judged on identical inputs.  Small dims keep the oracle to seconds while
+spanning several tiles and a ragged tail; the full-size cases compare
+sampled tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+gh = pytest.importorskip("gpu_harness")
+
+# Workloads at dims the oracle runs in seconds (routing structure unchanged).
+SMALL = {
+    1: dict(),
+    2: dict(T=256, H=1024, I=512),
+    3: dict(T=128, H=512, I=256),
+    4: dict(T=2048, H=512, I=256),
+    5: dict(T=512, H=1024, I=512),
+}
+
+
+def small_cfg(n, seed=None):
+    c = moe_synth.config(n, seed=seed)
+    kw = SMALL[n]
+    if kw:
+        c = moe_synth.scaled_config(n, seed=seed, **kw)
+    return c
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def _check_routing(L, st, tokens=None):
+    """Three checks:
+      1. GPU logits within the deterministic fp32-accumulation bound of the
+         fp64 oracle logits;
+      2. the oracle's softmax/top-K run on the GPU's own logits reproduces
+         the GPU's indices on every token (same inputs, same fp32 values:
+         exact) and its gates to fp32 rounding;
+      3. against the oracle's own logits, indices match on every token that
+         is not a near tie (sorted top-(K+1) gap < 1e-5); near ties counted.
+    Returns the near-tie mask."""
+    cfg = L.cfg
+    sel = (lambda a: a) if tokens is None else (lambda a: a[tokens])  # noqa: E731
+    h = sel(L.h)
+    ref_lg = oracle.router_logits(h, L.wr[: cfg.E], L.bias)
+    g_lg, g_idx, g_w = sel(st["logits"]), sel(st["topk_idx"]), sel(st["topk_w"])
+    bound = gh.logit_error_bound(L, tokens)
+    err = np.abs(g_lg.astype(np.float64) - ref_lg)
+    assert np.all(err <= bound), f"logit error {err.max():.3e} above bound"
+    idx2, w2 = oracle.softmax_topk(g_lg, cfg.K)
+    assert np.array_equal(g_idx, idx2), "top-K kernel differs from the oracle on the same logits"
+    assert np.allclose(g_w, w2, rtol=4e-6, atol=1e-9), "gates differ on the same logits"
+    ref_idx, _ = oracle.softmax_topk(ref_lg, cfg.K)
+    tie = oracle.near_tie_tokens(ref_lg, cfg.K)
+    ok = ~tie
+    assert np.array_equal(g_idx[ok], ref_idx[ok]), "top-k differs on a non-near-tie token"
+    if cfg.n_shared:
+        z = (h.astype(np.float64) @ L.wr[cfg.E].astype(np.float64))
+        ref_gs = 1.0 / (1.0 + np.exp(-z))
+        assert np.allclose(sel(st["shared_gate"]), ref_gs, rtol=1e-5, atol=1e-6)
+    print(f"[routing] tokens={len(ref_lg)} near_ties={int(tie.sum())} "
+          f"max|dlogit|={err.max():.2e}")
+    return tie
+
+
+def _check_dispatch(L, st):
+    cfg = L.cfg
+    S = len(L.slot_experts)
+    # the oracle builds its own table and is fed the GPU's top-k
+    rep = moe_synth.replica_expert(cfg)
+    ro, rs, _ = oracle.placement(cfg.E, cfg.ep_size, L.rank, replica_of=rep)
+    slot = oracle.slot_map(st["topk_idx"], ro, rs, L.seed)
+    counts, offsets, perm, inv = oracle.dispatch(slot, S)
+    assert np.array_equal(st["counts"], counts)
+    assert np.array_equal(st["offsets"], offsets)
+    assert np.array_equal(st["perm_src"], perm)
+    assert np.array_equal(st["inv_pos"], inv)
+    assert np.all(st["perm_tail"] == -7), "rows past P must stay untouched"
+    toks = perm // cfg.K
+    if cfg.dispatch == "fp8":
+        q, s = oracle.quant_e4m3_rows(L.h[toks]) if len(toks) else (np.zeros((0, cfg.H), np.uint8), np.zeros(0, np.float32))
+        assert np.array_equal(st["x_perm"], q), "fp8 codes differ"
+        assert np.array_equal(st["x_scale"], s), "fp8 scales differ"
+    else:
+        assert np.array_equal(st["x_perm"], L.h[toks]), "dispatched rows differ"
+    return slot
+
+
+def _check_ffn(L, st):
+    """y rows against the oracle SwiGLU on the GPU's own dispatched rows.
+    Tolerance: the output bar (fp16 y)."""
+    cfg = L.cfg
+    off = st["offsets"]
+    dec = oracle.e4m3_decode_table()
+    for s in range(len(L.slot_experts)):
+        a, b = off[s], off[s + 1]
+        if a == b:
+            continue
+        if cfg.dispatch == "fp8":
+            x = dec[st["x_perm"][a:b]].astype(np.float32) * st["x_scale"][a:b, None]
+        else:
+            x = st["x_perm"][a:b]
+        y, hm = oracle.expert_rows(x.astype(np.float64), *L.expert(L.slot_experts[s]), want_hm=True)
+        gh.assert_close(st["hm"][a:b], hm, f"hm slot {s}")
+        gh.assert_close(st["y"][a:b], y, f"y slot {s}")
+    if cfg.n_shared:
+        for j in range(cfg.n_shared):
+            y = oracle.expert_rows(L.h.astype(np.float64), *[m[j] for m in L.shared])
+            gh.assert_close(st["shared_y"][j * L.T:(j + 1) * L.T], y, f"shared expert {j}")
+
+
+def _check_combine(L, st):
+    cfg = L.cfg
+    shy = None
+    if cfg.n_shared:
+        shy = st["shared_y"].astype(np.float32).reshape(cfg.n_shared, L.T, cfg.H)
+    ref = oracle.combine(st["y"].astype(np.float32), st["inv_pos"], st["topk_w"], shy,
+                         st["shared_gate"])
+    gh.assert_close(st["out"], ref, "combine")
+    none_local = np.all(st["inv_pos"] < 0, axis=1)
+    if not cfg.n_shared:
+        assert np.all(st["out"][none_local] == 0), "rows with no local pair must be exact zeros"
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("seed_off", [0, 100])
+def test_stages_and_layer_small(n, seed_off):
+    cfg = small_cfg(n, seed=moe_synth.config(n).seed + seed_off)
+    print(f"[case] workload {n} {cfg}", flush=True)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    tie = _check_routing(L, st)
+    _check_dispatch(L, st)
+    _check_ffn(L, st)
+    _check_combine(L, st)
+    # the fused entry point runs the same kernels: bitwise equal
+    out = gh.gpu_forward(L).cpu().numpy()
+    assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8))
+    # end to end against the oracle's own routing (near-tie tokens excluded)
+    ref = gh.oracle_forward(L)
+    assert np.array_equal(ref["topk_idx"][~tie], st["topk_idx"][~tie])
+    err = gh.assert_close(out, ref["out"], "layer output", rows=~tie)
+    print(f"[layer] workload {n} P={st['P']} max|d|={err:.3e} near_ties={int(tie.sum())}")
+
+
+def test_layer_is_deterministic():
+    cfg = small_cfg(5)
+    L = gh.build_layer(cfg)
+    a = gh.gpu_forward(L).cpu().numpy()
+    b = gh.gpu_forward(L).cpu().numpy()
+    assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("T", [0, 1, 63, 65, 130])
+def test_ragged_and_empty_batches(T):
+    cfg = moe_synth.scaled_config(2, T=T, H=256, I=128, seed=21)
+    L = gh.build_layer(cfg)
+    if T == 0:
+        out = torch.empty((0, cfg.H), dtype=torch.float16, device=gh.DEV)
+        ws = gh.ws_for(L, 0)
+        import expert_router_gemm_amd as moe
+        moe.moe_layer_forward(L.shape, L.wmap, L.smap, 0, L.d["h"], out, ws)
+        torch.cuda.synchronize()
+        return
+    st = gh.gpu_stages(L)
+    tie = _check_routing(L, st)
+    _check_dispatch(L, st)
+    ref = gh.oracle_forward(L)
+    gh.assert_close(st["out"], ref["out"], "layer", rows=~tie)
+
+
+def test_hot_expert_spans_several_row_blocks():
+    """One expert takes every token (a group of T > 64 rows: several 64-row
+    blocks and the 4-tile path), most others get none."""
+    cfg = moe_synth.scaled_config(2, T=200, H=256, I=128, seed=22)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[[3, 17]] = 50.0  # experts 3 and 17 (both local on rank 0) win every token
+    L = gh.build_layer(cfg, bias_override=bias)
+    st = gh.gpu_stages(L)
+    _check_routing(L, st)
+    _check_dispatch(L, st)
+    assert st["counts"][3] == cfg.T and st["counts"][17] == cfg.T
+    _check_ffn(L, st)
+    ref = gh.oracle_forward(L)
+    gh.assert_close(st["out"], ref["out"], "layer")
+
+
+def test_no_local_pair_gives_exact_zeros():
+    cfg = moe_synth.scaled_config(2, T=70, H=256, I=128, seed=23)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[100:108] = 50.0  # every token picks experts 100..107 (rank 3)
+    L = gh.build_layer(cfg, bias_override=bias)
+    out = gh.gpu_forward(L).cpu().numpy()
+    assert np.all(out.view(np.uint16) == 0)
+
+
+def test_rank_shares_sum_to_full_layer():
+    """EP simulation on one GPU: the 8 rank shares' partial outputs add up to
+    the full layer's routed output; every (t, k) is local on one rank."""
+    base = moe_synth.scaled_config(2, T=96, H=256, I=128, seed=24)
+    full_cfg = moe_synth.scaled_config(2, T=96, H=256, I=128, seed=24, ep_size=1)
+    full = gh.gpu_forward(gh.build_layer(full_cfg)).cpu().numpy().astype(np.float64)
+    tot = np.zeros_like(full)
+    seen = None
+    for r in range(8):
+        L = gh.build_layer(base, rank=r)
+        st = gh.gpu_stages(L)
+        tot += st["out"].astype(np.float64)
+        m = (st["inv_pos"] >= 0).astype(int)
+        seen = m if seen is None else seen + m
+    assert np.all(seen == 1)
+    gh.assert_close(tot, full, "sum of rank shares", atol=4e-3)
+
+
+def test_dead_replica_sends_traffic_to_survivor():
+    """Section 6.3 replica table with the remote copy removed: every pair of
+    the replicated expert is computed on the local replica slot."""
+    import expert_router_gemm_amd as moe
+    cfg = small_cfg(5)
+    L = gh.build_layer(cfg)
+    rep = moe_synth.replica_expert(cfg)
+    off2, slot2 = moe.drop_replica(L.rep_off, L.rep_slot, rep, 0)
+    L.d["rep_off"], L.d["rep_slot"] = gh.to_dev(off2), gh.to_dev(slot2)
+    L.smap = moe.make_slot_map(L.d["rep_off"], L.d["rep_slot"], L.seed)
+    st = gh.gpu_stages(L)
+    n_rep = int((st["topk_idx"] == rep).sum())
+    assert st["counts"][len(L.slot_experts) - 1] == n_rep
+    ro, rs, _ = oracle.placement(cfg.E, cfg.ep_size, 0, replica_of=rep)
+    lo = ro[rep]
+    rs2 = np.delete(rs, lo)
+    ro2 = ro.copy()
+    ro2[rep + 1:] -= 1
+    slot = oracle.slot_map(st["topk_idx"], ro2, rs2, L.seed)
+    c, o, p, i = oracle.dispatch(slot, len(L.slot_experts))
+    assert np.array_equal(st["counts"], c) and np.array_equal(st["perm_src"], p)
+
+
+def test_fp8_codes_exhaustive_over_fp16_magnitudes():
+    """Dispatch quantises with per-row scale 448/amax: sweep rows built from
+    every positive finite fp16 value (with signs) and compare codes and
+    scales with the oracle's codec bit for bit."""
+    import expert_router_gemm_amd as moe
+    vals = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16)  # all positive finite
+    H = 512
+    n = (len(vals) + H - 1) // H
+    x = np.zeros(n * H, np.float16)
+    x[: len(vals)] = vals
+    rng = np.random.default_rng(5)
+    x = (x * np.where(rng.random(x.size) < 0.5, -1, 1).astype(np.float16)).reshape(n, H)
+    x = x[rng.permutation(n)]
+    T, K = n, 1
+    shape = moe.make_shape(hidden=H, inter=128, n_experts=1, top_k=1, n_slots=1,
+                           dispatch=moe.MOE_FP8_E4M3)
+    h = gh.to_dev(x)
+    idx = torch.zeros((T, K), dtype=torch.int32, device=gh.DEV)
+    rep_off = gh.to_dev(np.array([0, 1], np.int32))
+    rep_slot = gh.to_dev(np.array([0], np.int32))
+    sm = moe.make_slot_map(rep_off, rep_slot, 0)
+    xp = torch.empty((T, H), dtype=torch.uint8, device=gh.DEV)
+    xs = torch.empty((T,), dtype=torch.float32, device=gh.DEV)
+    counts = torch.empty(1, dtype=torch.int32, device=gh.DEV)
+    offs = torch.empty(2, dtype=torch.int32, device=gh.DEV)
+    perm = torch.empty(T, dtype=torch.int32, device=gh.DEV)
+    inv = torch.empty((T, K), dtype=torch.int32, device=gh.DEV)
+    ws = torch.empty(moe.moe_workspace_bytes(shape, T), dtype=torch.uint8, device=gh.DEV)
+    moe.moe_dispatch(shape, T, h, idx, sm, xp, xs, counts, offs, perm, inv, ws)
+    torch.cuda.synchronize()
+    q, s = oracle.quant_e4m3_rows(x)
+    assert np.array_equal(xs.cpu().numpy(), s)
+    assert np.array_equal(xp.cpu().numpy(), q)
+
+
+def test_dense_topk_equals_experts():
+    """top_k = E = S: every token uses every expert (dense softmax MoE)."""
+    cfg = moe_synth.scaled_config(1, T=40, H=256, I=128, E=8, K=8, n_shared=0, seed=25)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    assert np.all(st["counts"] == cfg.T)
+    ref = gh.oracle_forward(L)
+    gh.assert_close(st["out"], ref["out"], "dense layer", atol=1e-5, rtol=1e-4)
+
+
+# ------------------------------------------------------------ full sizes
+
+
+FULL_SAMPLE = {2: 32, 4: 24, 5: 32}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("n", [2, 5, 4])
+def test_full_size_sampled(n):
+    """Full workload sizes in the launch configuration the benchmark times;
+    routing of a token sample and the whole dispatch are compared exactly,
+    layer outputs on the sample within the output bar."""
+    cfg = moe_synth.config(n)
+    print(f"[case] full workload {n} {cfg.name}", flush=True)
+    L = gh.build_layer(cfg, keep_host_weights=False)
+    st = gh.gpu_stages(L)
+    out = gh.gpu_forward(L).cpu().numpy()
+    assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8))
+    rng = np.random.default_rng(n)
+    tok = np.sort(rng.choice(cfg.T, FULL_SAMPLE[n], replace=False))
+    tie = _check_routing(L, st, tokens=tok)
+    _check_dispatch(L, st)
+    ref = oracle_sample = gh.oracle_forward(L, tokens=tok)
+    _ = oracle_sample
+    err = gh.assert_close(out[tok], ref["out"], "layer output (sample)", rows=~tie)
+    print(f"[full] workload {n} P={st['P']} sample={len(tok)} max|d|={err:.3e}")
