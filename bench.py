@@ -1,0 +1,415 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE-layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+One step = one pass of the whole path over one batch resident in HBM:
+moe_route -> moe_dispatch -> moe_expert_ffn_up -> moe_expert_ffn_down ->
+(shared experts) -> moe_combine, through libmoe's C ABI on torch's current
+stream (the same kernels, in the same order, as moe_layer_forward, which is
+timed too and reported beside it).  The default workload is the EP=8
+rank-share decode batch: 256 tokens, hidden 7168, top-8 of 256 experts, the
+32 local experts' SwiGLU 7168x2048 weights in fp16.
+
+Printed: one JSON line with tokens/s, a roofline record for the dominant
+kernel (the gate/up weight stream, timed with HIP events on the stream it
+runs on) and the CPU oracle timed on the host for the same workload.
+
+--summarize-pmc FETCH_DIR WRITE_DIR: turn two `rocprofv3 --pmc FETCH_SIZE`
+/ `--pmc WRITE_SIZE` runs of this script (with --copy-calibration) into the
+HBM traffic record under profiles/ that later runs report.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+KERNEL_SOURCES = ["expert_router_gemm_amd/csrc/gemm_stream.hip",
+                  "expert_router_gemm_amd/csrc/common.h",
+                  "expert_router_gemm_amd/csrc/kernels.h"]
+DOMINANT = "stream_gemm_kernel"  # + the SwiGLU epilogue template argument
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ setup
+
+
+def setup(n: int):
+    import numpy as np
+    import torch
+
+    import expert_router_gemm_amd as moe
+    import moe_synth
+
+    cfg = moe_synth.config(n)
+    dev = "cuda:0"
+    rep = moe_synth.replica_expert(cfg)
+    rep_off, rep_slot, slot_experts = moe.build_slot_map(cfg.E, cfg.ep_size, cfg.ep_rank,
+                                                         [rep] if rep is not None else None)
+    S = len(slot_experts)
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.float16
+    t0 = time.time()
+    G = torch.empty((S, cfg.I, cfg.H), dtype=tdt, device=dev)
+    U = torch.empty((S, cfg.I, cfg.H), dtype=tdt, device=dev)
+    D = torch.empty((S, cfg.H, cfg.I), dtype=tdt, device=dev)
+    host_experts = {}
+    for s, e in enumerate(slot_experts):
+        g, u, d = moe_synth.gen_expert(cfg, int(e))
+        G[s].copy_(torch.from_numpy(g))
+        U[s].copy_(torch.from_numpy(u))
+        D[s].copy_(torch.from_numpy(d))
+        host_experts[int(e)] = (g, u, d)
+    h = moe_synth.gen_hidden(cfg)
+    wr = moe_synth.gen_router(cfg)
+    bias = moe_synth.gen_router_bias(cfg)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa
+    d = dict(h=t(h), wr=t(wr), bias=t(bias), G=G, U=U, D=D, ro=t(rep_off), rs=t(rep_slot))
+    shared = None
+    if cfg.n_shared:
+        shared = moe_synth.gen_shared_weights(cfg)
+        d.update(SG=t(shared[0]), SU=t(shared[1]), SD=t(shared[2]))
+    torch.cuda.synchronize()
+    log(f"[bench] generated and uploaded {cfg.name} in {time.time() - t0:.1f}s")
+    fp8 = cfg.dispatch == "fp8"
+    shape = moe.make_shape(hidden=cfg.H, inter=cfg.I, n_experts=cfg.E, top_k=cfg.K, n_slots=S,
+                           n_shared=cfg.n_shared,
+                           act=moe.MOE_F32 if cfg.dtype == "f32" else moe.MOE_F16,
+                           dispatch=moe.MOE_FP8_E4M3 if fp8 else None, shared=cfg.n_shared > 0)
+    T, K = cfg.T, cfg.K
+    bufs = dict(
+        ws=torch.empty(moe.moe_workspace_bytes(shape, T), dtype=torch.uint8, device=dev),
+        idx=torch.empty((T, K), dtype=torch.int32, device=dev),
+        tw=torch.empty((T, K), dtype=torch.float32, device=dev),
+        sg=torch.empty((T,), dtype=torch.float32, device=dev),
+        xp=torch.empty((T * K, cfg.H), dtype=torch.uint8 if fp8 else tdt, device=dev),
+        xs=torch.empty((T * K,), dtype=torch.float32, device=dev),
+        counts=torch.empty((S,), dtype=torch.int32, device=dev),
+        offsets=torch.empty((S + 1,), dtype=torch.int32, device=dev),
+        perm=torch.empty((T * K,), dtype=torch.int32, device=dev),
+        inv=torch.empty((T, K), dtype=torch.int32, device=dev),
+        hm=torch.empty((max(T * K, cfg.n_shared * T), cfg.I), dtype=tdt, device=dev),
+        y=torch.empty((T * K, cfg.H), dtype=tdt, device=dev),
+        shy=torch.empty((max(cfg.n_shared, 1) * T, cfg.H), dtype=tdt, device=dev),
+        shoff=t(np.arange(cfg.n_shared + 1, dtype=np.int32) * T),
+        out=torch.empty((T, cfg.H), dtype=tdt, device=dev),
+        out2=torch.empty((T, cfg.H), dtype=tdt, device=dev),
+    )
+    wmap = moe.make_weights(w_router=d["wr"], bias=d["bias"], w_gate=G, w_up=U, w_down=D,
+                            sh_gate=d.get("SG"), sh_up=d.get("SU"), sh_down=d.get("SD"))
+    smap = moe.make_slot_map(d["ro"], d["rs"], cfg.seed)
+    return dict(cfg=cfg, shape=shape, d=d, b=bufs, wmap=wmap, smap=smap, S=S, h=h, wr=wr,
+                bias=bias, host_experts=host_experts, shared=shared, rep=rep)
+
+
+def staged_step(ctx, ev=None):
+    """One pass of the hot path through the staged entry points; ev, if
+    given, is a list of 6 events recorded at the stage boundaries."""
+    import expert_router_gemm_amd as moe
+    cfg, shape, d, b = ctx["cfg"], ctx["shape"], ctx["d"], ctx["b"]
+    T, S = cfg.T, ctx["S"]
+    fp8 = cfg.dispatch == "fp8"
+    rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)  # noqa: E731
+    rec(0)
+    moe.moe_route(shape, T, d["h"], d["wr"], d["bias"], b["idx"], b["tw"],
+                  b["sg"] if cfg.n_shared else None, None, b["ws"])
+    rec(1)
+    moe.moe_dispatch(shape, T, d["h"], b["idx"], ctx["smap"], b["xp"], b["xs"] if fp8 else None,
+                     b["counts"], b["offsets"], b["perm"], b["inv"], b["ws"])
+    rec(2)
+    xdt = moe.MOE_FP8_E4M3 if fp8 else shape.act
+    moe.moe_expert_ffn_up(shape, S, T * cfg.K, b["xp"], xdt, b["xs"] if fp8 else None, 0,
+                          b["offsets"], d["G"], d["U"], b["hm"])
+    rec(3)
+    moe.moe_expert_ffn_down(shape, S, T * cfg.K, b["hm"], b["offsets"], d["D"], b["y"])
+    rec(4)
+    shy = None
+    if cfg.n_shared:
+        moe.moe_expert_ffn(shape, cfg.n_shared, cfg.n_shared * T, d["h"], shape.act, None, 1,
+                           b["shoff"], d["SG"], d["SU"], d["SD"], b["shy"], b["ws"])
+        shy = b["shy"]
+    moe.moe_combine(shape, T, b["y"], b["inv"], b["tw"], shy, b["sg"] if cfg.n_shared else None,
+                    b["out"])
+    rec(5)
+
+
+def fused_step(ctx):
+    import expert_router_gemm_amd as moe
+    moe.moe_layer_forward(ctx["shape"], ctx["wmap"], ctx["smap"], ctx["cfg"].T, ctx["d"]["h"],
+                          ctx["b"]["out2"], ctx["b"]["ws"])
+
+
+# ------------------------------------------------------------------ accounting
+
+
+def algorithmic_work(ctx):
+    """Per-step algorithmic bytes (and FLOPs) of each stage, from the routing
+    the step actually produced (same input every step)."""
+    cfg = ctx["cfg"]
+    counts = ctx["b"]["counts"].cpu().numpy()
+    P = int(counts.sum())
+    touched = int((counts > 0).sum())
+    isz = 4 if cfg.dtype == "f32" else 2
+    xsz = 1 if cfg.dispatch == "fp8" else isz
+    H, I, E, T, K = cfg.H, cfg.I, cfg.E, cfg.T, cfg.K
+    expert_bytes = 3 * H * I * isz
+    up = dict(bytes=touched * 2 * I * H * isz + P * H * xsz + P * 4 * (xsz == 1) + P * I * isz,
+              flops=2 * 2 * P * H * I)
+    down = dict(bytes=touched * H * I * isz + P * I * isz + P * H * isz, flops=2 * P * H * I)
+    route = dict(bytes=(E + (cfg.n_shared > 0)) * H * isz + T * H * isz + T * K * 8,
+                 flops=2 * T * H * (E + (cfg.n_shared > 0)))
+    shared = dict(bytes=cfg.n_shared * expert_bytes + cfg.n_shared * T * (H * isz * 2 + I * isz),
+                  flops=cfg.n_shared * 6 * T * H * I)
+    layer_bytes = (touched * expert_bytes + shared["bytes"] + route["bytes"]
+                   + T * H * isz  # output
+                   + 2 * P * H * xsz + 2 * P * H * isz)  # dispatch copy + y round trip
+    return dict(P=P, touched=touched, up=up, down=down, route=route, shared=shared,
+                layer_bytes=layer_bytes,
+                layer_flops=up["flops"] + down["flops"] + route["flops"] + shared["flops"])
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 PMC record, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"traffic_stream_gemm_swiglu_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+
+def cpu_baseline(ctx, budget_s: float = 20.0):
+    """The oracle (plain C, single thread) on the same workload's tokens, on
+    the host; tokens are taken in order until ~budget_s of CPU work."""
+    import numpy as np
+
+    import oracle
+    cfg = ctx["cfg"]
+    ro, rs, se = oracle.placement(cfg.E, cfg.ep_size, cfg.ep_rank, replica_of=ctx["rep"])
+    sw = [ctx["host_experts"][int(e)] for e in se]
+    done, t_used, n = 0, 0.0, 16
+    while done < cfg.T and t_used < budget_s:
+        n = min(n, cfg.T - done)
+        tok = np.arange(done, done + n, dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.layer_forward(h=np.ascontiguousarray(ctx["h"][tok]), w_router=ctx["wr"][: cfg.E],
+                             bias=ctx["bias"], w_sg=ctx["wr"][cfg.E] if cfg.n_shared else None,
+                             slot_weights=sw, shared=ctx["shared"], rep_off=ro, rep_slot=rs,
+                             seed=cfg.seed, K=cfg.K, fp8_dispatch=cfg.dispatch == "fp8",
+                             tok_ids=tok)
+        t_used += time.perf_counter() - t0
+        done += n
+        n *= 2
+    return dict(value=done / t_used, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {done} of {cfg.T} tokens of {cfg.name} "
+                       f"({t_used:.1f} s, single-threaded plain C, fp64 accumulation)")
+
+
+# ------------------------------------------------------------------ PMC summary
+
+
+def is_swiglu_stream(kernel_name: str) -> bool:
+    """The gate/up launch of the stream GEMM: template arguments NM = 2,
+    EPI = SwiGLU (1), in demangled or mangled form."""
+    import re
+    if DOMINANT not in kernel_name:
+        return False
+    n = kernel_name.replace(" ", "")
+    return bool(re.search(r"stream_gemm_kernel<[^,]+,\d+,2,1,", n) or re.search(r"Li2ELi1ELi\d+E", n))
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant
+    kernel, each scaled by what the counter reads for the calibration copy
+    kernel of known size; writes profiles/traffic_...json."""
+    import csv
+
+    def read(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                rows += list(csv.DictReader(fh))
+        dom, cp = [], []
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            v = float(r["Counter_Value"])
+            if is_swiglu_stream(name):
+                dom.append(v)
+            elif "elementwise" in name.lower():
+                cp.append(v)
+        return dom, cp
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        dom, cp = read(d, counter)
+        if not dom or not cp:
+            raise SystemExit(f"no {counter} rows for the dominant or copy kernel in {d}")
+        # the calibration copy reads and writes copy_bytes
+        factor = copy_bytes / 1024.0 / statistics.median(cp)
+        out[counter] = dict(kib_per_launch=statistics.median(dom), copy_kib=statistics.median(cp),
+                            copy_factor=factor,
+                            bytes_per_launch=statistics.median(dom) * 1024.0 * factor)
+    rec = dict(kernel=f"{DOMINANT} (SwiGLU gate/up weight stream)", workload=workload,
+               kernel_source_hash=kernel_source_hash(), counters=out,
+               traffic_bytes_per_launch=out["FETCH_SIZE"]["bytes_per_launch"]
+               + out["WRITE_SIZE"]["bytes_per_launch"])
+    p = os.path.join(ROOT, "profiles", f"traffic_stream_gemm_swiglu_{workload}.json")
+    with open(p, "w") as f:
+        json.dump(rec, f, indent=2)
+    print(json.dumps(rec, indent=2))
+
+
+# ------------------------------------------------------------------ main
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (PMC scale)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        import moe_synth
+        summarize_pmc(*args.summarize_pmc, moe_synth.config(args.workload).name, 1 << 30)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}); see the sharding note in DESIGN.md", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import expert_router_gemm_amd as moe
+    moe.lib()
+    ctx = setup(args.workload)
+    cfg = ctx["cfg"]
+
+    for _ in range(args.warmup):
+        staged_step(ctx)
+        fused_step(ctx)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        staged_step(ctx, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] timed {K} staged steps: {wall * 1e3 / K:.3f} ms/step")
+
+    # the fused entry point, same kernels
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        fused_step(ctx)
+    e1.record()
+    torch.cuda.synchronize()
+    fused_ms = e0.elapsed_time(e1) / K
+    same = bool(torch.equal(ctx["b"]["out"], ctx["b"]["out2"]))
+
+    names = ["route", "dispatch", "ffn_up", "ffn_down", "shared_ffn+combine"]
+    stage_ms = {n: statistics.median(ev[j].elapsed_time(ev[j + 1]) for ev in evs)
+                for j, n in enumerate(names)}
+    up_ms = statistics.mean(ev[2].elapsed_time(ev[3]) for ev in evs)
+    work = algorithmic_work(ctx)
+    ms_per_step = wall * 1e3 / K
+    value = cfg.T / (ms_per_step / 1e3)
+
+    decode = args.workload != 4
+    if decode:
+        achieved = work["up"]["bytes"] / (up_ms / 1e3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=load_traffic(cfg.name))
+    else:
+        achieved = work["up"]["flops"] / (up_ms / 1e3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_F16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                    traffic=load_traffic(cfg.name))
+    roof.update(kernel="stream_gemm_kernel (SwiGLU gate/up)", launch_ms=round(up_ms, 4),
+                algorithmic_bytes=work["up"]["bytes"], algorithmic_flops=work["up"]["flops"])
+
+    if args.copy_calibration:
+        # a plain elementwise kernel that reads 1 GiB and writes 1 GiB
+        a = torch.ones(1 << 29, dtype=torch.float16, device="cuda:0")
+        bb = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.mul(a, 1.0, out=bb)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(ctx, args.cpu_budget)
+
+    layer_gbs = work["layer_bytes"] / (ms_per_step / 1e3) / 1e9
+    rec = {
+        "metric": "MoE-layer tokens/s at 1 GPU + % HBM BW (decode) / % MFMA peak (prefill)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "inter": cfg.I,
+                   "experts": cfg.E, "top_k": cfg.K, "local_slots": ctx["S"],
+                   "shared_experts": cfg.n_shared, "dispatch": cfg.dispatch,
+                   "ep_size": cfg.ep_size, "ep_rank": cfg.ep_rank},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layer": {"hbm_gbs": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                  "algorithmic_bytes": work["layer_bytes"], "rows": work["P"],
+                  "touched_slots": work["touched"], "fused_entry_ms": round(fused_ms, 4),
+                  "fused_equals_staged": same,
+                  "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}},
+    }
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
