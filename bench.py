@@ -56,7 +56,7 @@ def log(msg):
 # ------------------------------------------------------------------ setup
 
 
-def setup(n: int):
+def setup(n: int, keep_host: bool = True):
     import numpy as np
     import torch
 
@@ -75,12 +75,12 @@ def setup(n: int):
     U = torch.empty((S, cfg.I, cfg.H), dtype=tdt, device=dev)
     D = torch.empty((S, cfg.H, cfg.I), dtype=tdt, device=dev)
     host_experts = {}
-    for s, e in enumerate(slot_experts):
-        g, u, d = moe_synth.gen_expert(cfg, int(e))
+    for s, (e, (g, u, d)) in enumerate(moe_synth.iter_experts(cfg, slot_experts)):
         G[s].copy_(torch.from_numpy(g))
         U[s].copy_(torch.from_numpy(u))
         D[s].copy_(torch.from_numpy(d))
-        host_experts[int(e)] = (g, u, d)
+        if keep_host:
+            host_experts[e] = (g, u, d)
     h = moe_synth.gen_hidden(cfg)
     wr = moe_synth.gen_router(cfg)
     bias = moe_synth.gen_router_bias(cfg)

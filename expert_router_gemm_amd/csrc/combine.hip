@@ -6,8 +6,10 @@
 // output dtype.  Pairs computed on other GPUs (inv_pos = -1) are skipped, so a
 // token with no local pair and no shared term gets exact zeros.
 //
-// One block of 128 threads per token; each thread owns 8 consecutive
-// features per step (16-byte fp16 loads, 2 x 16-byte fp32 loads).
+// One block per token with one thread per 8 consecutive features (up to
+// 1024 threads: 896 for hidden 7168), so every y row of the token is read
+// once with 16-byte loads; the token's local pairs are compacted in k order
+// into LDS first.
 #include "common.h"
 #include "kernels.h"
 
@@ -48,35 +50,50 @@ __device__ __forceinline__ void store8<float>(float *p, const float v[8]) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
+    __shared__ int rows[16];
+    __shared__ float gates[16];
+    __shared__ int npairs;
     const int t = blockIdx.x;
-    const int32_t *ip = a.inv_pos + (size_t)t * a.K;
-    const float *wp = a.topk_w + (size_t)t * a.K;
+    if (threadIdx.x == 0) {
+        // local pairs of this token, compacted in k order
+        int n = 0;
+        for (int k = 0; k < a.K; ++k) {
+            const int r = a.inv_pos[(size_t)t * a.K + k];
+            if (r >= 0) {
+                rows[n] = r;
+                gates[n] = a.topk_w[(size_t)t * a.K + k];
+                ++n;
+            }
+        }
+        npairs = n;
+    }
+    __syncthreads();
+    const int np = npairs;
     const T *y = reinterpret_cast<const T *>(a.y);
     const T *shy = reinterpret_cast<const T *>(a.shared_y);
-    const float gs = (shy && a.n_shared > 0) ? a.shared_gate[t] : 0.0f;
+    const bool sh = shy && a.n_shared > 0;
+    const float gs = sh ? a.shared_gate[t] : 0.0f;
     T *out = reinterpret_cast<T *>(a.out) + (size_t)t * a.H;
-    for (int i = threadIdx.x * 8; i < a.H; i += 128 * 8) {
+    for (int i = threadIdx.x * 8; i < a.H; i += blockDim.x * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < a.K; ++k) {
-            const int r = ip[k];
-            if (r < 0) continue;
-            const float g = wp[k];
+        for (int q = 0; q < np; ++q) {
             float v[8];
-            load8<T>(y + (size_t)r * a.H + i, v);
+            load8<T>(y + (size_t)rows[q] * a.H + i, v);
+            const float g = gates[q];
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[j] += g * v[j];
         }
-        if (shy && a.n_shared > 0) {
-            float sh[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (sh) {
+            float sv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int s = 0; s < a.n_shared; ++s) {
                 float v[8];
                 load8<T>(shy + ((size_t)s * a.T + t) * a.H + i, v);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) sh[j] += v[j];
+                for (int j = 0; j < 8; ++j) sv[j] += v[j];
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] += gs * sh[j];
+            for (int j = 0; j < 8; ++j) acc[j] += gs * sv[j];
         }
         store8<T>(out + i, acc);
     }
@@ -86,10 +103,13 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
+    // one thread per 8 features, up to 1024 threads (whole waves)
+    int threads = ((a.H / 8 + 63) / 64) * 64;
+    if (threads > 1024) threads = 1024;
     if (a.dtype == DT_F16)
-        hipLaunchKernelGGL(combine_kernel<f16>, dim3(a.T), dim3(128), 0, s, a);
+        hipLaunchKernelGGL(combine_kernel<f16>, dim3(a.T), dim3(threads), 0, s, a);
     else
-        hipLaunchKernelGGL(combine_kernel<float>, dim3(a.T), dim3(128), 0, s, a);
+        hipLaunchKernelGGL(combine_kernel<float>, dim3(a.T), dim3(threads), 0, s, a);
     return hipGetLastError();
 }
 

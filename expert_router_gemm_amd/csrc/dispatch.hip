@@ -10,7 +10,10 @@
 // Section 2.3 notes FP8 halves the dispatched bytes: with x_dtype = FP8 each
 // row is stored as E4M3 codes with one fp32 scale.
 //
-// Three kernels, all deterministic (no order-dependent atomics):
+// Decode-sized batches (T <= 1024 tokens, S <= 256 slots) run steps 1-2 and
+// the index half of step 3 in a single 1024-thread block, then the row copy.
+// Larger batches use three kernels.  All deterministic (no order-dependent
+// atomics):
 //  1. rank:    one wave per 64-token chunk.  Each (token, k) sets its lane bit
 //              in a per-slot 64-bit LDS mask (an OR, so arrival order cannot
 //              matter); the pair's rank inside the chunk is the popcount of
@@ -118,6 +121,97 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(DispatchArgs a) {
     }
 }
 
+// Decode-sized batches (T <= 1024, S <= 256): rank, scan and the index
+// outputs in one block of 1024 threads; wave w owns tokens [64w, 64w + 64).
+constexpr int kSmallT = 1024, kSmallS = 256;
+
+constexpr int kSmallE = 1024, kSmallNnz = 2048;
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
+    __shared__ unsigned long long masks[kSmallT / 64][kSmallS];
+    __shared__ int base[kSmallT / 64][kSmallS];  // rows of earlier chunks, per slot
+    __shared__ int offs[kSmallS + 1];
+    __shared__ int scan[2][kSmallS];
+    __shared__ int roff[kSmallE + 1];            // slot table staged in LDS
+    __shared__ int rslot[kSmallNnz];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+    const int C = (a.T + 63) / 64;
+    for (int i = tid; i < (kSmallT / 64) * kSmallS; i += 1024) (&masks[0][0])[i] = 0ull;
+    for (int i = tid; i <= a.E; i += 1024) roff[i] = a.rep_off[i];
+    const int nnz = a.rep_off[a.E];
+    const bool table_in_lds = nnz >= 0 && nnz <= kSmallNnz;
+    if (table_in_lds)
+        for (int i = tid; i < nnz; i += 1024) rslot[i] = a.rep_slot[i];
+    __syncthreads();
+    const int t = tid;
+    const unsigned long long bit = 1ull << lane;
+    if (t < a.T) {
+        int ex[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) ex[k] = k < a.K ? a.topk_idx[(size_t)t * a.K + k] : -1;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (k >= a.K) break;
+            const int e = ex[k];
+            int sl = -1;
+            if (e >= 0 && e < a.E) {
+                const int lo = roff[e], n = roff[e + 1] - lo;
+                if (n > 0) {
+                    int r = 0;
+                    if (n > 1)
+                        r = (int)(splitmix64(a.seed ^ ((uint64_t)t * (uint64_t)a.K + (uint64_t)k)) %
+                                  (uint64_t)n);
+                    sl = table_in_lds ? rslot[lo + r] : a.rep_slot[lo + r];
+                    if (sl < 0 || sl >= a.S) sl = -1;
+                }
+            }
+            a.pair_code[(size_t)t * a.K + k] = sl;
+            if (sl >= 0) atomicOr(&masks[wave][sl], bit);
+        }
+    }
+    __syncthreads();
+    // per slot: exclusive scan over chunks, total
+    int tot = 0;
+    if (tid < a.S) {
+        for (int c = 0; c < C; ++c) {
+            base[c][tid] = tot;
+            tot += __popcll(masks[c][tid]);
+        }
+        a.counts[tid] = tot;
+    }
+    // exclusive scan of totals over slots
+    int cur = 0;
+    if (tid < kSmallS) scan[0][tid] = tot;
+    __syncthreads();
+    for (int o = 1; o < kSmallS; o <<= 1) {
+        if (tid < kSmallS) scan[cur ^ 1][tid] = scan[cur][tid] + (tid >= o ? scan[cur][tid - o] : 0);
+        cur ^= 1;
+        __syncthreads();
+    }
+    if (tid < a.S) {
+        const int incl = scan[cur][tid];
+        offs[tid] = incl - tot;
+        a.offsets[tid] = incl - tot;
+        if (tid == a.S - 1) {
+            offs[a.S] = incl;
+            a.offsets[a.S] = incl;
+        }
+    }
+    __syncthreads();
+    if (t < a.T)
+        for (int k = 0; k < a.K; ++k) {
+            const size_t p = (size_t)t * a.K + k;
+            const int sl = a.pair_code[p];  // written by this thread above
+            if (sl < 0) {
+                a.inv_pos[p] = -1;
+                continue;
+            }
+            const int row = offs[sl] + base[wave][sl] + __popcll(masks[wave][sl] & (bit - 1ull));
+            a.inv_pos[p] = row;
+            a.perm_src[row] = (int32_t)p;
+        }
+}
+
 __device__ __forceinline__ uint32_t e4m3_rne(float v) {
     // |v| <= 448.  OCP E4M3: bias 7, 3 mantissa bits, subnormals below 2^-6.
     const uint32_t b = __float_as_uint(v);
@@ -134,22 +228,29 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
     return sign | (q - ((127u - 7u) << 3));
 }
 
-template <typename T, int XM>
+// FROM_INV: rows were already placed (small path): read them from inv_pos.
+template <typename T, int XM, bool FROM_INV>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(DispatchArgs a) {
     const size_t p = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (p >= (size_t)a.T * a.K) return;
     const int lane = lane_id();
-    const int code = __builtin_amdgcn_readfirstlane(a.pair_code[p]);
-    if (code < 0) {
-        if (lane == 0) a.inv_pos[p] = -1;
-        return;
-    }
     const int t = (int)(p / a.K);
-    const int s = code >> 6, rank = code & 63;
-    const int row = __builtin_amdgcn_readfirstlane(a.chunk_counts[(size_t)(t >> 6) * a.S + s] + rank);
-    if (lane == 0) {
-        a.inv_pos[p] = row;
-        a.perm_src[row] = (int32_t)p;
+    int row;
+    if (FROM_INV) {
+        row = __builtin_amdgcn_readfirstlane(a.inv_pos[p]);
+        if (row < 0) return;
+    } else {
+        const int code = __builtin_amdgcn_readfirstlane(a.pair_code[p]);
+        if (code < 0) {
+            if (lane == 0) a.inv_pos[p] = -1;
+            return;
+        }
+        const int s = code >> 6, rank = code & 63;
+        row = __builtin_amdgcn_readfirstlane(a.chunk_counts[(size_t)(t >> 6) * a.S + s] + rank);
+        if (lane == 0) {
+            a.inv_pos[p] = row;
+            a.perm_src[row] = (int32_t)p;
+        }
     }
     constexpr int EL = Frag<T>::kElems;
     const T *src = reinterpret_cast<const T *>(a.h) + (size_t)t * a.H;
@@ -198,10 +299,29 @@ size_t dispatch_scratch_bytes(int T, int K, int S) {
     return a;
 }
 
+template <bool FROM_INV>
+hipError_t launch_scatter(const DispatchArgs &a, hipStream_t s) {
+    const size_t pairs = (size_t)a.T * a.K;
+    dim3 grid((unsigned)((pairs + 3) / 4));
+    if (a.dtype == DT_F32)
+        hipLaunchKernelGGL((dispatch_scatter_kernel<float, DT_F32, FROM_INV>), grid, dim3(256), 0, s, a);
+    else if (a.x_dtype == DT_FP8)
+        hipLaunchKernelGGL((dispatch_scatter_kernel<f16, DT_FP8, FROM_INV>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((dispatch_scatter_kernel<f16, DT_F16, FROM_INV>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
     if (a.T < 0) return hipErrorInvalidValue;
     const int C = (a.T + 63) / 64;
     hipError_t e;
+    if (a.T > 0 && a.T <= kSmallT && a.S <= kSmallS && a.E <= kSmallE) {
+        hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_scatter<true>(a, s);
+    }
     if (C > 0) {
         hipLaunchKernelGGL(dispatch_rank_kernel, dim3((C + 3) / 4), dim3(256),
                            (size_t)4 * a.S * sizeof(unsigned long long), s, a);
@@ -213,15 +333,7 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.T == 0) return hipSuccess;
-    const size_t pairs = (size_t)a.T * a.K;
-    dim3 grid((unsigned)((pairs + 3) / 4));
-    if (a.dtype == DT_F32)
-        hipLaunchKernelGGL((dispatch_scatter_kernel<float, DT_F32>), grid, dim3(256), 0, s, a);
-    else if (a.x_dtype == DT_FP8)
-        hipLaunchKernelGGL((dispatch_scatter_kernel<f16, DT_FP8>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((dispatch_scatter_kernel<f16, DT_F16>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_scatter<false>(a, s);
 }
 
 }  // namespace moe

@@ -12,7 +12,10 @@
 // Work decomposition
 //   blockIdx.x  64 output features (4 waves x 16 features each)
 //   blockIdx.y  group g (expert slot)
-//   blockIdx.z  first row block; row blocks of 64 rows are strided by gridDim.z
+//   blockIdx.z  (first row block) * ksplit + K slice; row blocks of 64 rows
+//               are strided by gridDim.z / ksplit.  ksplit > 1 (router only)
+//               writes one fp32 partial per K slice; the top-K kernel sums
+//               them in slice order, so the result stays deterministic.
 // Each wave owns 16 features and runs the whole K loop for them, so no
 // cross-wave reduction is needed.  The 64 rows of a row block are processed
 // in MT = 1, 2 or 4 tiles of 16, chosen from the rows actually present, so
@@ -54,7 +57,7 @@ struct XFrag<f16, DT_FP8> {  // 8 fp8 codes, decoded to fp16 * 2^-8
 
 template <typename TW, int XM, int NM, int EPI, int MT, int U>
 __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, int rstart,
-                                            int r0, int r1) {
+                                            int r0, int r1, int kz) {
     typedef typename Frag<TW>::vec V;
     typedef XFrag<TW, XM> XF;
     typedef typename XF::raw XR;
@@ -63,14 +66,16 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
     const int lane = lane_id();
     const int lr = lane & 15, lg = lane >> 4;
     const int K = a.K;
-    const int NC = K / CK;
+    const int KS = K / a.ksplit;  // this block's K slice: [kz*KS, (kz+1)*KS)
+    const int NC = KS / CK;
 
     // weight rows (clamped: rows past N are read but never stored)
     const TW *wp[NM];
     {
         int wrow = f0 + lr;
         if (wrow > a.N - 1) wrow = a.N - 1;
-        const size_t off = (size_t)g * a.w_group_stride + (size_t)wrow * K + (size_t)lg * EL;
+        const size_t off = (size_t)g * a.w_group_stride + (size_t)wrow * K + (size_t)kz * KS +
+                           (size_t)lg * EL;
         wp[0] = reinterpret_cast<const TW *>(a.w0) + off;
         if (NM > 1) wp[NM - 1] = reinterpret_cast<const TW *>(a.w1) + off;
     }
@@ -83,7 +88,7 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
         rows[t] = r;
         int rc = r < r1 ? r : r1 - 1;
         int xr = a.x_broadcast ? rc - r0 : rc;
-        xo[t] = (size_t)xr * K + (size_t)lg * EL;
+        xo[t] = (size_t)xr * K + (size_t)kz * KS + (size_t)lg * EL;
     }
 
     f32x4 acc[NM][MT];
@@ -132,11 +137,12 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
         float sc = 1.0f;
         if (XM == DT_FP8) sc = a.x_scale[r] * 256.0f;  // undo the 2^-8 of the decode
         if (EPI == EPI_LOGITS) {
-            float *o = reinterpret_cast<float *>(a.out) + (size_t)r * a.out_ld;
+            float *o = reinterpret_cast<float *>(a.out) + (size_t)kz * a.split_stride +
+                       (size_t)r * a.out_ld;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int f = fb + j;
-                if (f < a.N) o[f] = acc[0][t][j] + (a.bias && f < a.n_bias ? a.bias[f] : 0.0f);
+                if (f < a.N) o[f] = acc[0][t][j];
             }
         } else {
             float v[4];
@@ -166,6 +172,9 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
     const int f0 = blockIdx.x * 64 + wave * 16;
     if (f0 >= a.N) return;
     const int g = blockIdx.y;
+    const int kz = blockIdx.z % a.ksplit;  // K slice
+    const int zr = blockIdx.z / a.ksplit;  // first row block
+    const int zn = gridDim.z / a.ksplit;   // row-block stride
     int r0, r1;
     if (a.offsets) {
         r0 = a.offsets[g];
@@ -174,23 +183,24 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
         r0 = g * a.rows_per_group;
         r1 = r0 + a.rows_per_group;
     }
-    for (int rb = blockIdx.z; r0 + rb * 64 < r1; rb += gridDim.z) {
+    for (int rb = zr; r0 + rb * 64 < r1; rb += zn) {
         const int rs = r0 + rb * 64;
         const int n = r1 - rs;
         if (n <= 16)
-            stream_pass<TW, XM, NM, EPI, 1, U>(a, g, f0, rs, r0, r1);
+            stream_pass<TW, XM, NM, EPI, 1, U>(a, g, f0, rs, r0, r1, kz);
         else if (n <= 32)
-            stream_pass<TW, XM, NM, EPI, 2, U>(a, g, f0, rs, r0, r1);
+            stream_pass<TW, XM, NM, EPI, 2, U>(a, g, f0, rs, r0, r1, kz);
         else
-            stream_pass<TW, XM, NM, EPI, 4, (U > 2 ? 2 : U)>(a, g, f0, rs, r0, r1);
+            stream_pass<TW, XM, NM, EPI, 4, (U > 2 ? 2 : U)>(a, g, f0, rs, r0, r1, kz);
     }
 }
 
 template <typename TW, int XM, int NM, int EPI>
 hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t s) {
-    dim3 grid((a.N + 63) / 64, n_groups, zblocks);
+    dim3 grid((a.N + 63) / 64, n_groups, zblocks * a.ksplit);
     constexpr int CK = 4 * Frag<TW>::kElems;
-    const int NC = a.K / CK;
+    const int NC = a.K / a.ksplit / CK;
+    if (a.ksplit < 1 || a.K % (a.ksplit * 4 * CK) != 0) return hipErrorInvalidValue;
     if (NC % 8 == 0)
         hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NM, EPI, 4>), grid, dim3(256), 0, s, a);
     else

@@ -21,9 +21,9 @@ struct StreamArgs {
     size_t w_group_stride;  // elements from one group's matrix to the next
     void *out;              // [rows][out_ld]
     int out_ld;
-    const float *bias;      // LOGITS: fp32 bias for columns < n_bias
-    int n_bias;
     int N, K;
+    int ksplit;             // LOGITS only: K is split in ksplit equal slices;
+    size_t split_stride;    // slice z writes out + z * split_stride (fp32)
 };
 
 // dtype: DT_F16 / DT_F32 (weights and output); x_dtype: dtype or DT_FP8.
@@ -31,12 +31,19 @@ struct StreamArgs {
 hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int mode,
                               int n_groups, int zblocks, hipStream_t s);
 
+// LDS-tiled persistent variant for groups of many rows (fp16 only, no K
+// split).  max_tiles bounds the total 128-row tiles (sizes the grid).
+bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype);
+hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,
+                             hipStream_t s);
+
 // ---------------------------------------------------------------- routing
-// logits [T][ld] fp32 (E expert columns, then the shared-gate column if
-// has_gate) -> topk_idx/topk_w [T][K], shared_gate [T], logits_out [T][E].
-hipError_t launch_topk(const float *logits, int ld, int T, int E, int K, int has_gate,
-                       int32_t *topk_idx, float *topk_w, float *shared_gate,
-                       float *logits_out, hipStream_t s);
+// Partial logits parts[z][T][ld] fp32, z < nsplit (E expert columns, then
+// the shared-gate column if has_gate), summed in z order, plus bias ->
+// topk_idx/topk_w [T][K], shared_gate [T], logits_out [T][E].
+hipError_t launch_topk(const float *parts, int nsplit, size_t split_stride, int ld, int T,
+                       int E, int K, int has_gate, const float *bias, int32_t *topk_idx,
+                       float *topk_w, float *shared_gate, float *logits_out, hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch
 struct DispatchArgs {

@@ -26,6 +26,25 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline int act_bytes(const moe_shape &s) { return s.act == MOE_F32 ? 4 : 2; }
 inline int has_gate(const moe_shape &s) { return (s.flags & MOE_F_SHARED) ? 1 : 0; }
 
+// Router K split: the smallest split (K slice a multiple of 4 MFMA steps)
+// that gives at least 256 workgroups, else the largest one up to 16.
+int router_ksplit(const moe_shape &s, int T) {
+    const int N = s.n_experts + has_gate(s);
+    const long base = (long)((N + 63) / 64) * ((T + 63) / 64);
+    const int gran = 4 * (s.act == MOE_F32 ? 16 : 32);
+    int best = 1;
+    for (int d = 1; d <= 16; ++d) {
+        if (s.hidden % (d * gran)) continue;
+        best = d;
+        if (base * d >= 256) break;
+    }
+    return best;
+}
+
+size_t route_ws_bytes(const moe_shape &s, int T) {
+    return up256((size_t)router_ksplit(s, T) * T * (s.n_experts + has_gate(s)) * 4);
+}
+
 moe_status check_shape(const moe_shape *s) {
     if (!s) return MOE_ERR_INVALID_ARG;
     if (s->flags & ~MOE_F_SHARED) return MOE_ERR_INVALID_ARG;
@@ -87,7 +106,7 @@ Layout layout(const moe_shape &s, int T) {
         o += up256(bytes);
         return at;
     };
-    L.logits = take((size_t)T * (s.n_experts + 1) * 4);
+    L.logits = take(route_ws_bytes(s, T));
     L.topk_idx = take(TK * 4);
     L.topk_w = take(TK * 4);
     L.shared_gate = take((size_t)T * 4);
@@ -109,6 +128,18 @@ Layout layout(const moe_shape &s, int T) {
 template <typename P>
 inline P at(void *ws, size_t off) {
     return reinterpret_cast<P>(reinterpret_cast<char *>(ws) + off);
+}
+
+// Groups expected to hold at least this many rows run on the LDS-tiled
+// kernel (weight tiles reused across rows); fewer rows stream the weights.
+constexpr int kTiledMinRows = 64;
+constexpr int kTiledRouterMinTokens = 2048;
+
+hipError_t gemm(const StreamArgs &a, int dtype, int x_dtype, int mode, int n_groups, int zblocks,
+                long est_rows, long cap_rows, hipStream_t st) {
+    if (est_rows >= kTiledMinRows && tiled_gemm_supported(a, dtype, x_dtype))
+        return launch_tiled_gemm(a, mode, n_groups, cap_rows / 128 + n_groups, st);
+    return launch_stream_gemm(a, dtype, x_dtype, mode, n_groups, zblocks, st);
 }
 
 int ffn_zblocks(int cap_rows, int n_groups) {
@@ -137,15 +168,21 @@ hipError_t route_impl(const moe_shape &s, int T, const void *h, const void *w_ro
     a.w_group_stride = 0;
     a.out = logits_buf;
     a.out_ld = N;
-    a.bias = bias;
-    a.n_bias = s.n_experts;
     a.N = N;
     a.K = s.hidden;
-    const int zb = (T + 63) / 64 < 65535 ? (T + 63) / 64 : 65535;  // rows stride by gridDim.z
-    hipError_t e = launch_stream_gemm(a, s.act, s.act, STREAM_LOGITS, 1, zb, st);
+    a.ksplit = router_ksplit(s, T);
+    a.split_stride = (size_t)T * N;
+    hipError_t e;
+    if (a.ksplit == 1 && T >= kTiledRouterMinTokens && tiled_gemm_supported(a, s.act, s.act)) {
+        e = launch_tiled_gemm(a, STREAM_LOGITS, 1, (T + 127) / 128, st);
+    } else {
+        const int rb = (T + 63) / 64;
+        const int zb = rb * a.ksplit <= 65535 ? rb : 65535 / a.ksplit;  // rows stride by gridDim.z
+        e = launch_stream_gemm(a, s.act, s.act, STREAM_LOGITS, 1, zb, st);
+    }
     if (e != hipSuccess) return e;
-    return launch_topk(logits_buf, N, T, s.n_experts, s.top_k, gate, topk_idx, topk_w,
-                       shared_gate, logits_user, st);
+    return launch_topk(logits_buf, a.ksplit, a.split_stride, N, T, s.n_experts, s.top_k, gate,
+                       bias, topk_idx, topk_w, shared_gate, logits_user, st);
 }
 
 hipError_t dispatch_impl(const moe_shape &s, int T, const void *h, const int32_t *topk_idx,
@@ -177,10 +214,10 @@ hipError_t dispatch_impl(const moe_shape &s, int T, const void *h, const int32_t
     return launch_dispatch(d, st);
 }
 
-hipError_t ffn_up_impl(const moe_shape &s, int n_groups, int zblocks, const void *x, int x_dtype,
-                       const float *x_scale, int x_broadcast, const int32_t *offsets,
-                       int rows_per_group, const void *w_gate, const void *w_up, void *hm,
-                       hipStream_t st) {
+hipError_t ffn_up_impl(const moe_shape &s, int n_groups, int zblocks, long est_rows,
+                       long cap_rows, const void *x, int x_dtype, const float *x_scale,
+                       int x_broadcast, const int32_t *offsets, int rows_per_group,
+                       const void *w_gate, const void *w_up, void *hm, hipStream_t st) {
     StreamArgs a{};
     a.x = x;
     a.x_scale = x_scale;
@@ -194,12 +231,13 @@ hipError_t ffn_up_impl(const moe_shape &s, int n_groups, int zblocks, const void
     a.out_ld = s.inter;
     a.N = s.inter;
     a.K = s.hidden;
-    return launch_stream_gemm(a, s.act, x_dtype, STREAM_SWIGLU, n_groups, zblocks, st);
+    a.ksplit = 1;
+    return gemm(a, s.act, x_dtype, STREAM_SWIGLU, n_groups, zblocks, est_rows, cap_rows, st);
 }
 
-hipError_t ffn_down_impl(const moe_shape &s, int n_groups, int zblocks, const void *hm,
-                         const int32_t *offsets, int rows_per_group, const void *w_down, void *y,
-                         hipStream_t st) {
+hipError_t ffn_down_impl(const moe_shape &s, int n_groups, int zblocks, long est_rows,
+                         long cap_rows, const void *hm, const int32_t *offsets,
+                         int rows_per_group, const void *w_down, void *y, hipStream_t st) {
     StreamArgs a{};
     a.x = hm;
     a.offsets = offsets;
@@ -210,7 +248,8 @@ hipError_t ffn_down_impl(const moe_shape &s, int n_groups, int zblocks, const vo
     a.out_ld = s.hidden;
     a.N = s.hidden;
     a.K = s.inter;
-    return launch_stream_gemm(a, s.act, s.act, STREAM_STORE, n_groups, zblocks, st);
+    a.ksplit = 1;
+    return gemm(a, s.act, s.act, STREAM_STORE, n_groups, zblocks, est_rows, cap_rows, st);
 }
 
 hipError_t combine_impl(const moe_shape &s, int T, const void *y, const int32_t *inv_pos,
@@ -230,6 +269,12 @@ hipError_t combine_impl(const moe_shape &s, int T, const void *y, const int32_t 
     c.out = out;
     return launch_combine(c, st);
 }
+
+// Rows a group is expected to hold, used only to pick the kernel: cap_rows
+// is T*K for the routed groups, spread about evenly over the E experts, and
+// n_shared*T for the shared experts; cap/E keeps both choices alike for the
+// staged and the fused entry points (outputs do not depend on the choice).
+long est_group_rows(const moe_shape &s, long cap_rows) { return cap_rows / s.n_experts; }
 
 moe_status check_ffn_common(const moe_shape *shape, int32_t n_groups, int32_t cap_rows) {
     TRY(check_shape(shape));
@@ -279,7 +324,7 @@ MOE_EXPORT moe_status moe_route(const moe_shape *shape, int32_t T, const void *h
     TRY(need4_opt(shared_gate));
     TRY(need4_opt(logits));
     if (has_gate(*shape) && !shared_gate) return MOE_ERR_INVALID_ARG;
-    const size_t req = up256((size_t)T * (shape->n_experts + 1) * 4);
+    const size_t req = route_ws_bytes(*shape, T);
     if (!ws || ws_bytes < req) return MOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
     TRY(device_ok());
@@ -333,8 +378,10 @@ MOE_EXPORT moe_status moe_expert_ffn_up(const moe_shape *shape, int32_t n_groups
     TRY(need(hm));
     if (cap_rows == 0) return MOE_OK;
     TRY(device_ok());
-    LAUNCH(ffn_up_impl(*shape, n_groups, ffn_zblocks(cap_rows, n_groups), x, x_dtype, x_scale,
-                       x_broadcast ? 1 : 0, offsets, 0, w_gate, w_up, hm, (hipStream_t)stream));
+    LAUNCH(ffn_up_impl(*shape, n_groups, ffn_zblocks(cap_rows, n_groups),
+                       est_group_rows(*shape, cap_rows), cap_rows, x,
+                       x_dtype, x_scale, x_broadcast ? 1 : 0, offsets, 0, w_gate, w_up, hm,
+                       (hipStream_t)stream));
     return MOE_OK;
 }
 
@@ -349,8 +396,9 @@ MOE_EXPORT moe_status moe_expert_ffn_down(const moe_shape *shape, int32_t n_grou
     TRY(need(y));
     if (cap_rows == 0) return MOE_OK;
     TRY(device_ok());
-    LAUNCH(ffn_down_impl(*shape, n_groups, ffn_zblocks(cap_rows, n_groups), hm, offsets, 0,
-                         w_down, y, (hipStream_t)stream));
+    LAUNCH(ffn_down_impl(*shape, n_groups, ffn_zblocks(cap_rows, n_groups),
+                         est_group_rows(*shape, cap_rows),
+                         cap_rows, hm, offsets, 0, w_down, y, (hipStream_t)stream));
     return MOE_OK;
 }
 
@@ -433,18 +481,21 @@ MOE_EXPORT moe_status moe_layer_forward(const moe_shape *shape, const moe_weight
                          at<int32_t *>(ws, L.counts), offsets, at<int32_t *>(ws, L.perm_src),
                          inv_pos, at<void *>(ws, L.disp), st));
     const int z = ffn_zblocks(cap, s.n_slots);
-    LAUNCH(ffn_up_impl(s, s.n_slots, z, at<void *>(ws, L.x_perm), s.dispatch, x_scale, 0, offsets,
-                       0, w->w_gate, w->w_up, at<void *>(ws, L.hm), st));
-    LAUNCH(ffn_down_impl(s, s.n_slots, z, at<void *>(ws, L.hm), offsets, 0, w->w_down,
+    const long est = est_group_rows(s, cap);
+    LAUNCH(ffn_up_impl(s, s.n_slots, z, est, cap, at<void *>(ws, L.x_perm), s.dispatch, x_scale, 0,
+                       offsets, 0, w->w_gate, w->w_up, at<void *>(ws, L.hm), st));
+    LAUNCH(ffn_down_impl(s, s.n_slots, z, est, cap, at<void *>(ws, L.hm), offsets, 0, w->w_down,
                          at<void *>(ws, L.y), st));
     void *shared_y = nullptr;
     if (gate) {
         shared_y = at<void *>(ws, L.shared_y);
         const int zs = (T + 63) / 64 < 65535 ? (T + 63) / 64 : 65535;
-        LAUNCH(ffn_up_impl(s, s.n_shared, zs, h, s.act, nullptr, 1, nullptr, T, w->sh_gate,
-                           w->sh_up, at<void *>(ws, L.hm), st));
-        LAUNCH(ffn_down_impl(s, s.n_shared, zs, at<void *>(ws, L.hm), nullptr, T, w->sh_down,
-                             shared_y, st));
+        const long cap_sh = (long)s.n_shared * T;
+        const long est_sh = est_group_rows(s, cap_sh);
+        LAUNCH(ffn_up_impl(s, s.n_shared, zs, est_sh, cap_sh, h, s.act, nullptr, 1, nullptr, T,
+                           w->sh_gate, w->sh_up, at<void *>(ws, L.hm), st));
+        LAUNCH(ffn_down_impl(s, s.n_shared, zs, est_sh, cap_sh, at<void *>(ws, L.hm), nullptr, T,
+                             w->sh_down, shared_y, st));
     }
     LAUNCH(combine_impl(s, T, at<void *>(ws, L.y), inv_pos, topk_w, shared_y, sgate, out, st));
     return MOE_OK;

@@ -21,8 +21,10 @@ namespace moe {
 namespace {
 
 template <int EPL>
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int ld, int T,
-                                                   int E, int K, int has_gate,
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ parts, int nsplit,
+                                                   size_t split_stride, int ld, int T, int E,
+                                                   int K, int has_gate,
+                                                   const float *__restrict__ bias,
                                                    int32_t *__restrict__ topk_idx,
                                                    float *__restrict__ topk_w,
                                                    float *__restrict__ shared_gate,
@@ -30,13 +32,27 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const int lane = lane_id();
-    const float *l = logits + (size_t)t * ld;
+    const float *l = parts + (size_t)t * ld;
 
+    // logits = sum of the K-slice partials in slice order, then + bias
     float v[EPL];
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
         const int e = lane + 64 * j;
-        v[j] = e < E ? l[e] : -INFINITY;
+        float acc = -INFINITY;
+        if (e < E) {
+            // issue every slice's load before summing (at most 16 slices)
+            float part[16];
+#pragma unroll
+            for (int zs = 0; zs < 16; ++zs)
+                part[zs] = zs < nsplit ? l[(size_t)zs * split_stride + e] : 0.0f;
+            acc = part[0];
+#pragma unroll
+            for (int zs = 1; zs < 16; ++zs)
+                if (zs < nsplit) acc += part[zs];
+            if (bias) acc += bias[e];
+        }
+        v[j] = acc;
     }
     if (logits_out) {
 #pragma unroll
@@ -83,31 +99,35 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
             topk_w[(size_t)t * K + k] = expf(bv - m) / z;
         }
     }
-    if (has_gate && shared_gate && lane == 0) shared_gate[t] = sigmoidf_(l[E]);
+    if (has_gate && shared_gate && lane == 0) {
+        float zg = l[E];
+        for (int zs = 1; zs < nsplit; ++zs) zg += l[(size_t)zs * split_stride + E];
+        shared_gate[t] = sigmoidf_(zg);
+    }
 }
 
 }  // namespace
 
-hipError_t launch_topk(const float *logits, int ld, int T, int E, int K, int has_gate,
-                       int32_t *topk_idx, float *topk_w, float *shared_gate, float *logits_out,
-                       hipStream_t s) {
+hipError_t launch_topk(const float *logits, int nsplit, size_t split_stride, int ld, int T,
+                       int E, int K, int has_gate, const float *bias, int32_t *topk_idx,
+                       float *topk_w, float *shared_gate, float *logits_out, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     dim3 grid((T + 3) / 4), block(256);
     if (E <= 64)
-        hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, ld, T, E, K, has_gate,
-                           topk_idx, topk_w, shared_gate, logits_out);
+        hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, nsplit, split_stride, ld, T,
+                           E, K, has_gate, bias, topk_idx, topk_w, shared_gate, logits_out);
     else if (E <= 128)
-        hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, ld, T, E, K, has_gate,
-                           topk_idx, topk_w, shared_gate, logits_out);
+        hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, nsplit, split_stride, ld, T,
+                           E, K, has_gate, bias, topk_idx, topk_w, shared_gate, logits_out);
     else if (E <= 256)
-        hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, ld, T, E, K, has_gate,
-                           topk_idx, topk_w, shared_gate, logits_out);
+        hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, nsplit, split_stride, ld, T,
+                           E, K, has_gate, bias, topk_idx, topk_w, shared_gate, logits_out);
     else if (E <= 512)
-        hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, ld, T, E, K, has_gate,
-                           topk_idx, topk_w, shared_gate, logits_out);
+        hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, nsplit, split_stride, ld, T,
+                           E, K, has_gate, bias, topk_idx, topk_w, shared_gate, logits_out);
     else
-        hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, ld, T, E, K, has_gate,
-                           topk_idx, topk_w, shared_gate, logits_out);
+        hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, nsplit, split_stride, ld, T,
+                           E, K, has_gate, bias, topk_idx, topk_w, shared_gate, logits_out);
     return hipGetLastError();
 }
 

@@ -112,8 +112,8 @@ typedef struct {
  * h [T][H] (act); topk_idx int32 [T][K]; topk_w fp32 [T][K];
  * shared_gate fp32 [T] or NULL; logits fp32 [T][E] or NULL (if non-NULL the
  * raw logits including bias are stored).
- * Workspace: ws of at least T*(E+1)*4 bytes rounded up to 256 (any
- * moe_workspace_bytes(shape, T) sized buffer works). */
+ * Workspace: ws of moe_workspace_bytes(shape, T) bytes (holds the fp32
+ * partial logits of the K-split router GEMM). */
 moe_status moe_route(const moe_shape *shape, int32_t T, const void *h,
                      const void *w_router, const float *bias, int32_t *topk_idx,
                      float *topk_w, float *shared_gate, float *logits, void *ws,

@@ -20,6 +20,7 @@ from .gen import (  # noqa: F401
     gen_expert,
     gen_shared_expert,
     gen_slot_weights,
+    iter_experts,
     gen_shared_weights,
     replica_expert,
     LONG_TAIL_BETA,

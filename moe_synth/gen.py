@@ -20,8 +20,11 @@ Distributions
 """
 from __future__ import annotations
 
+import collections
 import dataclasses
-from typing import Optional
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Iterable, Optional
 
 import numpy as np
 
@@ -208,3 +211,24 @@ def gen_shared_weights(cfg: MoEConfig):
         return None, None, None
     parts = [gen_shared_expert(cfg, j) for j in range(cfg.n_shared)]
     return tuple(np.ascontiguousarray(np.stack(p)) for p in zip(*parts))
+
+
+def iter_experts(cfg: MoEConfig, experts: Iterable[int], workers: Optional[int] = None):
+    """Yield (e, (gate, up, down)) for ``experts`` in order, drawn on a
+    thread pool (numpy releases the GIL while drawing) with a bounded
+    look-ahead so at most ~2*workers experts are held at once."""
+    workers = workers or min(16, os.cpu_count() or 1)
+    it = iter(int(e) for e in experts)
+    with ThreadPoolExecutor(workers) as ex:
+        pending = collections.deque()
+        for _ in range(2 * workers):
+            e = next(it, None)
+            if e is None:
+                break
+            pending.append((e, ex.submit(gen_expert, cfg, e)))
+        while pending:
+            e, fut = pending.popleft()
+            yield e, fut.result()
+            nxt = next(it, None)
+            if nxt is not None:
+                pending.append((nxt, ex.submit(gen_expert, cfg, nxt)))

@@ -102,13 +102,12 @@ def build_layer(cfg, *, rank: Optional[int] = None, T: Optional[int] = None,
     U = torch.empty((S, cfg.I, cfg.H), dtype=tdt, device=DEV)
     D = torch.empty((S, cfg.H, cfg.I), dtype=tdt, device=DEV)
     experts = {}
-    for s, e in enumerate(slot_experts):
-        g, u, dd = moe_synth.gen_expert(cfg, int(e))
+    for s, (e, (g, u, dd)) in enumerate(moe_synth.iter_experts(cfg, slot_experts)):
         G[s].copy_(torch.from_numpy(g))
         U[s].copy_(torch.from_numpy(u))
         D[s].copy_(torch.from_numpy(dd))
         if keep_host_weights:
-            experts[int(e)] = (g, u, dd)
+            experts[e] = (g, u, dd)
     shared = None
     d = dict(h=to_dev(h), wr=to_dev(wr), bias=to_dev(bias), G=G, U=U, D=D)
     if cfg.n_shared:
@@ -203,6 +202,9 @@ def oracle_forward(L: Layer, tokens: Optional[np.ndarray] = None):
     idx, _ = oracle.softmax_topk(lg, cfg.K)
     slot = oracle.slot_map(idx, ro, rs, L.seed, tok_ids=tok_ids)
     need = set(int(s) for s in np.unique(slot) if s >= 0)
+    missing = [int(se[s]) for s in sorted(need) if int(se[s]) not in L.experts]
+    for e, w in moe_synth.iter_experts(cfg, missing):
+        L.experts[e] = w
     sw = [L.expert(se[s]) if s in need else None for s in range(len(se))]
     res = oracle.layer_forward(h=h, w_router=L.wr[: cfg.E], bias=L.bias,
                                w_sg=L.wr[cfg.E] if cfg.n_shared else None, slot_weights=sw,

@@ -301,11 +301,11 @@ def test_dense_topk_equals_experts():
 # ------------------------------------------------------------ full sizes
 
 
-FULL_SAMPLE = {2: 32, 4: 24, 5: 32}
+FULL_SAMPLE = {2: 32, 3: 12, 4: 24, 5: 32}
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("n", [2, 5, 4])
+@pytest.mark.parametrize("n", [2, 5, 4, 3])
 def test_full_size_sampled(n):
     """Full workload sizes in the launch configuration the benchmark times;
     routing of a token sample and the whole dispatch are compared exactly,
@@ -324,3 +324,35 @@ def test_full_size_sampled(n):
     _ = oracle_sample
     err = gh.assert_close(out[tok], ref["out"], "layer output (sample)", rows=~tie)
     print(f"[full] workload {n} P={st['P']} sample={len(tok)} max|d|={err:.3e}")
+
+
+def test_prefill_tiled_path_small():
+    """T = 4096 rank share: the router (T >= 2048, no K split) and the routed
+    FFN (>= 64 expected rows per group) take the LDS-tiled kernel."""
+    cfg = moe_synth.scaled_config(4, T=4096, H=256, I=128, seed=31)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    tie = _check_routing(L, st)
+    _check_dispatch(L, st)
+    _check_ffn(L, st)
+    _check_combine(L, st)
+    out = gh.gpu_forward(L).cpu().numpy()
+    assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8))
+    ref = gh.oracle_forward(L)
+    err = gh.assert_close(out, ref["out"], "layer output", rows=~tie)
+    print(f"[tiled] P={st['P']} max|d|={err:.3e} near_ties={int(tie.sum())}")
+
+
+def test_tiled_shared_and_ragged_groups():
+    """fp16 16-expert layer with a shared expert at T = 1000: routed groups
+    (~125 rows) and the shared group (1000 rows, not a multiple of 128) on
+    the tiled kernel, full layer, against the oracle."""
+    cfg = moe_synth.scaled_config(1, T=1000, H=256, I=128, dtype="f16", seed=32)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    tie = _check_routing(L, st)
+    _check_dispatch(L, st)
+    _check_ffn(L, st)
+    _check_combine(L, st)
+    ref = gh.oracle_forward(L)
+    gh.assert_close(st["out"], ref["out"], "layer output", rows=~tie)
