@@ -264,7 +264,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int
             v = float(r["Counter_Value"])
             if is_swiglu_stream(name):
                 dom.append(v)
-            elif "elementwise" in name.lower():
+            elif "AUnaryFunctor" in name and "MulFunctor" in name:  # the calibration copy
                 cp.append(v)
         return dom, cp
 
@@ -282,6 +282,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int
                kernel_source_hash=kernel_source_hash(), counters=out,
                traffic_bytes_per_launch=out["FETCH_SIZE"]["bytes_per_launch"]
                + out["WRITE_SIZE"]["bytes_per_launch"])
+    rec["command"] = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv "
+                      "-d DIR -o run -- python3 bench.py --workload N --steps 3 --warmup 1 "
+                      "--no-cpu-baseline --copy-calibration; python3 bench.py --summarize-pmc "
+                      "FETCH_DIR WRITE_DIR --workload N")
     p = os.path.join(ROOT, "profiles", f"traffic_stream_gemm_swiglu_{workload}.json")
     with open(p, "w") as f:
         json.dump(rec, f, indent=2)

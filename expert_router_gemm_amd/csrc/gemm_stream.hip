@@ -31,6 +31,30 @@
 #include "common.h"
 #include "kernels.h"
 
+// Compile-time tuning knobs (defaults are the measured best on MI355X):
+//   MOE_STREAM_U          K chunks per register buffer (double-buffered)
+//   MOE_STREAM_MAX_WAVES  cap on waves per SIMD (0 = compiler's choice)
+//   MOE_STREAM_COND_PREFETCH  1: skip the prefetch past the end (the
+//       compiler then waits for every load before the second compute)
+//   MOE_STREAM_NT         1: weights loaded with the non-temporal hint
+#ifndef MOE_STREAM_U
+#define MOE_STREAM_U 8
+#endif
+#ifndef MOE_STREAM_MAX_WAVES
+#define MOE_STREAM_MAX_WAVES 0
+#endif
+#ifndef MOE_STREAM_COND_PREFETCH
+#define MOE_STREAM_COND_PREFETCH 1
+#endif
+#ifndef MOE_STREAM_NT
+#define MOE_STREAM_NT 0
+#endif
+#if MOE_STREAM_MAX_WAVES > 0
+#define MOE_STREAM_OCC __attribute__((amdgpu_waves_per_eu(1, MOE_STREAM_MAX_WAVES)))
+#else
+#define MOE_STREAM_OCC
+#endif
+
 namespace moe {
 
 namespace {
@@ -54,6 +78,16 @@ struct XFrag<f16, DT_FP8> {  // 8 fp8 codes, decoded to fp16 * 2^-8
     }
     __device__ static __forceinline__ f16x8 cvt(const raw &v) { return e4m3x8_to_f16x8_scaled(v); }
 };
+
+// Weight loads: every weight byte is read exactly once per launch.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::vec wload16(const T *p) {
+#if MOE_STREAM_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const typename Frag<T>::vec *>(p));
+#else
+    return load16(p);
+#endif
+}
 
 template <typename TW, int XM, int NM, int EPI, int MT, int U>
 __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, int rstart,
@@ -103,7 +137,7 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
 #define MOE_LOAD(WBUF, XBUF, c)                                                  \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                              \
         _Pragma("unroll") for (int m = 0; m < NM; ++m) WBUF[u][m] =              \
-            load16(wp[m] + (size_t)((c) + u) * CK);                              \
+            wload16(wp[m] + (size_t)((c) + u) * CK);                             \
         _Pragma("unroll") for (int t = 0; t < MT; ++t) XBUF[u][t] =              \
             XF::load(a.x, xo[t] + (size_t)((c) + u) * CK);                       \
     }
@@ -116,13 +150,19 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
         }                                                                        \
     }
 
+    // Branch-free double buffering (NC is a multiple of 2U): a conditional
+    // prefetch would make the compiler wait for every outstanding load before
+    // the second compute; the last prefetch instead re-reads the chunk group
+    // just loaded (cache hits, never used).
     MOE_LOAD(wa, xa, 0);
     for (int c = 0; c < NC; c += 2 * U) {
         MOE_LOAD(wb, xb, c + U);
         MOE_COMPUTE(wa, xa);
-        if (c + 2 * U < NC) {
-            MOE_LOAD(wa, xa, c + 2 * U);
-        }
+#if MOE_STREAM_COND_PREFETCH
+        if (c + 2 * U < NC) MOE_LOAD(wa, xa, c + 2 * U);
+#else
+        MOE_LOAD(wa, xa, (c + 2 * U < NC) ? c + 2 * U : c + U);
+#endif
         MOE_COMPUTE(wb, xb);
     }
 #undef MOE_LOAD
@@ -167,7 +207,7 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
 }
 
 template <typename TW, int XM, int NM, int EPI, int U>
-__global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
+__global__ __launch_bounds__(256) MOE_STREAM_OCC void stream_gemm_kernel(StreamArgs a) {
     const int wave = threadIdx.x >> 6;
     const int f0 = blockIdx.x * 64 + wave * 16;
     if (f0 >= a.N) return;
@@ -201,8 +241,8 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t 
     constexpr int CK = 4 * Frag<TW>::kElems;
     const int NC = a.K / a.ksplit / CK;
     if (a.ksplit < 1 || a.K % (a.ksplit * 4 * CK) != 0) return hipErrorInvalidValue;
-    if (NC % 8 == 0)
-        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NM, EPI, 4>), grid, dim3(256), 0, s, a);
+    if (NC % (2 * MOE_STREAM_U) == 0)
+        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NM, EPI, MOE_STREAM_U>), grid, dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NM, EPI, 2>), grid, dim3(256), 0, s, a);
     return hipGetLastError();

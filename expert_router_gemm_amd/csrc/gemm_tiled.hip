@@ -8,27 +8,47 @@
 //
 //   out[r][n] = epilogue( sum_k W[g][n][k] * x[r][k] )   rows r of group g
 //
-// Tile: BM = 128 rows x BN = 128 features (x2 weight matrices for SwiGLU),
-// BK = 64.  256 threads = 4 waves in a 2 x 2 arrangement; each wave owns a
-// 64 x 64 block (x2 matrices) as 4 x 4 tiles of v_mfma_f32_16x16x32_f16.
-// Global -> register -> LDS staging, two LDS buffers, one barrier per K step;
-// LDS rows are padded by 16 bytes so the 16-byte fragment reads of 16
-// different rows fall in different banks.
+// Tile: 128 rows x 256 weight rows (128 features x gate and up for SwiGLU,
+// 256 features otherwise), BK = 64.  512 threads = 8 waves (2 per SIMD) in a
+// 2 x 4 arrangement; each wave owns 64 rows x 64 weight rows as 16 tiles of
+// v_mfma_f32_16x16x32_f16.
+// Global -> register -> LDS staging with a two-step register prefetch (the
+// loads for step k+2 are in flight while step k computes), two LDS buffers,
+// one barrier per K step, XOR-swizzled LDS rows (see swz()).
 //
-// The grid is persistent (one workgroup per CU): see tiled_gemm_kernel.
+// The grid is persistent (all resident workgroup slots): see tiled_gemm_kernel.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int PITCH = BK + 8;  // halves per LDS row (16 B pad)
-constexpr int kThreads = 256;
+constexpr int BM = 128;    // x rows per tile
+constexpr int WR = 256;    // weight rows per tile: 128 gate + 128 up, or 256 down/logits
+constexpr int BK = 64;     // reduction per pipeline step
+constexpr int PITCH = BK;  // halves per LDS row (128 B, XOR-swizzled chunks)
+constexpr int kThreads = 512;
 
+// LDS offset (halves) of 16-byte chunk c of row r: the chunk index is XORed
+// with r % 8, so the 16 rows one MFMA fragment read touches spread over all
+// banks (a 16-byte row pad still leaves 2-way conflicts on gfx950, as
+// measured with SQ_LDS_BANK_CONFLICT).
+__device__ __forceinline__ int swz(int r, int c) { return r * PITCH + ((c ^ (r & 7)) << 3); }
+
+// One output tile: rows [rs, rs+128) of group g x features [n0, n0 + WR/NM).
+// 8 waves = 2 (rows) x 4 (weight rows); wave (wm, wn) owns x rows
+// wm*64..+64 and, per matrix m, weight rows m*FN + wn*FN/4 .. +FN/4
+// (FN = WR/NM features), as 4 x (4/NM) x NM tiles of 16x16x32 MFMAs.
 template <int NM, int EPI>
 __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs, int g, int mt,
                                           int nt) {
+    constexpr int FN = WR / NM;   // features per tile
+    constexpr int NJ = 4 / NM;    // 16-feature subtiles per wave and matrix
+    // wave-uniform by construction; readfirstlane keeps them (and the buffer
+    // descriptors built from them) in scalar registers
+    g = __builtin_amdgcn_readfirstlane(g);
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    nt = __builtin_amdgcn_readfirstlane(nt);
     int r0, r1;
     if (a.offsets) {
         r0 = a.offsets[g];
@@ -37,100 +57,118 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
         r0 = g * a.rows_per_group;
         r1 = r0 + a.rows_per_group;
     }
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    r1 = __builtin_amdgcn_readfirstlane(r1);
     const int rs = r0 + mt * BM;
-    const int n0 = nt * BN;
+    const int n0 = nt * FN;
     const int K = a.K;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
     const int lr = lane & 15, lg = lane >> 4;
 
-    // ---- global load assignment: 16-byte chunks, 8 per 128-byte row slice
-    // A: BM rows x 8 chunks = 1024 chunks -> 4 per thread
-    // B: NM*BN rows x 8 chunks -> 4*NM per thread
-    const f16 *xg[4];
-    int a_lds[4];
+    // ---- global loads: buffer loads against per-tile resource descriptors.
+    // Rows past the tile's valid rows fall outside the descriptor's range and
+    // load zeros, so no clamping is needed; 32-bit lane offsets keep the
+    // address cost at one VGPR per load.  Thread t moves 16-byte chunk t%8 of
+    // rows t/8 + 64*i (i < 2 for x, i < 4 for the weight rows).
+    const int rows_valid = (r1 - rs) < BM ? (r1 - rs) : BM;
+    const int xrow0 = a.x_broadcast ? rs - r0 : rs;
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(reinterpret_cast<const f16 *>(a.x) + (size_t)xrow0 * K), (short)0,
+        rows_valid * K * 2, 0x00020000);
+    const int ncols = (a.N - n0) < FN ? (a.N - n0) : FN;
+    __amdgpu_buffer_rsrc_t wres[NM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + kThreads * i;
-        const int row = c >> 3, col = (c & 7) * 8;
-        int r = rs + row;
-        if (r > r1 - 1) r = r1 - 1;
-        const int xr = a.x_broadcast ? r - r0 : r;
-        xg[i] = reinterpret_cast<const f16 *>(a.x) + (size_t)xr * K + col;
-        a_lds[i] = row * PITCH + col;
+    for (int m = 0; m < NM; ++m)
+        wres[m] = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(reinterpret_cast<const f16 *>(m == 0 ? a.w0 : a.w1) +
+                     (size_t)g * a.w_group_stride + (size_t)n0 * K),
+            (short)0, ncols * K * 2, 0x00020000);
+    const int trow = tid >> 3, tch = tid & 7;
+    const int goff = trow * K * 2 + tch * 16;  // byte offset of row trow, chunk tch
+    const int rstep = 64 * K * 2;              // 64 rows further
+    const int lds0 = swz(trow, tch);           // (trow + 64 i) % 8 == trow % 8
+
+    // two register staging sets: set 0 holds even K steps, set 1 odd ones
+    f16x8 ra0[2], rb0[4], ra1[2], rb1[4];
+#define MOE_GLOAD(RA, RB, k0)                                                          \
+    {                                                                                  \
+        const int kb_ = (k0) * 2;                                                      \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i) RA[i] = __builtin_bit_cast(       \
+            f16x8, __builtin_amdgcn_raw_buffer_load_b128(xres, goff + i * rstep + kb_, 0, 0)); \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) RB[i] = __builtin_bit_cast(       \
+            f16x8, __builtin_amdgcn_raw_buffer_load_b128(                              \
+                       wres[(i * 64) / FN], goff + ((i * 64) % FN / 64) * rstep + kb_, 0, 0)); \
     }
-    const f16 *wg[4 * NM];
-    int b_lds[4 * NM];
-#pragma unroll
-    for (int i = 0; i < 4 * NM; ++i) {
-        const int c = tid + kThreads * i;
-        const int row = c >> 3, col = (c & 7) * 8;  // row in [0, NM*BN)
-        const int m = row / BN, rr = row % BN;
-        int n = n0 + rr;
-        if (n > a.N - 1) n = a.N - 1;
-        const f16 *base = reinterpret_cast<const f16 *>(m == 0 ? a.w0 : a.w1);
-        wg[i] = base + (size_t)g * a.w_group_stride + (size_t)n * K + col;
-        b_lds[i] = row * PITCH + col;
+#define MOE_LSTORE(RA, RB, buf)                                                        \
+    {                                                                                  \
+        f16 *A_ = As + (buf) * BM * PITCH + lds0;                                      \
+        f16 *B_ = Bs + (buf) * WR * PITCH + lds0;                                      \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                  \
+            *reinterpret_cast<f16x8 *>(A_ + i * 64 * PITCH) = RA[i];                   \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                  \
+            *reinterpret_cast<f16x8 *>(B_ + i * 64 * PITCH) = RB[i];                   \
     }
 
-    f16x8 ra[4], rb[4 * NM];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = load16(xg[i] + k0);
-#pragma unroll
-        for (int i = 0; i < 4 * NM; ++i) rb[i] = load16(wg[i] + k0);
-    };
-    auto lstore = [&](int buf) {
-        f16 *A = As + buf * BM * PITCH;
-        f16 *B = Bs + buf * NM * BN * PITCH;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<f16x8 *>(A + a_lds[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < 4 * NM; ++i) *reinterpret_cast<f16x8 *>(B + b_lds[i]) = rb[i];
-    };
-
-    f32x4 acc[NM][4][4];
+    f32x4 acc[NM][4][NJ];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NJ; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
+    auto compute = [&](int buf) {
         const f16 *A = As + buf * BM * PITCH;
-        const f16 *B = Bs + buf * NM * BN * PITCH;
+        const f16 *B = Bs + buf * WR * PITCH;
 #pragma unroll
-        for (int ks = 0; ks < BK; ks += 32) {
-            f16x8 af[4], bf[NM][4];
+        for (int ks = 0; ks < BK / 8; ks += 4) {  // two 32-wide MFMA steps (in chunks)
+            const int ch = ks + lg;                // this lane's logical 16-byte chunk
+            f16x8 af[4], bf[NM][NJ];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const f16x8 *>(A + (wm * 64 + i * 16 + lr) * PITCH + ks + lg * 8);
+                af[i] = *reinterpret_cast<const f16x8 *>(A + swz(wm * 64 + i * 16 + lr, ch));
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
                     bf[m][j] = *reinterpret_cast<const f16x8 *>(
-                        B + (m * BN + wn * 64 + j * 16 + lr) * PITCH + ks + lg * 8);
+                        B + swz(m * FN + wn * (FN / 4) + j * 16 + lr, ch));
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[m][i][j] = mfma16(af[i], bf[m][j], acc[m][i][j]);
+                    for (int j = 0; j < NJ; ++j) acc[m][i][j] = mfma16(af[i], bf[m][j], acc[m][i][j]);
         }
-        if (kt + 1 < nk) lstore(buf ^ 1);
+    };
+
+    // K / BK is even (K is a multiple of 128).  The loop body is branch-free
+    // so the compiler's wait counts stay exact (a prefetch past the end
+    // re-reads the last step and is never used).
+    const int nk = K / BK;
+    MOE_GLOAD(ra0, rb0, 0);
+    MOE_GLOAD(ra1, rb1, BK);
+    MOE_LSTORE(ra0, rb0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        // step kt: LDS buffer 0; refill set 0 with step kt+2; stage set 1 (kt+1)
+        MOE_GLOAD(ra0, rb0, (kt + 2 < nk ? kt + 2 : nk - 1) * BK);
+        compute(0);
+        MOE_LSTORE(ra1, rb1, 1);
+        __syncthreads();
+        // step kt+1: LDS buffer 1; refill set 1 with step kt+3; stage set 0 (kt+2)
+        MOE_GLOAD(ra1, rb1, (kt + 3 < nk ? kt + 3 : nk - 1) * BK);
+        compute(1);
+        MOE_LSTORE(ra0, rb0, 0);
         __syncthreads();
     }
+#undef MOE_GLOAD
+#undef MOE_LSTORE
 
-    // ---- epilogue.  acc[m][i][j]: rows wm*64 + i*16 + 4*lg + q (q = 0..3),
-    // feature n0 + wn*64 + j*16 + lr (A = x rows, B = weight rows).
+    // ---- epilogue.  acc[m][i][j]: x row wm*64 + i*16 + 4*lg + q (q = 0..3),
+    // feature n0 + wn*FN/4 + j*16 + lr (A = x rows, B = weight rows).
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -138,8 +176,8 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
             const int r = rs + wm * 64 + i * 16 + 4 * lg + q;
             if (r >= r1) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int f = n0 + wn * 64 + j * 16 + lr;
+            for (int j = 0; j < NJ; ++j) {
+                const int f = n0 + wn * (FN / 4) + j * 16 + lr;
                 if (f >= a.N) continue;
                 if (EPI == 2) {  // logits, fp32
                     reinterpret_cast<float *>(a.out)[(size_t)r * a.out_ld + f] = acc[0][i][j][q];
@@ -170,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
                                                               int n_groups) {
     extern __shared__ __attribute__((aligned(16))) f16 lds[];
     f16 *As = lds;                          // [2][BM][PITCH]
-    f16 *Bs = lds + 2 * BM * PITCH;         // [2][NM*BN][PITCH]
+    f16 *Bs = lds + 2 * BM * PITCH;         // [2][WR][PITCH]
     __shared__ int tstart[kMaxGroups + 1];  // first row tile of each group
     __shared__ int scan[2][kThreads];
 
@@ -221,8 +259,8 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
 template <int NM, int EPI>
 hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream_t s) {
     if (n_groups <= 0 || n_groups > kMaxGroups) return hipErrorInvalidValue;
-    const int n_ntiles = (a.N + BN - 1) / BN;
-    const size_t lds = (size_t)2 * (BM + NM * BN) * PITCH * sizeof(f16);
+    const int n_ntiles = (a.N + WR / NM - 1) / (WR / NM);
+    const size_t lds = (size_t)2 * (BM + WR) * PITCH * sizeof(f16);
     static bool attr_set = false;  // idempotent; a race only repeats the call
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<NM, EPI>,
@@ -230,11 +268,14 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    int dev = 0, cus = 256;
+    int dev = 0, cus = 256, per_cu = 1;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    // one resident workgroup per CU (LDS-bound); never more than the items
-    long grid = cus;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tiled_gemm_kernel<NM, EPI>, kThreads,
+                                                     lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    // every resident workgroup slot, never more than the items
+    long grid = (long)cus * per_cu;
     const long items = max_tiles * n_ntiles;
     if (items < grid) grid = items > 0 ? items : 1;
     hipLaunchKernelGGL((tiled_gemm_kernel<NM, EPI>), dim3((unsigned)grid), dim3(kThreads), lds, s,
@@ -245,7 +286,7 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
 }  // namespace
 
 bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype) {
-    return dtype == DT_F16 && x_dtype == DT_F16 && a.ksplit == 1 && a.K % BK == 0;
+    return dtype == DT_F16 && x_dtype == DT_F16 && a.ksplit == 1 && a.K % (2 * BK) == 0;
 }
 
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,
