@@ -135,19 +135,25 @@ def staged_step(ctx, ev=None):
     moe.moe_route(shape, T, d["h"], d["wr"], d["bias"], b["idx"], b["tw"],
                   b["sg"] if cfg.n_shared else None, None, b["ws"])
     rec(1)
-    moe.moe_dispatch(shape, T, d["h"], b["idx"], ctx["smap"], b["xp"], b["xs"] if fp8 else None,
-                     b["counts"], b["offsets"], b["perm"], b["inv"], b["ws"])
+    # fp8 rows are quantised copies; fp16 rows are gathered by the GEMM
+    moe.moe_dispatch(shape, T, d["h"], b["idx"], ctx["smap"], b["xp"] if fp8 else None,
+                     b["xs"] if fp8 else None, b["counts"], b["offsets"], b["perm"], b["inv"],
+                     b["ws"])
     rec(2)
-    xdt = moe.MOE_FP8_E4M3 if fp8 else shape.act
-    moe.moe_expert_ffn_up(shape, S, T * cfg.K, b["xp"], xdt, b["xs"] if fp8 else None, 0,
-                          b["offsets"], d["G"], d["U"], b["hm"])
+    if fp8:
+        moe.moe_expert_ffn_up(shape, S, T * cfg.K, b["xp"], moe.MOE_FP8_E4M3, b["xs"],
+                              moe.MOE_X_PERMUTED, None, b["offsets"], d["G"], d["U"], b["hm"])
+    else:
+        moe.moe_expert_ffn_up(shape, S, T * cfg.K, d["h"], shape.act, None, moe.MOE_X_GATHER,
+                              b["perm"], b["offsets"], d["G"], d["U"], b["hm"])
     rec(3)
     moe.moe_expert_ffn_down(shape, S, T * cfg.K, b["hm"], b["offsets"], d["D"], b["y"])
     rec(4)
     shy = None
     if cfg.n_shared:
-        moe.moe_expert_ffn(shape, cfg.n_shared, cfg.n_shared * T, d["h"], shape.act, None, 1,
-                           b["shoff"], d["SG"], d["SU"], d["SD"], b["shy"], b["ws"])
+        moe.moe_expert_ffn(shape, cfg.n_shared, cfg.n_shared * T, d["h"], shape.act, None,
+                           moe.MOE_X_SHARED, None, b["shoff"], d["SG"], d["SU"], d["SD"], b["shy"],
+                           b["ws"])
         shy = b["shy"]
     moe.moe_combine(shape, T, b["y"], b["inv"], b["tw"], shy, b["sg"] if cfg.n_shared else None,
                     b["out"])
@@ -181,9 +187,10 @@ def algorithmic_work(ctx):
                  flops=2 * T * H * (E + (cfg.n_shared > 0)))
     shared = dict(bytes=cfg.n_shared * expert_bytes + cfg.n_shared * T * (H * isz * 2 + I * isz),
                   flops=cfg.n_shared * 6 * T * H * I)
+    copy = 2 * P * H * xsz if cfg.dispatch == "fp8" else 0  # fp8 rows: quantised copy
     layer_bytes = (touched * expert_bytes + shared["bytes"] + route["bytes"]
                    + T * H * isz  # output
-                   + 2 * P * H * xsz + 2 * P * H * isz)  # dispatch copy + y round trip
+                   + copy + 2 * P * H * isz)  # dispatch copy, y round trip
     return dict(P=P, touched=touched, up=up, down=down, route=route, shared=shared,
                 layer_bytes=layer_bytes,
                 layer_flops=up["flops"] + down["flops"] + route["flops"] + shared["flops"])

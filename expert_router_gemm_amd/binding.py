@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_F16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_F_SHARED = 1
+MOE_X_PERMUTED, MOE_X_SHARED, MOE_X_GATHER = 0, 1, 2
 
 EXPORTED = (
     "moe_route", "moe_dispatch", "moe_expert_ffn_up", "moe_expert_ffn_down",
@@ -67,9 +68,9 @@ def lib() -> ctypes.CDLL:
         SP = ctypes.POINTER(Shape)
         L.moe_route.argtypes = [SP, I32, P, P, P, P, P, P, P, P, SZ, P]
         L.moe_dispatch.argtypes = [SP, I32, P, P, ctypes.POINTER(SlotMap), P, P, P, P, P, P, P, SZ, P]
-        L.moe_expert_ffn_up.argtypes = [SP, I32, I32, P, I32, P, I32, P, P, P, P, P]
+        L.moe_expert_ffn_up.argtypes = [SP, I32, I32, P, I32, P, I32, P, P, P, P, P, P]
         L.moe_expert_ffn_down.argtypes = [SP, I32, I32, P, P, P, P, P]
-        L.moe_expert_ffn.argtypes = [SP, I32, I32, P, I32, P, I32, P, P, P, P, P, P, SZ, P]
+        L.moe_expert_ffn.argtypes = [SP, I32, I32, P, I32, P, I32, P, P, P, P, P, P, P, SZ, P]
         L.moe_combine.argtypes = [SP, I32, P, P, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [SP, ctypes.POINTER(Weights), ctypes.POINTER(SlotMap),
                                         I32, P, P, P, SZ, P]
@@ -149,11 +150,11 @@ def moe_dispatch(shape, T, h, topk_idx, slot_map: SlotMap, x_perm, x_scale, coun
         _stream(stream)))
 
 
-def moe_expert_ffn_up(shape, n_groups, cap_rows, x, x_dtype, x_scale, x_broadcast, offsets,
+def moe_expert_ffn_up(shape, n_groups, cap_rows, x, x_dtype, x_scale, x_rows, gather, offsets,
                       w_gate, w_up, hm, stream=None):
     _check("moe_expert_ffn_up", lib().moe_expert_ffn_up(
-        ctypes.byref(shape), n_groups, cap_rows, _p(x), x_dtype, _p(x_scale), int(x_broadcast),
-        _p(offsets), _p(w_gate), _p(w_up), _p(hm), _stream(stream)))
+        ctypes.byref(shape), n_groups, cap_rows, _p(x), x_dtype, _p(x_scale), int(x_rows),
+        _p(gather), _p(offsets), _p(w_gate), _p(w_up), _p(hm), _stream(stream)))
 
 
 def moe_expert_ffn_down(shape, n_groups, cap_rows, hm, offsets, w_down, y, stream=None):
@@ -162,11 +163,11 @@ def moe_expert_ffn_down(shape, n_groups, cap_rows, hm, offsets, w_down, y, strea
         _stream(stream)))
 
 
-def moe_expert_ffn(shape, n_groups, cap_rows, x, x_dtype, x_scale, x_broadcast, offsets,
+def moe_expert_ffn(shape, n_groups, cap_rows, x, x_dtype, x_scale, x_rows, gather, offsets,
                    w_gate, w_up, w_down, y, ws, stream=None):
     _check("moe_expert_ffn", lib().moe_expert_ffn(
-        ctypes.byref(shape), n_groups, cap_rows, _p(x), x_dtype, _p(x_scale), int(x_broadcast),
-        _p(offsets), _p(w_gate), _p(w_up), _p(w_down), _p(y), _p(ws), _nbytes(ws),
+        ctypes.byref(shape), n_groups, cap_rows, _p(x), x_dtype, _p(x_scale), int(x_rows),
+        _p(gather), _p(offsets), _p(w_gate), _p(w_up), _p(w_down), _p(y), _p(ws), _nbytes(ws),
         _stream(stream)))
 
 

@@ -252,6 +252,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(DispatchArgs a) {
             a.perm_src[row] = (int32_t)p;
         }
     }
+    if (!a.x_perm) return;  // indices only: the GEMM gathers the rows itself
     constexpr int EL = Frag<T>::kElems;
     const T *src = reinterpret_cast<const T *>(a.h) + (size_t)t * a.H;
     if (XM != DT_FP8) {
@@ -320,6 +321,7 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
         hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (!a.x_perm) return hipSuccess;  // rows are gathered by the GEMM instead
         return launch_scatter<true>(a, s);
     }
     if (C > 0) {

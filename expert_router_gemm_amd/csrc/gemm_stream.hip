@@ -10,13 +10,13 @@
 //   out[r][n] = epilogue( sum_k W[g][n][k] * x[r][k] )   for rows r of group g
 //
 // Work decomposition
-//   blockIdx.x  64 output features (4 waves x 16 features each)
+//   blockIdx.x  4 waves x (16 features, or 16*NM for the plain GEMM)
 //   blockIdx.y  group g (expert slot)
 //   blockIdx.z  (first row block) * ksplit + K slice; row blocks of 64 rows
 //               are strided by gridDim.z / ksplit.  ksplit > 1 (router only)
 //               writes one fp32 partial per K slice; the top-K kernel sums
 //               them in slice order, so the result stays deterministic.
-// Each wave owns 16 features and runs the whole K loop for them, so no
+// Each wave owns its features and runs the whole K loop for them, so no
 // cross-wave reduction is needed.  The 64 rows of a row block are processed
 // in MT = 1, 2 or 4 tiles of 16, chosen from the rows actually present, so
 // one pass over the weights serves every row of a decode-sized group.
@@ -48,6 +48,13 @@
 #endif
 #ifndef MOE_STREAM_NT
 #define MOE_STREAM_NT 0
+#endif
+//   MOE_STREAM_STORE_WIDE_ROWS  expected rows per group from which the plain
+//       (down projection) GEMM gives each wave two 16-feature subtiles that
+//       share every activation fragment (one subtile below: measured faster
+//       at ~8 rows per group, two at ~16-50)
+#ifndef MOE_STREAM_STORE_WIDE_ROWS
+#define MOE_STREAM_STORE_WIDE_ROWS 12
 #endif
 #if MOE_STREAM_MAX_WAVES > 0
 #define MOE_STREAM_OCC __attribute__((amdgpu_waves_per_eu(1, MOE_STREAM_MAX_WAVES)))
@@ -103,15 +110,18 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
     const int KS = K / a.ksplit;  // this block's K slice: [kz*KS, (kz+1)*KS)
     const int NC = KS / CK;
 
-    // weight rows (clamped: rows past N are read but never stored)
+    // weight rows (clamped: rows past N are read but never stored).  SwiGLU:
+    // subtile m is matrix m (gate, up) at rows f0..f0+15; otherwise subtile m
+    // is rows f0 + 16m .. +15 of the one matrix.
+    constexpr bool SAME = EPI != EPI_SWIGLU;
     const TW *wp[NM];
-    {
-        int wrow = f0 + lr;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        int wrow = f0 + (SAME ? 16 * m : 0) + lr;
         if (wrow > a.N - 1) wrow = a.N - 1;
         const size_t off = (size_t)g * a.w_group_stride + (size_t)wrow * K + (size_t)kz * KS +
                            (size_t)lg * EL;
-        wp[0] = reinterpret_cast<const TW *>(a.w0) + off;
-        if (NM > 1) wp[NM - 1] = reinterpret_cast<const TW *>(a.w1) + off;
+        wp[m] = reinterpret_cast<const TW *>(SAME || m == 0 ? a.w0 : a.w1) + off;
     }
     // token rows (clamped to the group's last row; extra columns are dropped)
     size_t xo[MT];
@@ -121,7 +131,7 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
         int r = rstart + t * 16 + lr;
         rows[t] = r;
         int rc = r < r1 ? r : r1 - 1;
-        int xr = a.x_broadcast ? rc - r0 : rc;
+        int xr = a.gather ? a.gather[rc] / a.gather_div : (a.x_broadcast ? rc - r0 : rc);
         xo[t] = (size_t)xr * K + (size_t)kz * KS + (size_t)lg * EL;
     }
 
@@ -168,48 +178,57 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
 #undef MOE_LOAD
 #undef MOE_COMPUTE
 
-    // epilogue: lane holds features f0 + 4*lg + j (j = 0..3) of token rows[t]
-    const int fb = f0 + 4 * lg;
+    // epilogue: lane holds features f0 (+16m) + 4*lg + j (j = 0..3) of token rows[t]
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         const int r = rows[t];
         if (r >= r1) continue;
         float sc = 1.0f;
         if (XM == DT_FP8) sc = a.x_scale[r] * 256.0f;  // undo the 2^-8 of the decode
-        if (EPI == EPI_LOGITS) {
-            float *o = reinterpret_cast<float *>(a.out) + (size_t)kz * a.split_stride +
-                       (size_t)r * a.out_ld;
+        constexpr int NOUT = SAME ? NM : 1;  // 16-feature output blocks per wave
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int f = fb + j;
-                if (f < a.N) o[f] = acc[0][t][j];
-            }
-        } else {
-            float v[4];
+        for (int m = 0; m < NOUT; ++m) {
+            const int fb = f0 + 16 * m + 4 * lg;
+            if (EPI == EPI_LOGITS) {
+                float *o = reinterpret_cast<float *>(a.out) + (size_t)kz * a.split_stride +
+                           (size_t)r * a.out_ld;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (EPI == EPI_SWIGLU) {
-                    const float ga = acc[0][t][j] * sc, ub = acc[NM - 1][t][j] * sc;
-                    v[j] = siluf_(ga) * ub;
-                } else {
-                    v[j] = acc[0][t][j] * sc;
+                for (int j = 0; j < 4; ++j) {
+                    const int f = fb + j;
+                    if (f < a.N) o[f] = acc[m][t][j];
                 }
-            }
-            TW *o = reinterpret_cast<TW *>(a.out) + (size_t)r * a.out_ld + fb;
-            if (sizeof(TW) == 2) {
-                f16x4 h4 = {to_f16(v[0]), to_f16(v[1]), to_f16(v[2]), to_f16(v[3])};
-                *reinterpret_cast<f16x4 *>(o) = h4;
             } else {
-                *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
+                if (fb >= a.N) continue;  // N % 64 == 0 makes this unreachable
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (EPI == EPI_SWIGLU) {
+                        const float ga = acc[0][t][j] * sc, ub = acc[NM - 1][t][j] * sc;
+                        v[j] = siluf_(ga) * ub;
+                    } else {
+                        v[j] = acc[m][t][j] * sc;
+                    }
+                }
+                TW *o = reinterpret_cast<TW *>(a.out) + (size_t)r * a.out_ld + fb;
+                if (sizeof(TW) == 2) {
+                    f16x4 h4 = {to_f16(v[0]), to_f16(v[1]), to_f16(v[2]), to_f16(v[3])};
+                    *reinterpret_cast<f16x4 *>(o) = h4;
+                } else {
+                    *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
+                }
             }
         }
     }
 }
 
+template <int NM, int EPI>
+constexpr int features_per_wave() { return EPI == EPI_SWIGLU ? 16 : 16 * NM; }
+
 template <typename TW, int XM, int NM, int EPI, int U>
 __global__ __launch_bounds__(256) MOE_STREAM_OCC void stream_gemm_kernel(StreamArgs a) {
+    constexpr int FPW = features_per_wave<NM, EPI>();
     const int wave = threadIdx.x >> 6;
-    const int f0 = blockIdx.x * 64 + wave * 16;
+    const int f0 = blockIdx.x * (4 * FPW) + wave * FPW;
     if (f0 >= a.N) return;
     const int g = blockIdx.y;
     const int kz = blockIdx.z % a.ksplit;  // K slice
@@ -237,7 +256,8 @@ __global__ __launch_bounds__(256) MOE_STREAM_OCC void stream_gemm_kernel(StreamA
 
 template <typename TW, int XM, int NM, int EPI>
 hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t s) {
-    dim3 grid((a.N + 63) / 64, n_groups, zblocks * a.ksplit);
+    constexpr int FPB = 4 * features_per_wave<NM, EPI>();  // features per block
+    dim3 grid((a.N + FPB - 1) / FPB, n_groups, zblocks * a.ksplit);
     constexpr int CK = 4 * Frag<TW>::kElems;
     const int NC = a.K / a.ksplit / CK;
     if (a.ksplit < 1 || a.K % (a.ksplit * 4 * CK) != 0) return hipErrorInvalidValue;
@@ -251,14 +271,18 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t 
 }  // namespace
 
 hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int mode,
-                              int n_groups, int zblocks, hipStream_t s) {
+                              int n_groups, int zblocks, long est_rows, hipStream_t s) {
     if (n_groups <= 0 || zblocks <= 0) return hipSuccess;
     if (dtype == DT_F16) {
         if (mode == STREAM_SWIGLU) {
             if (x_dtype == DT_FP8) return launch_t<f16, DT_FP8, 2, EPI_SWIGLU>(a, n_groups, zblocks, s);
             return launch_t<f16, DT_F16, 2, EPI_SWIGLU>(a, n_groups, zblocks, s);
         }
-        if (mode == STREAM_STORE) return launch_t<f16, DT_F16, 1, EPI_STORE>(a, n_groups, zblocks, s);
+        if (mode == STREAM_STORE) {
+            if (est_rows >= MOE_STREAM_STORE_WIDE_ROWS)
+                return launch_t<f16, DT_F16, 2, EPI_STORE>(a, n_groups, zblocks, s);
+            return launch_t<f16, DT_F16, 1, EPI_STORE>(a, n_groups, zblocks, s);
+        }
         return launch_t<f16, DT_F16, 1, EPI_LOGITS>(a, n_groups, zblocks, s);
     }
     if (mode == STREAM_SWIGLU) return launch_t<float, DT_F32, 2, EPI_SWIGLU>(a, n_groups, zblocks, s);

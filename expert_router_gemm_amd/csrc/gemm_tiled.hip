@@ -39,7 +39,7 @@ __device__ __forceinline__ int swz(int r, int c) { return r * PITCH + ((c ^ (r &
 // 8 waves = 2 (rows) x 4 (weight rows); wave (wm, wn) owns x rows
 // wm*64..+64 and, per matrix m, weight rows m*FN + wn*FN/4 .. +FN/4
 // (FN = WR/NM features), as 4 x (4/NM) x NM tiles of 16x16x32 MFMAs.
-template <int NM, int EPI>
+template <int NM, int EPI, bool GATHER>
 __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs, int g, int mt,
                                           int nt) {
     constexpr int FN = WR / NM;   // features per tile
@@ -77,6 +77,20 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(reinterpret_cast<const f16 *>(a.x) + (size_t)xrow0 * K), (short)0,
         rows_valid * K * 2, 0x00020000);
+    // gathered x rows (rows named by a.gather): plain global loads from the
+    // row each thread moves; rows past the group repeat its last row (never
+    // stored)
+    const f16 *xgat[2];
+    if (GATHER) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int r = rs + (tid >> 3) + 64 * i;
+            if (r > r1 - 1) r = r1 - 1;
+            xgat[i] = reinterpret_cast<const f16 *>(a.x) +
+                      (size_t)(a.gather[r] / a.gather_div) * K + (tid & 7) * 8;
+        }
+    }
+
     const int ncols = (a.N - n0) < FN ? (a.N - n0) : FN;
     __amdgpu_buffer_rsrc_t wres[NM];
 #pragma unroll
@@ -95,8 +109,12 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
 #define MOE_GLOAD(RA, RB, k0)                                                          \
     {                                                                                  \
         const int kb_ = (k0) * 2;                                                      \
-        _Pragma("unroll") for (int i = 0; i < 2; ++i) RA[i] = __builtin_bit_cast(       \
-            f16x8, __builtin_amdgcn_raw_buffer_load_b128(xres, goff + i * rstep + kb_, 0, 0)); \
+        if (GATHER) {                                                                  \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i) RA[i] = load16(xgat[i] + (k0)); \
+        } else {                                                                       \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i) RA[i] = __builtin_bit_cast(   \
+                f16x8, __builtin_amdgcn_raw_buffer_load_b128(xres, goff + i * rstep + kb_, 0, 0)); \
+        }                                                                              \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) RB[i] = __builtin_bit_cast(       \
             f16x8, __builtin_amdgcn_raw_buffer_load_b128(                              \
                        wres[(i * 64) / FN], goff + ((i * 64) % FN / 64) * rstep + kb_, 0, 0)); \
@@ -203,7 +221,7 @@ constexpr int kMaxGroups = 1024;
 // with 8 XCDs dealt round-robin and a multiple-of-8 feature-tile count, all
 // row tiles of one (group, feature tile) land on the same XCD, so that
 // weight tile is reused from its L2.
-template <int NM, int EPI>
+template <int NM, int EPI, bool GATHER>
 __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int n_ntiles,
                                                               int n_groups) {
     extern __shared__ __attribute__((aligned(16))) f16 lds[];
@@ -252,18 +270,18 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
         }
         const int g = lo;
         const int mt = tile - tstart[g];
-        tile_body<NM, EPI>(a, As, Bs, g, mt, nt);
+        tile_body<NM, EPI, GATHER>(a, As, Bs, g, mt, nt);
     }
 }
 
-template <int NM, int EPI>
+template <int NM, int EPI, bool GATHER>
 hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream_t s) {
     if (n_groups <= 0 || n_groups > kMaxGroups) return hipErrorInvalidValue;
     const int n_ntiles = (a.N + WR / NM - 1) / (WR / NM);
     const size_t lds = (size_t)2 * (BM + WR) * PITCH * sizeof(f16);
     static bool attr_set = false;  // idempotent; a race only repeats the call
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<NM, EPI>,
+        hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<NM, EPI, GATHER>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
@@ -271,15 +289,15 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
     int dev = 0, cus = 256, per_cu = 1;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tiled_gemm_kernel<NM, EPI>, kThreads,
-                                                     lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tiled_gemm_kernel<NM, EPI, GATHER>,
+                                                     kThreads, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
     // every resident workgroup slot, never more than the items
     long grid = (long)cus * per_cu;
     const long items = max_tiles * n_ntiles;
     if (items < grid) grid = items > 0 ? items : 1;
-    hipLaunchKernelGGL((tiled_gemm_kernel<NM, EPI>), dim3((unsigned)grid), dim3(kThreads), lds, s,
-                       a, n_ntiles, n_groups);
+    hipLaunchKernelGGL((tiled_gemm_kernel<NM, EPI, GATHER>), dim3((unsigned)grid), dim3(kThreads),
+                       lds, s, a, n_ntiles, n_groups);
     return hipGetLastError();
 }
 
@@ -291,9 +309,11 @@ bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype) {
 
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,
                              hipStream_t s) {
-    if (mode == STREAM_SWIGLU) return launch_t<2, 1>(a, n_groups, max_tiles, s);
-    if (mode == STREAM_STORE) return launch_t<1, 0>(a, n_groups, max_tiles, s);
-    return launch_t<1, 2>(a, n_groups, max_tiles, s);
+    if (mode == STREAM_SWIGLU)
+        return a.gather ? launch_t<2, 1, true>(a, n_groups, max_tiles, s)
+                        : launch_t<2, 1, false>(a, n_groups, max_tiles, s);
+    if (mode == STREAM_STORE) return launch_t<1, 0, false>(a, n_groups, max_tiles, s);
+    return launch_t<1, 2, false>(a, n_groups, max_tiles, s);
 }
 
 }  // namespace moe

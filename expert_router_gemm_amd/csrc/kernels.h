@@ -14,6 +14,8 @@ struct StreamArgs {
     const void *x;          // [rows][K] activations (dtype, or fp8 codes)
     const float *x_scale;   // fp8 rows: per-row scale
     int x_broadcast;        // x row = r - group start (shared experts)
+    const int32_t *gather;  // if set: x row = gather[r] / gather_div (perm_src / top_k)
+    int gather_div;
     const int32_t *offsets; // [G+1] group row ranges, or NULL: uniform groups
     int rows_per_group;     // uniform groups: group g = rows [g*rpg, (g+1)*rpg)
     const void *w0;         // [G][N][K]: gate (SWIGLU) or the only matrix
@@ -28,8 +30,9 @@ struct StreamArgs {
 
 // dtype: DT_F16 / DT_F32 (weights and output); x_dtype: dtype or DT_FP8.
 // Grid: ceil(N/64) x n_groups x zblocks; see gemm_stream.hip.
+// est_rows: expected rows per group (host estimate), picks the kernel shape.
 hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int mode,
-                              int n_groups, int zblocks, hipStream_t s);
+                              int n_groups, int zblocks, long est_rows, hipStream_t s);
 
 // LDS-tiled persistent variant for groups of many rows (fp16 only, no K
 // split).  max_tiles bounds the total 128-row tiles (sizes the grid).

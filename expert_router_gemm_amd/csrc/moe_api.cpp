@@ -114,7 +114,7 @@ Layout layout(const moe_shape &s, int T) {
     L.offsets = take((size_t)(s.n_slots + 1) * 4);
     L.perm_src = take(TK * 4);
     L.inv_pos = take(TK * 4);
-    L.x_perm = take(TK * s.hidden * xsz);
+    L.x_perm = take(s.dispatch == MOE_FP8_E4M3 ? TK * s.hidden * xsz : 0);  // fp8 copies only
     L.x_scale = take(TK * 4);
     const size_t hm_rows = TK > nsh * T ? TK : nsh * T;
     L.hm = take(hm_rows * s.inter * isz);
@@ -139,7 +139,7 @@ hipError_t gemm(const StreamArgs &a, int dtype, int x_dtype, int mode, int n_gro
                 long est_rows, long cap_rows, hipStream_t st) {
     if (est_rows >= kTiledMinRows && tiled_gemm_supported(a, dtype, x_dtype))
         return launch_tiled_gemm(a, mode, n_groups, cap_rows / 128 + n_groups, st);
-    return launch_stream_gemm(a, dtype, x_dtype, mode, n_groups, zblocks, st);
+    return launch_stream_gemm(a, dtype, x_dtype, mode, n_groups, zblocks, est_rows, st);
 }
 
 int ffn_zblocks(int cap_rows, int n_groups) {
@@ -178,7 +178,7 @@ hipError_t route_impl(const moe_shape &s, int T, const void *h, const void *w_ro
     } else {
         const int rb = (T + 63) / 64;
         const int zb = rb * a.ksplit <= 65535 ? rb : 65535 / a.ksplit;  // rows stride by gridDim.z
-        e = launch_stream_gemm(a, s.act, s.act, STREAM_LOGITS, 1, zb, st);
+        e = launch_stream_gemm(a, s.act, s.act, STREAM_LOGITS, 1, zb, T, st);
     }
     if (e != hipSuccess) return e;
     return launch_topk(logits_buf, a.ksplit, a.split_stride, N, T, s.n_experts, s.top_k, gate,
@@ -216,12 +216,15 @@ hipError_t dispatch_impl(const moe_shape &s, int T, const void *h, const int32_t
 
 hipError_t ffn_up_impl(const moe_shape &s, int n_groups, int zblocks, long est_rows,
                        long cap_rows, const void *x, int x_dtype, const float *x_scale,
-                       int x_broadcast, const int32_t *offsets, int rows_per_group,
-                       const void *w_gate, const void *w_up, void *hm, hipStream_t st) {
+                       int x_rows, const int32_t *gather, const int32_t *offsets,
+                       int rows_per_group, const void *w_gate, const void *w_up, void *hm,
+                       hipStream_t st) {
     StreamArgs a{};
     a.x = x;
     a.x_scale = x_scale;
-    a.x_broadcast = x_broadcast;
+    a.x_broadcast = x_rows == MOE_X_SHARED;
+    a.gather = x_rows == MOE_X_GATHER ? gather : nullptr;
+    a.gather_div = s.top_k;
     a.offsets = offsets;
     a.rows_per_group = rows_per_group;
     a.w0 = w_gate;
@@ -348,8 +351,12 @@ MOE_EXPORT moe_status moe_dispatch(const moe_shape *shape, int32_t T, const void
         TRY(need4(topk_idx));
         TRY(need4(map->rep_off));
         TRY(need4(map->rep_slot));
-        TRY(need(x_perm));
-        if (shape->dispatch == MOE_FP8_E4M3) TRY(need4(x_scale));
+        if (shape->dispatch == MOE_FP8_E4M3) {  // quantised rows must be stored
+            TRY(need(x_perm));
+            TRY(need4(x_scale));
+        } else {
+            TRY(need_opt(x_perm));  // NULL: indices only, the GEMM gathers rows
+        }
         TRY(need4(perm_src));
         TRY(need4(inv_pos));
     }
@@ -364,12 +371,19 @@ MOE_EXPORT moe_status moe_dispatch(const moe_shape *shape, int32_t T, const void
 
 MOE_EXPORT moe_status moe_expert_ffn_up(const moe_shape *shape, int32_t n_groups,
                                         int32_t cap_rows, const void *x, int32_t x_dtype,
-                                        const float *x_scale, int32_t x_broadcast,
-                                        const int32_t *offsets, const void *w_gate,
-                                        const void *w_up, void *hm, void *stream) {
+                                        const float *x_scale, int32_t x_rows,
+                                        const int32_t *gather, const int32_t *offsets,
+                                        const void *w_gate, const void *w_up, void *hm,
+                                        void *stream) {
     TRY(check_ffn_common(shape, n_groups, cap_rows));
     if (x_dtype != shape->act && !(x_dtype == MOE_FP8_E4M3 && shape->act == MOE_F16))
         return MOE_ERR_DTYPE;
+    if (x_rows != MOE_X_PERMUTED && x_rows != MOE_X_SHARED && x_rows != MOE_X_GATHER)
+        return MOE_ERR_INVALID_ARG;
+    if (x_rows == MOE_X_GATHER) {
+        TRY(need4(gather));
+        if (x_dtype == MOE_FP8_E4M3) return MOE_ERR_DTYPE;  // fp8 rows are dispatched copies
+    }
     TRY(need(x));
     if (x_dtype == MOE_FP8_E4M3) TRY(need4(x_scale));
     TRY(need4(offsets));
@@ -379,9 +393,8 @@ MOE_EXPORT moe_status moe_expert_ffn_up(const moe_shape *shape, int32_t n_groups
     if (cap_rows == 0) return MOE_OK;
     TRY(device_ok());
     LAUNCH(ffn_up_impl(*shape, n_groups, ffn_zblocks(cap_rows, n_groups),
-                       est_group_rows(*shape, cap_rows), cap_rows, x,
-                       x_dtype, x_scale, x_broadcast ? 1 : 0, offsets, 0, w_gate, w_up, hm,
-                       (hipStream_t)stream));
+                       est_group_rows(*shape, cap_rows), cap_rows, x, x_dtype, x_scale, x_rows,
+                       gather, offsets, 0, w_gate, w_up, hm, (hipStream_t)stream));
     return MOE_OK;
 }
 
@@ -404,17 +417,18 @@ MOE_EXPORT moe_status moe_expert_ffn_down(const moe_shape *shape, int32_t n_grou
 
 MOE_EXPORT moe_status moe_expert_ffn(const moe_shape *shape, int32_t n_groups, int32_t cap_rows,
                                      const void *x, int32_t x_dtype, const float *x_scale,
-                                     int32_t x_broadcast, const int32_t *offsets,
-                                     const void *w_gate, const void *w_up, const void *w_down,
-                                     void *y, void *ws, size_t ws_bytes, void *stream) {
+                                     int32_t x_rows, const int32_t *gather,
+                                     const int32_t *offsets, const void *w_gate,
+                                     const void *w_up, const void *w_down, void *y, void *ws,
+                                     size_t ws_bytes, void *stream) {
     TRY(check_ffn_common(shape, n_groups, cap_rows));
     const size_t req = up256((size_t)cap_rows * shape->inter * act_bytes(*shape));
     if (cap_rows > 0 && (!ws || ws_bytes < req)) return MOE_ERR_WORKSPACE;
     if (cap_rows > 0 && !aligned16(ws)) return MOE_ERR_ALIGN;
     TRY(need(w_down));
     TRY(need(y));
-    moe_status st = moe_expert_ffn_up(shape, n_groups, cap_rows, x, x_dtype, x_scale,
-                                      x_broadcast, offsets, w_gate, w_up, ws, stream);
+    moe_status st = moe_expert_ffn_up(shape, n_groups, cap_rows, x, x_dtype, x_scale, x_rows,
+                                      gather, offsets, w_gate, w_up, ws, stream);
     if (st != MOE_OK) return st;
     return moe_expert_ffn_down(shape, n_groups, cap_rows, ws, offsets, w_down, y, stream);
 }
@@ -477,12 +491,17 @@ MOE_EXPORT moe_status moe_layer_forward(const moe_shape *shape, const moe_weight
 
     LAUNCH(route_impl(s, T, h, w->w_router, w->bias, topk_idx, topk_w, gate ? sgate : nullptr,
                       nullptr, at<float *>(ws, L.logits), st));
-    LAUNCH(dispatch_impl(s, T, h, topk_idx, *map, at<void *>(ws, L.x_perm), x_scale,
-                         at<int32_t *>(ws, L.counts), offsets, at<int32_t *>(ws, L.perm_src),
-                         inv_pos, at<void *>(ws, L.disp), st));
+    // fp8 rows are quantised copies; otherwise the gate/up GEMM gathers the
+    // hidden rows through perm_src and dispatch writes indices only
+    const bool copy_rows = s.dispatch == MOE_FP8_E4M3;
+    int32_t *perm_src = at<int32_t *>(ws, L.perm_src);
+    LAUNCH(dispatch_impl(s, T, h, topk_idx, *map, copy_rows ? at<void *>(ws, L.x_perm) : nullptr,
+                         x_scale, at<int32_t *>(ws, L.counts), offsets, perm_src, inv_pos,
+                         at<void *>(ws, L.disp), st));
     const int z = ffn_zblocks(cap, s.n_slots);
     const long est = est_group_rows(s, cap);
-    LAUNCH(ffn_up_impl(s, s.n_slots, z, est, cap, at<void *>(ws, L.x_perm), s.dispatch, x_scale, 0,
+    LAUNCH(ffn_up_impl(s, s.n_slots, z, est, cap, copy_rows ? at<void *>(ws, L.x_perm) : h,
+                       s.dispatch, x_scale, copy_rows ? MOE_X_PERMUTED : MOE_X_GATHER, perm_src,
                        offsets, 0, w->w_gate, w->w_up, at<void *>(ws, L.hm), st));
     LAUNCH(ffn_down_impl(s, s.n_slots, z, est, cap, at<void *>(ws, L.hm), offsets, 0, w->w_down,
                          at<void *>(ws, L.y), st));
@@ -492,8 +511,8 @@ MOE_EXPORT moe_status moe_layer_forward(const moe_shape *shape, const moe_weight
         const int zs = (T + 63) / 64 < 65535 ? (T + 63) / 64 : 65535;
         const long cap_sh = (long)s.n_shared * T;
         const long est_sh = est_group_rows(s, cap_sh);
-        LAUNCH(ffn_up_impl(s, s.n_shared, zs, est_sh, cap_sh, h, s.act, nullptr, 1, nullptr, T,
-                           w->sh_gate, w->sh_up, at<void *>(ws, L.hm), st));
+        LAUNCH(ffn_up_impl(s, s.n_shared, zs, est_sh, cap_sh, h, s.act, nullptr, MOE_X_SHARED,
+                           nullptr, nullptr, T, w->sh_gate, w->sh_up, at<void *>(ws, L.hm), st));
         LAUNCH(ffn_down_impl(s, s.n_shared, zs, est_sh, cap_sh, at<void *>(ws, L.hm), nullptr, T,
                              w->sh_down, shared_y, st));
     }

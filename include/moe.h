@@ -63,6 +63,13 @@ typedef enum { MOE_F32 = 0, MOE_F16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 /* moe_shape.flags */
 #define MOE_F_SHARED 1u /* layer has shared experts: add their gated sum */
 
+/* Where the expert GEMM finds the input row of output row r of group g
+ * (x_rows argument of moe_expert_ffn_up / moe_expert_ffn). */
+#define MOE_X_PERMUTED 0 /* x[r]: rows already permuted (moe_dispatch's x_perm) */
+#define MOE_X_SHARED 1   /* x[r - offsets[g]]: every group reads the same rows */
+#define MOE_X_GATHER 2   /* x[gather[r] / top_k]: gather = perm_src from
+                            moe_dispatch, x = h (fp16/fp32 rows only) */
+
 /* Layer description (host struct). */
 typedef struct {
     int32_t hidden;    /* H: 7168 for DeepSeek-V3 (section 2.2, Step 1) */
@@ -131,7 +138,9 @@ moe_status moe_route(const moe_shape *shape, int32_t T, const void *h,
  *                      x_scale[row] = amax/448 and codes
  *                      E4M3_RNE(clamp(h * (448/amax), -448, 448)) (section
  *                      2.3: FP8 halves the dispatch payload); x_scale may be
- *                      NULL otherwise.  Rows >= P are untouched.
+ *                      NULL otherwise.  Rows >= P are untouched.  Without
+ *                      FP8, x_perm may be NULL: only the indices are written
+ *                      and the gate/up GEMM gathers h rows (MOE_X_GATHER).
  * Workspace: ws of at least moe_workspace_bytes(shape, T) bytes. */
 moe_status moe_dispatch(const moe_shape *shape, int32_t T, const void *h,
                         const int32_t *topk_idx, const moe_slot_map *map, void *x_perm,
@@ -142,14 +151,15 @@ moe_status moe_dispatch(const moe_shape *shape, int32_t T, const void *h,
 /* Step 3, first half (section 一 gives gate/up [7168, 2048]): for every group
  * g < n_groups and every row r in [offsets[g], offsets[g+1]):
  *   hm[r] = silu(w_gate[g] . x_r) * (w_up[g] . x_r),  silu(z) = z*sigmoid(z)
- * x_r = x[r] normally, or x[r - offsets[g]] when x_broadcast != 0 (every
- * group reads the same rows: how the shared experts see all tokens).  With
- * x_dtype FP8_E4M3 the row is decoded and multiplied by x_scale[r].
+ * x_r per x_rows: MOE_X_PERMUTED x[r]; MOE_X_SHARED x[r - offsets[g]] (how
+ * the shared experts see all tokens); MOE_X_GATHER x[gather[r] / top_k]
+ * (gather int32 [cap_rows], NULL otherwise).  With x_dtype FP8_E4M3 (only
+ * with MOE_X_PERMUTED) the row is decoded and multiplied by x_scale[r].
  * hm [cap_rows][I] (act).  cap_rows (host) bounds offsets[n_groups]; groups
  * with no rows read no weights. */
 moe_status moe_expert_ffn_up(const moe_shape *shape, int32_t n_groups, int32_t cap_rows,
                              const void *x, int32_t x_dtype, const float *x_scale,
-                             int32_t x_broadcast, const int32_t *offsets,
+                             int32_t x_rows, const int32_t *gather, const int32_t *offsets,
                              const void *w_gate, const void *w_up, void *hm, void *stream);
 
 /* Step 3, second half (section 6.3's 88 MB per expert = three 7168 x 2048
@@ -162,9 +172,9 @@ moe_status moe_expert_ffn_down(const moe_shape *shape, int32_t n_groups, int32_t
 /* Step 3 whole: up then down, with hm in the workspace. */
 moe_status moe_expert_ffn(const moe_shape *shape, int32_t n_groups, int32_t cap_rows,
                           const void *x, int32_t x_dtype, const float *x_scale,
-                          int32_t x_broadcast, const int32_t *offsets, const void *w_gate,
-                          const void *w_up, const void *w_down, void *y, void *ws,
-                          size_t ws_bytes, void *stream);
+                          int32_t x_rows, const int32_t *gather, const int32_t *offsets,
+                          const void *w_gate, const void *w_up, const void *w_down, void *y,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /* Steps 4 and 5 (section 2.2):
  *   out[t] = sum_{k = 0..K-1, inv_pos[t][k] >= 0} topk_w[t][k] * y[inv_pos[t][k]]

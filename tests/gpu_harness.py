@@ -168,15 +168,21 @@ def gpu_stages(L: Layer):
     hm = torch.empty((max(cap, 1), I), dtype=act, device=dev)
     y = torch.empty((max(cap, 1), H), dtype=act, device=dev)
     xdt = moe.MOE_FP8_E4M3 if fp8 else act_code(cfg)
-    moe.moe_expert_ffn_up(L.shape, S, cap, xp, xdt, xs if fp8 else None, 0, offsets,
-                          L.d["G"], L.d["U"], hm)
+    moe.moe_expert_ffn_up(L.shape, S, cap, xp, xdt, xs if fp8 else None, moe.MOE_X_PERMUTED,
+                          None, offsets, L.d["G"], L.d["U"], hm)
+    hm_gather = None
+    if not fp8:  # the same rows gathered straight from h must give the same hm
+        hm_gather = torch.empty_like(hm)
+        moe.moe_expert_ffn_up(L.shape, S, cap, L.d["h"], act_code(cfg), None, moe.MOE_X_GATHER,
+                              perm, offsets, L.d["G"], L.d["U"], hm_gather)
     moe.moe_expert_ffn_down(L.shape, S, cap, hm, offsets, L.d["D"], y)
     shy = None
     if cfg.n_shared:
         shoff = to_dev(np.arange(cfg.n_shared + 1, dtype=np.int32) * T)
         shy = torch.empty((cfg.n_shared * T, H), dtype=act, device=dev)
         moe.moe_expert_ffn(L.shape, cfg.n_shared, cfg.n_shared * T, L.d["h"], act_code(cfg),
-                           None, 1, shoff, L.d["SG"], L.d["SU"], L.d["SD"], shy, ws)
+                           None, moe.MOE_X_SHARED, None, shoff, L.d["SG"], L.d["SU"], L.d["SD"],
+                           shy, ws)
     out = torch.empty((T, H), dtype=act, device=dev)
     moe.moe_combine(L.shape, T, y, inv, tw, shy, sg, out)
     torch.cuda.synchronize()
@@ -186,6 +192,7 @@ def gpu_stages(L: Layer):
                 x_perm=host(xp[:P]), x_scale=host(xs[:P]) if fp8 else None, counts=host(counts),
                 offsets=host(offsets), perm_src=host(perm[:P]), inv_pos=host(inv),
                 hm=host(hm[:P]), y=host(y[:P]), shared_y=host(shy), out=host(out), P=P,
+                hm_gather=None if hm_gather is None else host(hm_gather[:P]),
                 perm_tail=host(perm[P:]))
 
 

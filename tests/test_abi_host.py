@@ -52,15 +52,15 @@ def test_workspace_bytes():
     s = _shape()
     w = moe.moe_workspace_bytes(s, 256)
     T, K, H, I, E = 256, 8, 7168, 2048, 256
-    # at least x_perm, hm and y plus the routing buffers
-    assert w >= T * K * H * 2 * 2 + T * K * I * 2 + T * (E + 1) * 4
+    # at least hm and y plus the routing buffers (fp16 rows are gathered, not copied)
+    assert w >= T * K * H * 2 + T * K * I * 2 + T * (E + 1) * 4
     assert moe.moe_workspace_bytes(s, 0) > 0
     assert moe.moe_workspace_bytes(_shape(hidden=100), 16) == 0
     assert moe.moe_workspace_bytes(s, -1) == 0
     sh = _shape(n_shared=2, shared=True, n_slots=256)
     assert moe.moe_workspace_bytes(sh, 128) > moe.moe_workspace_bytes(_shape(n_slots=256), 128)
-    f8 = _shape(dispatch=moe.MOE_FP8_E4M3)
-    assert moe.moe_workspace_bytes(f8, 512) < moe.moe_workspace_bytes(_shape(), 512)
+    f8 = _shape(dispatch=moe.MOE_FP8_E4M3)  # adds the quantised row copies: 1 B/element
+    assert moe.moe_workspace_bytes(f8, 512) >= moe.moe_workspace_bytes(_shape(), 512) + 512 * K * H
 
 
 FAKE = 0x100000  # aligned, never dereferenced: validation fails first
@@ -107,15 +107,21 @@ def test_other_entry_points_validate_before_launch():
     f8 = _shape(dispatch=moe.MOE_FP8_E4M3)
     assert L.moe_dispatch(ctypes.byref(f8), 16, FAKE, FAKE, ctypes.byref(sm), FAKE, None, FAKE,
                           FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
-    assert L.moe_expert_ffn_up(ctypes.byref(s), 0, 16, FAKE, 1, None, 0, FAKE, FAKE, FAKE, FAKE,
-                               None) == 2
-    assert L.moe_expert_ffn_up(ctypes.byref(s), 4, 16, FAKE, 2, None, 0, FAKE, FAKE, FAKE, FAKE,
-                               None) == 1  # fp8 rows need scales
+    assert L.moe_expert_ffn_up(ctypes.byref(s), 0, 16, FAKE, 1, None, 0, None, FAKE, FAKE, FAKE,
+                               FAKE, None) == 2
+    assert L.moe_expert_ffn_up(ctypes.byref(s), 4, 16, FAKE, 2, None, 0, None, FAKE, FAKE, FAKE,
+                               FAKE, None) == 1  # fp8 rows need scales
     assert L.moe_expert_ffn_up(ctypes.byref(_shape(act=0, dispatch=0)), 4, 16, FAKE, 2, FAKE, 0,
-                               FAKE, FAKE, FAKE, FAKE, None) == 3
+                               None, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert L.moe_expert_ffn_up(ctypes.byref(s), 4, 16, FAKE, 1, None, 2, None, FAKE, FAKE, FAKE,
+                               FAKE, None) == 1  # gather needs the index array
+    assert L.moe_expert_ffn_up(ctypes.byref(s), 4, 16, FAKE, 2, FAKE, 2, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, None) == 3  # fp8 rows cannot be gathered from h
+    assert L.moe_expert_ffn_up(ctypes.byref(s), 4, 16, FAKE, 1, None, 7, None, FAKE, FAKE, FAKE,
+                               FAKE, None) == 1  # unknown row mode
     assert L.moe_expert_ffn_down(ctypes.byref(s), 4, -1, FAKE, FAKE, FAKE, FAKE, None) == 2
-    assert L.moe_expert_ffn(ctypes.byref(s), 4, 16, FAKE, 1, None, 0, FAKE, FAKE, FAKE, FAKE,
-                            FAKE, FAKE, 8, None) == 5
+    assert L.moe_expert_ffn(ctypes.byref(s), 4, 16, FAKE, 1, None, 0, None, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, FAKE, 8, None) == 5
     assert L.moe_combine(ctypes.byref(s), 16, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 1
     w = moe.Weights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)
     assert L.moe_layer_forward(ctypes.byref(s), ctypes.byref(w), ctypes.byref(sm), 16, FAKE,

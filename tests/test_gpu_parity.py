@@ -106,9 +106,12 @@ def _check_dispatch(L, st):
 
 def _check_ffn(L, st):
     """y rows against the oracle SwiGLU on the GPU's own dispatched rows.
-    Tolerance: the output bar (fp16 y)."""
+    Tolerance: the output bar (fp16 y).  Gathering the rows from h through
+    perm_src must give bit-identical hm."""
     cfg = L.cfg
     off = st["offsets"]
+    if st["hm_gather"] is not None:
+        assert np.array_equal(st["hm_gather"].view(np.uint8), st["hm"].view(np.uint8))
     dec = oracle.e4m3_decode_table()
     for s in range(len(L.slot_experts)):
         a, b = off[s], off[s + 1]
