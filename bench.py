@@ -3,11 +3,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 
-One step = one pass of the whole path over one batch resident in HBM:
-moe_route -> moe_dispatch -> moe_expert_ffn_up -> moe_expert_ffn_down ->
-(shared experts) -> moe_combine, through libmoe's C ABI on torch's current
-stream (the same kernels, in the same order, as moe_layer_forward, which is
-timed too and reported beside it).  The default workload is the EP=8
+One step = one pass of the whole path over one batch resident in HBM: one
+call of moe_layer_forward_profiled (router + top-K, dispatch, gate/up and
+down grouped GEMMs with the shared experts, combine) through libmoe's C ABI
+on torch's current stream; the call records HIP events around the gate/up
+GEMM, which give the roofline record.  The same pass without events, a
+per-stage breakdown and the staged entry points are reported beside it.  The default workload is the EP=8
 rank-share decode batch: 256 tokens, hidden 7168, top-8 of 256 experts, the
 32 local experts' SwiGLU 7168x2048 weights in fp16.
 
@@ -164,6 +165,12 @@ def fused_step(ctx):
     import expert_router_gemm_amd as moe
     moe.moe_layer_forward(ctx["shape"], ctx["wmap"], ctx["smap"], ctx["cfg"].T, ctx["d"]["h"],
                           ctx["b"]["out2"], ctx["b"]["ws"])
+
+
+def profiled_step(ctx, prof):
+    import expert_router_gemm_amd as moe
+    moe.moe_layer_forward_profiled(ctx["shape"], ctx["wmap"], ctx["smap"], ctx["cfg"].T,
+                                   ctx["d"]["h"], ctx["b"]["out2"], ctx["b"]["ws"], prof)
 
 
 # ------------------------------------------------------------------ accounting
@@ -334,37 +341,57 @@ def main():
     cfg = ctx["cfg"]
 
     for _ in range(args.warmup):
-        staged_step(ctx)
         fused_step(ctx)
+        staged_step(ctx)
     torch.cuda.synchronize()
 
+    # Timed region: K passes of moe_layer_forward_profiled.  Every EVERY-th
+    # pass records HIP events on the launch stream around the gate/up GEMM
+    # (events[2], [3]); the others pass no events (an event record costs the
+    # stream a few microseconds).
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    EVERY = 5
+    ev_up = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for i in range(0, K, EVERY)}
+    no_ev = moe.make_profile([])
+    profs = [moe.make_profile([None, None, *ev_up[i]]) if i in ev_up else no_ev
+             for i in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        staged_step(ctx, evs[i])
+        profiled_step(ctx, profs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    log(f"[bench] timed {K} staged steps: {wall * 1e3 / K:.3f} ms/step")
+    ms_per_step = wall * 1e3 / K
+    up_ms = statistics.mean(a.elapsed_time(b) for a, b in ev_up.values())
+    log(f"[bench] timed {K} steps of moe_layer_forward_profiled: {ms_per_step:.4f} ms/step, "
+        f"gate/up {up_ms * 1e3:.1f} us")
 
-    # the fused entry point, same kernels
+    # References, not the reported value: the entry point without events, a
+    # per-stage breakdown, and the staged entry points (same kernels).
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record()
     for _ in range(K):
         fused_step(ctx)
     e1.record()
     torch.cuda.synchronize()
-    fused_ms = e0.elapsed_time(e1) / K
+    plain_ms = e0.elapsed_time(e1) / K
+    ev_all = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    for i in range(K):
+        profiled_step(ctx, moe.make_profile(ev_all[i]))
+    torch.cuda.synchronize()
+    names = ["route", "dispatch", "ffn_up", "ffn_down+shared", "combine"]
+    stage_ms = {n: statistics.median(ev[j].elapsed_time(ev[j + 1]) for ev in ev_all)
+                for j, n in enumerate(names)}
+    e0.record()
+    for _ in range(K):
+        staged_step(ctx)
+    e1.record()
+    torch.cuda.synchronize()
+    staged_ms = e0.elapsed_time(e1) / K
     same = bool(torch.equal(ctx["b"]["out"], ctx["b"]["out2"]))
 
-    names = ["route", "dispatch", "ffn_up", "ffn_down", "shared_ffn+combine"]
-    stage_ms = {n: statistics.median(ev[j].elapsed_time(ev[j + 1]) for ev in evs)
-                for j, n in enumerate(names)}
-    up_ms = statistics.mean(ev[2].elapsed_time(ev[3]) for ev in evs)
     work = algorithmic_work(ctx)
-    ms_per_step = wall * 1e3 / K
     value = cfg.T / (ms_per_step / 1e3)
 
     decode = args.workload != 4
@@ -377,7 +404,8 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_F16_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                     traffic=load_traffic(cfg.name))
-    roof.update(kernel="stream_gemm_kernel (SwiGLU gate/up)", launch_ms=round(up_ms, 4),
+    roof.update(kernel=("stream_gemm_kernel" if decode else "tiled_gemm_kernel") +
+                " (SwiGLU gate/up, in moe_layer_forward)", launch_ms=round(up_ms, 4),
                 algorithmic_bytes=work["up"]["bytes"], algorithmic_flops=work["up"]["flops"])
 
     if args.copy_calibration:
@@ -412,10 +440,11 @@ def main():
                    "ep_size": cfg.ep_size, "ep_rank": cfg.ep_rank},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "layer": {"hbm_gbs": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+        "layer": {"entry": "moe_layer_forward_profiled", "hbm_gbs": round(layer_gbs, 1),
+                  "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                   "algorithmic_bytes": work["layer_bytes"], "rows": work["P"],
-                  "touched_slots": work["touched"], "fused_entry_ms": round(fused_ms, 4),
-                  "fused_equals_staged": same,
+                  "touched_slots": work["touched"], "no_events_ms": round(plain_ms, 4),
+                  "staged_calls_ms": round(staged_ms, 4), "staged_equals_fused": same,
                   "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}},
     }
     print(json.dumps(rec))

@@ -20,8 +20,8 @@ MOE_X_PERMUTED, MOE_X_SHARED, MOE_X_GATHER = 0, 1, 2
 
 EXPORTED = (
     "moe_route", "moe_dispatch", "moe_expert_ffn_up", "moe_expert_ffn_down",
-    "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_workspace_bytes",
-    "moe_status_str", "moe_version",
+    "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_profiled",
+    "moe_workspace_bytes", "moe_status_str", "moe_version",
 )
 
 
@@ -45,6 +45,10 @@ class Shape(ctypes.Structure):
 class SlotMap(ctypes.Structure):
     _fields_ = [("rep_off", ctypes.c_void_p), ("rep_slot", ctypes.c_void_p),
                 ("seed", ctypes.c_uint64)]
+
+
+class Profile(ctypes.Structure):
+    _fields_ = [("events", ctypes.c_void_p * 6)]
 
 
 class Weights(ctypes.Structure):
@@ -74,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [SP, I32, P, P, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [SP, ctypes.POINTER(Weights), ctypes.POINTER(SlotMap),
                                         I32, P, P, P, SZ, P]
+        L.moe_layer_forward_profiled.argtypes = [SP, ctypes.POINTER(Weights),
+                                                 ctypes.POINTER(SlotMap), I32, P, P, P, SZ,
+                                                 ctypes.POINTER(Profile), P]
         L.moe_workspace_bytes.argtypes = [SP, I32]
         L.moe_workspace_bytes.restype = SZ
         L.moe_status_str.argtypes = [ctypes.c_int]
@@ -181,6 +188,29 @@ def moe_layer_forward(shape, weights: Weights, slot_map: SlotMap, T, h, out, ws,
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(shape), ctypes.byref(weights), ctypes.byref(slot_map), T, _p(h), _p(out),
         _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def make_profile(events) -> Profile:
+    """Stage-boundary events (torch.cuda.Event or raw hipEvent_t ints, or
+    None); a torch event is recorded once first so its handle exists."""
+    handles = []
+    for e in list(events) + [None] * (6 - len(events)):
+        if e is None:
+            handles.append(None)
+        elif isinstance(e, int):
+            handles.append(e)
+        else:
+            if not e.cuda_event:
+                e.record()
+            handles.append(e.cuda_event)
+    return Profile((ctypes.c_void_p * 6)(*handles))
+
+
+def moe_layer_forward_profiled(shape, weights: Weights, slot_map: SlotMap, T, h, out, ws,
+                               profile: Profile, stream=None):
+    _check("moe_layer_forward_profiled", lib().moe_layer_forward_profiled(
+        ctypes.byref(shape), ctypes.byref(weights), ctypes.byref(slot_map), T, _p(h), _p(out),
+        _p(ws), _nbytes(ws), ctypes.byref(profile), _stream(stream)))
 
 
 def make_weights(*, w_router, bias=None, w_gate, w_up, w_down, sh_gate=None, sh_up=None,

@@ -127,7 +127,12 @@ constexpr int kSmallT = 1024, kSmallS = 256;
 
 constexpr int kSmallE = 1024, kSmallNnz = 2048;
 
+// KT > 0: top_k known at compile time (loads issued together, no branches);
+// KT == 0: any top_k up to 16.
+template <int KT>
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
+    constexpr int KMAX = KT > 0 ? KT : 16;
+    const int K = KT > 0 ? KT : a.K;
     __shared__ unsigned long long masks[kSmallT / 64][kSmallS];
     __shared__ int base[kSmallT / 64][kSmallS];  // rows of earlier chunks, per slot
     __shared__ int offs[kSmallS + 1];
@@ -146,12 +151,12 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
     const int t = tid;
     const unsigned long long bit = 1ull << lane;
     if (t < a.T) {
-        int ex[16];
+        int ex[KMAX];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) ex[k] = k < a.K ? a.topk_idx[(size_t)t * a.K + k] : -1;
+        for (int k = 0; k < KMAX; ++k) ex[k] = k < K ? a.topk_idx[(size_t)t * K + k] : -1;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            if (k >= a.K) break;
+        for (int k = 0; k < KMAX; ++k) {
+            if (k >= K) break;
             const int e = ex[k];
             int sl = -1;
             if (e >= 0 && e < a.E) {
@@ -159,13 +164,13 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
                 if (n > 0) {
                     int r = 0;
                     if (n > 1)
-                        r = (int)(splitmix64(a.seed ^ ((uint64_t)t * (uint64_t)a.K + (uint64_t)k)) %
+                        r = (int)(splitmix64(a.seed ^ ((uint64_t)t * (uint64_t)K + (uint64_t)k)) %
                                   (uint64_t)n);
                     sl = table_in_lds ? rslot[lo + r] : a.rep_slot[lo + r];
                     if (sl < 0 || sl >= a.S) sl = -1;
                 }
             }
-            a.pair_code[(size_t)t * a.K + k] = sl;
+            a.pair_code[(size_t)t * K + k] = sl;
             if (sl >= 0) atomicOr(&masks[wave][sl], bit);
         }
     }
@@ -199,8 +204,10 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
     }
     __syncthreads();
     if (t < a.T)
-        for (int k = 0; k < a.K; ++k) {
-            const size_t p = (size_t)t * a.K + k;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k >= K) break;
+            const size_t p = (size_t)t * K + k;
             const int sl = a.pair_code[p];  // written by this thread above
             if (sl < 0) {
                 a.inv_pos[p] = -1;
@@ -318,7 +325,12 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
     const int C = (a.T + 63) / 64;
     hipError_t e;
     if (a.T > 0 && a.T <= kSmallT && a.S <= kSmallS && a.E <= kSmallE) {
-        hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, a);
+        if (a.K == 8)
+            hipLaunchKernelGGL(dispatch_small_kernel<8>, dim3(1), dim3(1024), 0, s, a);
+        else if (a.K == 2)
+            hipLaunchKernelGGL(dispatch_small_kernel<2>, dim3(1), dim3(1024), 0, s, a);
+        else
+            hipLaunchKernelGGL(dispatch_small_kernel<0>, dim3(1), dim3(1024), 0, s, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (!a.x_perm) return hipSuccess;  // rows are gathered by the GEMM instead

@@ -230,34 +230,45 @@ __global__ __launch_bounds__(256) MOE_STREAM_OCC void stream_gemm_kernel(StreamA
     const int wave = threadIdx.x >> 6;
     const int f0 = blockIdx.x * (4 * FPW) + wave * FPW;
     if (f0 >= a.N) return;
-    const int g = blockIdx.y;
     const int kz = blockIdx.z % a.ksplit;  // K slice
     const int zr = blockIdx.z / a.ksplit;  // first row block
     const int zn = gridDim.z / a.ksplit;   // row-block stride
-    int r0, r1;
-    if (a.offsets) {
-        r0 = a.offsets[g];
-        r1 = a.offsets[g + 1];
+    int g = blockIdx.y, r0, r1;
+    StreamArgs b = a;
+    if (g < a.n_sec) {  // secondary uniform group (e.g. a shared expert)
+        b.x = a.x2;
+        b.x_broadcast = a.x2_broadcast;
+        b.gather = nullptr;
+        b.w0 = a.w0b;
+        b.w1 = a.w1b;
+        r0 = a.row2_base + g * a.rows2;
+        r1 = r0 + a.rows2;
     } else {
-        r0 = g * a.rows_per_group;
-        r1 = r0 + a.rows_per_group;
+        g -= a.n_sec;
+        if (a.offsets) {
+            r0 = a.offsets[g];
+            r1 = a.offsets[g + 1];
+        } else {
+            r0 = g * a.rows_per_group;
+            r1 = r0 + a.rows_per_group;
+        }
     }
     for (int rb = zr; r0 + rb * 64 < r1; rb += zn) {
         const int rs = r0 + rb * 64;
         const int n = r1 - rs;
         if (n <= 16)
-            stream_pass<TW, XM, NM, EPI, 1, U>(a, g, f0, rs, r0, r1, kz);
+            stream_pass<TW, XM, NM, EPI, 1, U>(b, g, f0, rs, r0, r1, kz);
         else if (n <= 32)
-            stream_pass<TW, XM, NM, EPI, 2, U>(a, g, f0, rs, r0, r1, kz);
+            stream_pass<TW, XM, NM, EPI, 2, U>(b, g, f0, rs, r0, r1, kz);
         else
-            stream_pass<TW, XM, NM, EPI, 4, (U > 2 ? 2 : U)>(a, g, f0, rs, r0, r1, kz);
+            stream_pass<TW, XM, NM, EPI, 4, (U > 2 ? 2 : U)>(b, g, f0, rs, r0, r1, kz);
     }
 }
 
 template <typename TW, int XM, int NM, int EPI>
 hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t s) {
     constexpr int FPB = 4 * features_per_wave<NM, EPI>();  // features per block
-    dim3 grid((a.N + FPB - 1) / FPB, n_groups, zblocks * a.ksplit);
+    dim3 grid((a.N + FPB - 1) / FPB, n_groups + a.n_sec, zblocks * a.ksplit);
     constexpr int CK = 4 * Frag<TW>::kElems;
     const int NC = a.K / a.ksplit / CK;
     if (a.ksplit < 1 || a.K % (a.ksplit * 4 * CK) != 0) return hipErrorInvalidValue;
@@ -272,7 +283,8 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t 
 
 hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int mode,
                               int n_groups, int zblocks, long est_rows, hipStream_t s) {
-    if (n_groups <= 0 || zblocks <= 0) return hipSuccess;
+    if (n_groups + a.n_sec <= 0 || zblocks <= 0) return hipSuccess;
+    if (n_groups + a.n_sec > 65535) return hipErrorInvalidValue;
     if (dtype == DT_F16) {
         if (mode == STREAM_SWIGLU) {
             if (x_dtype == DT_FP8) return launch_t<f16, DT_FP8, 2, EPI_SWIGLU>(a, n_groups, zblocks, s);

@@ -303,8 +303,12 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
 
 }  // namespace
 
+bool tiled_gemm_supported_shape(int K, int dtype, int x_dtype) {
+    return dtype == DT_F16 && x_dtype == DT_F16 && K % (2 * BK) == 0;
+}
+
 bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype) {
-    return dtype == DT_F16 && x_dtype == DT_F16 && a.ksplit == 1 && a.K % (2 * BK) == 0;
+    return a.ksplit == 1 && a.n_sec == 0 && tiled_gemm_supported_shape(a.K, dtype, x_dtype);
 }
 
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,

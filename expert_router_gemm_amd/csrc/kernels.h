@@ -26,6 +26,16 @@ struct StreamArgs {
     int N, K;
     int ksplit;             // LOGITS only: K is split in ksplit equal slices;
     size_t split_stride;    // slice z writes out + z * split_stride (fp32)
+    // Optional secondary groups (stream kernel only), placed before the
+    // groups above in the grid: n_sec groups of rows2 rows each, weights
+    // w0b/w1b [n_sec][N][K], output rows row2_base + g2*rows2 + i, input row
+    // x2[i] (x2_broadcast) or x2[output row].  Lets the shared experts run in
+    // the routed experts' launch.
+    int n_sec;
+    const void *x2;
+    int x2_broadcast;
+    const void *w0b, *w1b;
+    int rows2, row2_base;
 };
 
 // dtype: DT_F16 / DT_F32 (weights and output); x_dtype: dtype or DT_FP8.
@@ -37,6 +47,7 @@ hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int m
 // LDS-tiled persistent variant for groups of many rows (fp16 only, no K
 // split).  max_tiles bounds the total 128-row tiles (sizes the grid).
 bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype);
+bool tiled_gemm_supported_shape(int K, int dtype, int x_dtype);
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,
                              hipStream_t s);
 

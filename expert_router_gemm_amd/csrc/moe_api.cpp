@@ -116,10 +116,10 @@ Layout layout(const moe_shape &s, int T) {
     L.inv_pos = take(TK * 4);
     L.x_perm = take(s.dispatch == MOE_FP8_E4M3 ? TK * s.hidden * xsz : 0);  // fp8 copies only
     L.x_scale = take(TK * 4);
-    const size_t hm_rows = TK > nsh * T ? TK : nsh * T;
-    L.hm = take(hm_rows * s.inter * isz);
-    L.y = take(TK * s.hidden * isz);
-    L.shared_y = take(nsh * T * s.hidden * isz);
+    // routed rows [0, T*K), then the shared experts' rows (n_shared x T)
+    L.hm = take((TK + nsh * T) * s.inter * isz);
+    L.y = take((TK + nsh * T) * s.hidden * isz);
+    L.shared_y = 0;  // inside y, after the routed rows
     L.disp = take(dispatch_scratch_bytes(T, s.top_k, s.n_slots));
     L.total = o;
     return L;
@@ -135,9 +135,13 @@ inline P at(void *ws, size_t off) {
 constexpr int kTiledMinRows = 64;
 constexpr int kTiledRouterMinTokens = 2048;
 
+bool use_tiled(long est_rows, int K, int dtype, int x_dtype) {
+    return est_rows >= kTiledMinRows && tiled_gemm_supported_shape(K, dtype, x_dtype);
+}
+
 hipError_t gemm(const StreamArgs &a, int dtype, int x_dtype, int mode, int n_groups, int zblocks,
                 long est_rows, long cap_rows, hipStream_t st) {
-    if (est_rows >= kTiledMinRows && tiled_gemm_supported(a, dtype, x_dtype))
+    if (a.n_sec == 0 && est_rows >= kTiledMinRows && tiled_gemm_supported(a, dtype, x_dtype))
         return launch_tiled_gemm(a, mode, n_groups, cap_rows / 128 + n_groups, st);
     return launch_stream_gemm(a, dtype, x_dtype, mode, n_groups, zblocks, est_rows, st);
 }
@@ -214,12 +218,32 @@ hipError_t dispatch_impl(const moe_shape &s, int T, const void *h, const int32_t
     return launch_dispatch(d, st);
 }
 
+// Secondary uniform groups riding in the same launch (shared experts).
+struct Secondary {
+    int n = 0;
+    const void *x = nullptr;
+    int x_broadcast = 0;
+    const void *w0 = nullptr, *w1 = nullptr;
+    int rows = 0, row_base = 0;
+};
+
+void set_secondary(StreamArgs &a, const Secondary &sec) {
+    a.n_sec = sec.n;
+    a.x2 = sec.x;
+    a.x2_broadcast = sec.x_broadcast;
+    a.w0b = sec.w0;
+    a.w1b = sec.w1;
+    a.rows2 = sec.rows;
+    a.row2_base = sec.row_base;
+}
+
 hipError_t ffn_up_impl(const moe_shape &s, int n_groups, int zblocks, long est_rows,
                        long cap_rows, const void *x, int x_dtype, const float *x_scale,
                        int x_rows, const int32_t *gather, const int32_t *offsets,
                        int rows_per_group, const void *w_gate, const void *w_up, void *hm,
-                       hipStream_t st) {
+                       hipStream_t st, const Secondary &sec = Secondary()) {
     StreamArgs a{};
+    set_secondary(a, sec);
     a.x = x;
     a.x_scale = x_scale;
     a.x_broadcast = x_rows == MOE_X_SHARED;
@@ -240,8 +264,10 @@ hipError_t ffn_up_impl(const moe_shape &s, int n_groups, int zblocks, long est_r
 
 hipError_t ffn_down_impl(const moe_shape &s, int n_groups, int zblocks, long est_rows,
                          long cap_rows, const void *hm, const int32_t *offsets,
-                         int rows_per_group, const void *w_down, void *y, hipStream_t st) {
+                         int rows_per_group, const void *w_down, void *y, hipStream_t st,
+                         const Secondary &sec = Secondary()) {
     StreamArgs a{};
+    set_secondary(a, sec);
     a.x = hm;
     a.offsets = offsets;
     a.rows_per_group = rows_per_group;
@@ -452,9 +478,31 @@ MOE_EXPORT moe_status moe_combine(const moe_shape *shape, int32_t T, const void 
     return MOE_OK;
 }
 
+namespace {
+moe_status layer_forward_impl(const moe_shape *shape, const moe_weights *w,
+                              const moe_slot_map *map, int32_t T, const void *h, void *out,
+                              void *ws, size_t ws_bytes, const moe_profile *prof, void *stream);
+}
+
 MOE_EXPORT moe_status moe_layer_forward(const moe_shape *shape, const moe_weights *w,
                                         const moe_slot_map *map, int32_t T, const void *h,
                                         void *out, void *ws, size_t ws_bytes, void *stream) {
+    return layer_forward_impl(shape, w, map, T, h, out, ws, ws_bytes, nullptr, stream);
+}
+
+MOE_EXPORT moe_status moe_layer_forward_profiled(const moe_shape *shape, const moe_weights *w,
+                                                 const moe_slot_map *map, int32_t T,
+                                                 const void *h, void *out, void *ws,
+                                                 size_t ws_bytes, const moe_profile *prof,
+                                                 void *stream) {
+    if (!prof) return MOE_ERR_INVALID_ARG;
+    return layer_forward_impl(shape, w, map, T, h, out, ws, ws_bytes, prof, stream);
+}
+
+namespace {
+moe_status layer_forward_impl(const moe_shape *shape, const moe_weights *w,
+                              const moe_slot_map *map, int32_t T, const void *h, void *out,
+                              void *ws, size_t ws_bytes, const moe_profile *prof, void *stream) {
     TRY(check_shape(shape));
     TRY(check_T(T));
     if (!w || !map) return MOE_ERR_INVALID_ARG;
@@ -480,6 +528,14 @@ MOE_EXPORT moe_status moe_layer_forward(const moe_shape *shape, const moe_weight
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
     TRY(device_ok());
     hipStream_t st = (hipStream_t)stream;
+    auto mark = [&](int i) -> bool {
+        return !prof || !prof->events[i] ||
+               hipEventRecord((hipEvent_t)prof->events[i], st) == hipSuccess;
+    };
+#define MARK(i)                                  \
+    do {                                         \
+        if (!mark(i)) return MOE_ERR_LAUNCH;     \
+    } while (0)
 
     int32_t *topk_idx = at<int32_t *>(ws, L.topk_idx);
     float *topk_w = at<float *>(ws, L.topk_w);
@@ -489,8 +545,10 @@ MOE_EXPORT moe_status moe_layer_forward(const moe_shape *shape, const moe_weight
     float *x_scale = at<float *>(ws, L.x_scale);
     const int cap = T * s.top_k;
 
+    MARK(0);
     LAUNCH(route_impl(s, T, h, w->w_router, w->bias, topk_idx, topk_w, gate ? sgate : nullptr,
                       nullptr, at<float *>(ws, L.logits), st));
+    MARK(1);
     // fp8 rows are quantised copies; otherwise the gate/up GEMM gathers the
     // hidden rows through perm_src and dispatch writes indices only
     const bool copy_rows = s.dispatch == MOE_FP8_E4M3;
@@ -498,24 +556,54 @@ MOE_EXPORT moe_status moe_layer_forward(const moe_shape *shape, const moe_weight
     LAUNCH(dispatch_impl(s, T, h, topk_idx, *map, copy_rows ? at<void *>(ws, L.x_perm) : nullptr,
                          x_scale, at<int32_t *>(ws, L.counts), offsets, perm_src, inv_pos,
                          at<void *>(ws, L.disp), st));
+    MARK(2);
     const int z = ffn_zblocks(cap, s.n_slots);
     const long est = est_group_rows(s, cap);
-    LAUNCH(ffn_up_impl(s, s.n_slots, z, est, cap, copy_rows ? at<void *>(ws, L.x_perm) : h,
-                       s.dispatch, x_scale, copy_rows ? MOE_X_PERMUTED : MOE_X_GATHER, perm_src,
-                       offsets, 0, w->w_gate, w->w_up, at<void *>(ws, L.hm), st));
-    LAUNCH(ffn_down_impl(s, s.n_slots, z, est, cap, at<void *>(ws, L.hm), offsets, 0, w->w_down,
-                         at<void *>(ws, L.y), st));
-    void *shared_y = nullptr;
-    if (gate) {
-        shared_y = at<void *>(ws, L.shared_y);
-        const int zs = (T + 63) / 64 < 65535 ? (T + 63) / 64 : 65535;
-        const long cap_sh = (long)s.n_shared * T;
-        const long est_sh = est_group_rows(s, cap_sh);
-        LAUNCH(ffn_up_impl(s, s.n_shared, zs, est_sh, cap_sh, h, s.act, nullptr, MOE_X_SHARED,
-                           nullptr, nullptr, T, w->sh_gate, w->sh_up, at<void *>(ws, L.hm), st));
-        LAUNCH(ffn_down_impl(s, s.n_shared, zs, est_sh, cap_sh, at<void *>(ws, L.hm), nullptr, T,
-                             w->sh_down, shared_y, st));
+    void *hm = at<void *>(ws, L.hm), *y = at<void *>(ws, L.y);
+    const size_t isz = act_bytes(s);
+    void *shared_y = gate ? (void *)((char *)y + (size_t)cap * s.hidden * isz) : nullptr;
+    const void *x_routed = copy_rows ? at<void *>(ws, L.x_perm) : h;
+    const int x_mode = copy_rows ? MOE_X_PERMUTED : MOE_X_GATHER;
+    const long cap_sh = (long)s.n_shared * T;
+    const long est_sh = est_group_rows(s, cap_sh);
+    // The shared experts (every token, Step 5) ride in the routed launches as
+    // secondary groups when both stream their weights; rows cap.. of hm/y.
+    const bool merged = gate && !copy_rows && !use_tiled(est, s.hidden, s.act, s.act) &&
+                        !use_tiled(est_sh, s.hidden, s.act, s.act);
+    if (merged) {
+        Secondary up_sec, down_sec;
+        up_sec.n = down_sec.n = s.n_shared;
+        up_sec.x = h;
+        up_sec.x_broadcast = 1;
+        up_sec.w0 = w->sh_gate;
+        up_sec.w1 = w->sh_up;
+        down_sec.x = hm;
+        down_sec.w0 = w->sh_down;
+        up_sec.rows = down_sec.rows = T;
+        up_sec.row_base = down_sec.row_base = cap;
+        LAUNCH(ffn_up_impl(s, s.n_slots, z, est, cap, x_routed, s.dispatch, x_scale, x_mode,
+                           perm_src, offsets, 0, w->w_gate, w->w_up, hm, st, up_sec));
+        MARK(3);
+        LAUNCH(ffn_down_impl(s, s.n_slots, z, est, cap, hm, offsets, 0, w->w_down, y, st,
+                             down_sec));
+    } else {
+        LAUNCH(ffn_up_impl(s, s.n_slots, z, est, cap, x_routed, s.dispatch, x_scale, x_mode,
+                           perm_src, offsets, 0, w->w_gate, w->w_up, hm, st));
+        MARK(3);
+        LAUNCH(ffn_down_impl(s, s.n_slots, z, est, cap, hm, offsets, 0, w->w_down, y, st));
+        if (gate) {
+            const int zs = (T + 63) / 64 < 65535 ? (T + 63) / 64 : 65535;
+            void *hm_sh = (char *)hm + (size_t)cap * s.inter * isz;
+            LAUNCH(ffn_up_impl(s, s.n_shared, zs, est_sh, cap_sh, h, s.act, nullptr, MOE_X_SHARED,
+                               nullptr, nullptr, T, w->sh_gate, w->sh_up, hm_sh, st));
+            LAUNCH(ffn_down_impl(s, s.n_shared, zs, est_sh, cap_sh, hm_sh, nullptr, T,
+                                 w->sh_down, shared_y, st));
+        }
     }
+    MARK(4);
     LAUNCH(combine_impl(s, T, at<void *>(ws, L.y), inv_pos, topk_w, shared_y, sgate, out, st));
+    MARK(5);
+#undef MARK
     return MOE_OK;
 }
+}  // namespace

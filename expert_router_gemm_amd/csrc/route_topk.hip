@@ -20,7 +20,9 @@
 namespace moe {
 namespace {
 
-template <int EPL>
+// NS > 0: the number of K-slice partials, known at compile time (all loads
+// issued up front, no branches); NS == 0: any count, runtime loop.
+template <int EPL, int NS>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ parts, int nsplit,
                                                    size_t split_stride, int ld, int T, int E,
                                                    int K, int has_gate,
@@ -41,15 +43,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ par
         const int e = lane + 64 * j;
         float acc = -INFINITY;
         if (e < E) {
-            // issue every slice's load before summing (at most 16 slices)
-            float part[16];
+            if (NS > 0) {
+                float part[NS > 0 ? NS : 1];
 #pragma unroll
-            for (int zs = 0; zs < 16; ++zs)
-                part[zs] = zs < nsplit ? l[(size_t)zs * split_stride + e] : 0.0f;
-            acc = part[0];
+                for (int zs = 0; zs < NS; ++zs) part[zs] = l[(size_t)zs * split_stride + e];
+                acc = part[0];
 #pragma unroll
-            for (int zs = 1; zs < 16; ++zs)
-                if (zs < nsplit) acc += part[zs];
+                for (int zs = 1; zs < NS; ++zs) acc += part[zs];
+            } else {
+                acc = l[e];
+                for (int zs = 1; zs < nsplit; ++zs) acc += l[(size_t)zs * split_stride + e];
+            }
             if (bias) acc += bias[e];
         }
         v[j] = acc;
@@ -106,29 +110,48 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ par
     }
 }
 
+template <int EPL>
+hipError_t launch_e(dim3 grid, const float *logits, int nsplit, size_t split_stride, int ld,
+                    int T, int E, int K, int has_gate, const float *bias, int32_t *topk_idx,
+                    float *topk_w, float *shared_gate, float *logits_out, hipStream_t s) {
+#define MOE_TOPK(NS)                                                                          \
+    hipLaunchKernelGGL((topk_kernel<EPL, NS>), grid, dim3(256), 0, s, logits, nsplit,         \
+                       split_stride, ld, T, E, K, has_gate, bias, topk_idx, topk_w,            \
+                       shared_gate, logits_out)
+    switch (nsplit) {  // the splits the router picks for common hidden sizes
+    case 1: MOE_TOPK(1); break;
+    case 2: MOE_TOPK(2); break;
+    case 4: MOE_TOPK(4); break;
+    case 7: MOE_TOPK(7); break;
+    case 8: MOE_TOPK(8); break;
+    case 14: MOE_TOPK(14); break;
+    default: MOE_TOPK(0); break;
+    }
+#undef MOE_TOPK
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float *logits, int nsplit, size_t split_stride, int ld, int T,
                        int E, int K, int has_gate, const float *bias, int32_t *topk_idx,
                        float *topk_w, float *shared_gate, float *logits_out, hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    dim3 grid((T + 3) / 4), block(256);
+    dim3 grid((T + 3) / 4);
     if (E <= 64)
-        hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, nsplit, split_stride, ld, T,
-                           E, K, has_gate, bias, topk_idx, topk_w, shared_gate, logits_out);
-    else if (E <= 128)
-        hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, nsplit, split_stride, ld, T,
-                           E, K, has_gate, bias, topk_idx, topk_w, shared_gate, logits_out);
-    else if (E <= 256)
-        hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, nsplit, split_stride, ld, T,
-                           E, K, has_gate, bias, topk_idx, topk_w, shared_gate, logits_out);
-    else if (E <= 512)
-        hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, nsplit, split_stride, ld, T,
-                           E, K, has_gate, bias, topk_idx, topk_w, shared_gate, logits_out);
-    else
-        hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, nsplit, split_stride, ld, T,
-                           E, K, has_gate, bias, topk_idx, topk_w, shared_gate, logits_out);
-    return hipGetLastError();
+        return launch_e<1>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, bias,
+                           topk_idx, topk_w, shared_gate, logits_out, s);
+    if (E <= 128)
+        return launch_e<2>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, bias,
+                           topk_idx, topk_w, shared_gate, logits_out, s);
+    if (E <= 256)
+        return launch_e<4>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, bias,
+                           topk_idx, topk_w, shared_gate, logits_out, s);
+    if (E <= 512)
+        return launch_e<8>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, bias,
+                           topk_idx, topk_w, shared_gate, logits_out, s);
+    return launch_e<16>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, bias,
+                        topk_idx, topk_w, shared_gate, logits_out, s);
 }
 
 }  // namespace moe

@@ -195,6 +195,22 @@ moe_status moe_layer_forward(const moe_shape *shape, const moe_weights *weights,
                              const moe_slot_map *map, int32_t T, const void *h, void *out,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* Profiling variant of moe_layer_forward for benchmarks: the same kernels
+ * in the same order, and additionally records the caller's events
+ * (hipEvent_t created by the caller; NULL entries are skipped) on the
+ * stream at the stage boundaries: events[0] before Step 1, [1] after the
+ * router (Step 1), [2] after dispatch (Step 2), [3] after the gate/up GEMM,
+ * [4] after the down GEMM and the shared experts, [5] after combine
+ * (Steps 4-5).  An event record that fails returns MOE_ERR_LAUNCH. */
+typedef struct {
+    void *events[6];
+} moe_profile;
+
+moe_status moe_layer_forward_profiled(const moe_shape *shape, const moe_weights *weights,
+                                      const moe_slot_map *map, int32_t T, const void *h,
+                                      void *out, void *ws, size_t ws_bytes,
+                                      const moe_profile *prof, void *stream);
+
 /* (host) Workspace bytes that moe_layer_forward needs for T tokens; also
  * enough for moe_dispatch and moe_expert_ffn with cap_rows <= T*K (or
  * n_shared*T for the shared experts).  Returns 0 for an invalid shape. */

@@ -159,3 +159,12 @@ def test_drop_replica_matches_oracle_reading():
     off2, slot2 = moe.drop_replica(off, slot, 40, 0)
     assert off2[-1] == off[-1] - 1
     assert list(slot2[off2[40]:off2[41]]) == [32]
+
+
+def test_profiled_entry_requires_profile():
+    L = moe.lib()
+    s = _shape()
+    sm = moe.SlotMap(FAKE, FAKE, 0)
+    w = moe.Weights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)
+    assert L.moe_layer_forward_profiled(ctypes.byref(s), ctypes.byref(w), ctypes.byref(sm), 16,
+                                        FAKE, FAKE, FAKE, 1 << 40, None, None) == 1

@@ -359,3 +359,19 @@ def test_tiled_shared_and_ragged_groups():
     _check_combine(L, st)
     ref = gh.oracle_forward(L)
     gh.assert_close(st["out"], ref["out"], "layer output", rows=~tie)
+
+
+def test_profiled_entry_matches_and_records_stage_events():
+    import expert_router_gemm_amd as moe
+    cfg = small_cfg(3)
+    L = gh.build_layer(cfg)
+    ref = gh.gpu_forward(L).cpu().numpy()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    out = torch.empty((L.T, cfg.H), dtype=torch.float16, device=gh.DEV)
+    ws = gh.ws_for(L)
+    moe.moe_layer_forward_profiled(L.shape, L.wmap, L.smap, L.T, L.d["h"], out, ws,
+                                   moe.make_profile(ev))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint8), ref.view(np.uint8))
+    gaps = [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
+    assert all(g >= 0 for g in gaps) and sum(gaps) > 0
