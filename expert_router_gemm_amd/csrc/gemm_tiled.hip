@@ -41,7 +41,7 @@ __device__ __forceinline__ int swz(int r, int c) { return r * PITCH + ((c ^ (r &
 // (FN = WR/NM features), as 4 x (4/NM) x NM tiles of 16x16x32 MFMAs.
 template <int NM, int EPI, bool GATHER>
 __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs, int g, int mt,
-                                          int nt) {
+                                          int nt, int kz) {
     constexpr int FN = WR / NM;   // features per tile
     constexpr int NJ = 4 / NM;    // 16-feature subtiles per wave and matrix
     // wave-uniform by construction; readfirstlane keeps them (and the buffer
@@ -49,6 +49,7 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
     g = __builtin_amdgcn_readfirstlane(g);
     mt = __builtin_amdgcn_readfirstlane(mt);
     nt = __builtin_amdgcn_readfirstlane(nt);
+    kz = __builtin_amdgcn_readfirstlane(kz);
     int r0, r1;
     if (a.offsets) {
         r0 = a.offsets[g];
@@ -162,22 +163,24 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
         }
     };
 
-    // K / BK is even (K is a multiple of 128).  The loop body is branch-free
-    // so the compiler's wait counts stay exact (a prefetch past the end
-    // re-reads the last step and is never used).
-    const int nk = K / BK;
-    MOE_GLOAD(ra0, rb0, 0);
-    MOE_GLOAD(ra1, rb1, BK);
+    // This tile's K slice: steps [kz*nk, (kz+1)*nk), nk even (K is a
+    // multiple of 2*BK*ksplit).  The loop body is branch-free so the
+    // compiler's wait counts stay exact (a prefetch past the end re-reads the
+    // last step and is never used).
+    const int nk = K / BK / a.ksplit;
+    const int k0 = kz * nk * BK;
+    MOE_GLOAD(ra0, rb0, k0);
+    MOE_GLOAD(ra1, rb1, k0 + BK);
     MOE_LSTORE(ra0, rb0, 0);
     __syncthreads();
     for (int kt = 0; kt < nk; kt += 2) {
         // step kt: LDS buffer 0; refill set 0 with step kt+2; stage set 1 (kt+1)
-        MOE_GLOAD(ra0, rb0, (kt + 2 < nk ? kt + 2 : nk - 1) * BK);
+        MOE_GLOAD(ra0, rb0, k0 + (kt + 2 < nk ? kt + 2 : nk - 1) * BK);
         compute(0);
         MOE_LSTORE(ra1, rb1, 1);
         __syncthreads();
         // step kt+1: LDS buffer 1; refill set 1 with step kt+3; stage set 0 (kt+2)
-        MOE_GLOAD(ra1, rb1, (kt + 3 < nk ? kt + 3 : nk - 1) * BK);
+        MOE_GLOAD(ra1, rb1, k0 + (kt + 3 < nk ? kt + 3 : nk - 1) * BK);
         compute(1);
         MOE_LSTORE(ra0, rb0, 0);
         __syncthreads();
@@ -197,8 +200,9 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
             for (int j = 0; j < NJ; ++j) {
                 const int f = n0 + wn * (FN / 4) + j * 16 + lr;
                 if (f >= a.N) continue;
-                if (EPI == 2) {  // logits, fp32
-                    reinterpret_cast<float *>(a.out)[(size_t)r * a.out_ld + f] = acc[0][i][j][q];
+                if (EPI == 2) {  // logits, fp32 partial of K slice kz
+                    reinterpret_cast<float *>(a.out)[(size_t)kz * a.split_stride +
+                                                     (size_t)r * a.out_ld + f] = acc[0][i][j][q];
                 } else {
                     float v;
                     if (EPI == 1)
@@ -254,11 +258,12 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
     }
     if (tid == 0) tstart[n_groups] = carry;
     __syncthreads();
-    const int total = carry * n_ntiles;
+    const int total = carry * n_ntiles * a.ksplit;
 
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int tile = item / n_ntiles;
-        const int nt = item % n_ntiles;
+        const int kz = item % a.ksplit;
+        const int tile = item / a.ksplit / n_ntiles;
+        const int nt = (item / a.ksplit) % n_ntiles;
         // group holding this row tile: last g with tstart[g] <= tile
         int lo = 0, hi = n_groups - 1;
         while (lo < hi) {
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
         }
         const int g = lo;
         const int mt = tile - tstart[g];
-        tile_body<NM, EPI, GATHER>(a, As, Bs, g, mt, nt);
+        tile_body<NM, EPI, GATHER>(a, As, Bs, g, mt, nt, kz);
     }
 }
 
@@ -294,7 +299,7 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
         per_cu = 1;
     // every resident workgroup slot, never more than the items
     long grid = (long)cus * per_cu;
-    const long items = max_tiles * n_ntiles;
+    const long items = max_tiles * n_ntiles * a.ksplit;
     if (items < grid) grid = items > 0 ? items : 1;
     hipLaunchKernelGGL((tiled_gemm_kernel<NM, EPI, GATHER>), dim3((unsigned)grid), dim3(kThreads),
                        lds, s, a, n_ntiles, n_groups);
@@ -308,7 +313,8 @@ bool tiled_gemm_supported_shape(int K, int dtype, int x_dtype) {
 }
 
 bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype) {
-    return a.ksplit == 1 && a.n_sec == 0 && tiled_gemm_supported_shape(a.K, dtype, x_dtype);
+    return a.ksplit >= 1 && a.K % (2 * BK * a.ksplit) == 0 && a.n_sec == 0 &&
+           tiled_gemm_supported_shape(a.K, dtype, x_dtype);
 }
 
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,

@@ -26,20 +26,32 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline int act_bytes(const moe_shape &s) { return s.act == MOE_F32 ? 4 : 2; }
 inline int has_gate(const moe_shape &s) { return (s.flags & MOE_F_SHARED) ? 1 : 0; }
 
-// Router K split: the smallest split (K slice a multiple of 4 MFMA steps)
-// that gives at least 256 workgroups, else the largest one up to 16.
-int router_ksplit(const moe_shape &s, int T) {
+// Router plan.  Large batches (T >= 2048, fp16) use the LDS-tiled kernel
+// and small ones the weight-stream kernel; either way K is split (slices a
+// multiple of the kernel's K granularity) until there are at least 256
+// workgroups, at most 16 slices.  The top-K kernel sums the slices in order.
+struct RouterPlan {
+    bool tiled;
+    int ksplit;
+};
+
+RouterPlan router_plan(const moe_shape &s, int T) {
     const int N = s.n_experts + has_gate(s);
-    const long base = (long)((N + 63) / 64) * ((T + 63) / 64);
-    const int gran = 4 * (s.act == MOE_F32 ? 16 : 32);
-    int best = 1;
+    RouterPlan p;
+    p.tiled = T >= 2048 && tiled_gemm_supported_shape(s.hidden, s.act, s.act);
+    const long base = p.tiled ? (long)((N + 255) / 256) * ((T + 127) / 128)
+                              : (long)((N + 63) / 64) * ((T + 63) / 64);
+    const int gran = p.tiled ? 128 : 4 * (s.act == MOE_F32 ? 16 : 32);
+    p.ksplit = 1;
     for (int d = 1; d <= 16; ++d) {
         if (s.hidden % (d * gran)) continue;
-        best = d;
+        p.ksplit = d;
         if (base * d >= 256) break;
     }
-    return best;
+    return p;
 }
+
+int router_ksplit(const moe_shape &s, int T) { return router_plan(s, T).ksplit; }
 
 size_t route_ws_bytes(const moe_shape &s, int T) {
     return up256((size_t)router_ksplit(s, T) * T * (s.n_experts + has_gate(s)) * 4);
@@ -133,7 +145,6 @@ inline P at(void *ws, size_t off) {
 // Groups expected to hold at least this many rows run on the LDS-tiled
 // kernel (weight tiles reused across rows); fewer rows stream the weights.
 constexpr int kTiledMinRows = 64;
-constexpr int kTiledRouterMinTokens = 2048;
 
 bool use_tiled(long est_rows, int K, int dtype, int x_dtype) {
     return est_rows >= kTiledMinRows && tiled_gemm_supported_shape(K, dtype, x_dtype);
@@ -174,10 +185,11 @@ hipError_t route_impl(const moe_shape &s, int T, const void *h, const void *w_ro
     a.out_ld = N;
     a.N = N;
     a.K = s.hidden;
-    a.ksplit = router_ksplit(s, T);
+    const RouterPlan plan = router_plan(s, T);
+    a.ksplit = plan.ksplit;
     a.split_stride = (size_t)T * N;
     hipError_t e;
-    if (a.ksplit == 1 && T >= kTiledRouterMinTokens && tiled_gemm_supported(a, s.act, s.act)) {
+    if (plan.tiled) {
         e = launch_tiled_gemm(a, STREAM_LOGITS, 1, (T + 127) / 128, st);
     } else {
         const int rb = (T + 63) / 64;

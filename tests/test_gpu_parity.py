@@ -330,8 +330,8 @@ def test_full_size_sampled(n):
 
 
 def test_prefill_tiled_path_small():
-    """T = 4096 rank share: the router (T >= 2048, no K split) and the routed
-    FFN (>= 64 expected rows per group) take the LDS-tiled kernel."""
+    """T = 4096 rank share: the router (T >= 2048, K split in 2 slices) and
+    the routed FFN (>= 64 expected rows per group) take the LDS-tiled kernel."""
     cfg = moe_synth.scaled_config(4, T=4096, H=256, I=128, seed=31)
     L = gh.build_layer(cfg)
     st = gh.gpu_stages(L)
@@ -359,6 +359,19 @@ def test_tiled_shared_and_ragged_groups():
     _check_combine(L, st)
     ref = gh.oracle_forward(L)
     gh.assert_close(st["out"], ref["out"], "layer output", rows=~tie)
+
+
+@pytest.mark.parametrize("H", [1536, 7168])
+def test_tiled_router_k_split_with_shared_gate(H):
+    """Router on the tiled kernel with the shared-gate column (N = E + 1, a
+    ragged feature tile) and a ragged token tail (T = 2100): H = 1536 splits
+    K in 12 slices of 2 K steps, H = 7168 in 14 slices of 8; routing is
+    checked token by token."""
+    cfg = moe_synth.scaled_config(1, T=2100, H=H, I=128, dtype="f16", seed=33)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    tie = _check_routing(L, st)
+    print(f"[tiled router] H={H} near_ties={int(tie.sum())}")
 
 
 def test_profiled_entry_matches_and_records_stage_events():
