@@ -250,13 +250,17 @@ def cpu_baseline(ctx, budget_s: float = 20.0):
 
 
 def is_swiglu_stream(kernel_name: str) -> bool:
-    """The gate/up launch of the stream GEMM: template arguments NM = 2,
-    EPI = SwiGLU (1), in demangled or mangled form."""
+    """The gate/up launch of the stream GEMM: template arguments
+    <TW, XM, NSUB, EPI, KW, U> with EPI = SwiGLU (1), demangled or mangled."""
     import re
     if DOMINANT not in kernel_name:
         return False
     n = kernel_name.replace(" ", "")
-    return bool(re.search(r"stream_gemm_kernel<[^,]+,\d+,2,1,", n) or re.search(r"Li2ELi1ELi\d+E", n))
+    m = re.search(r"stream_gemm_kernel<[^,]+,(\d+),(\d+),(\d+),", n)
+    if m:
+        return m.group(3) == "1"
+    m = re.search(r"stream_gemm_kernelI(?:DF16_|f)Li(\d+)ELi(\d+)ELi(\d+)E", n)
+    return bool(m) and m.group(3) == "1"
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int):

@@ -10,19 +10,20 @@
 // Section 2.3 notes FP8 halves the dispatched bytes: with x_dtype = FP8 each
 // row is stored as E4M3 codes with one fp32 scale.
 //
-// Decode-sized batches (T <= 1024 tokens, S <= 256 slots) run steps 1-2 and
-// the index half of step 3 in a single 1024-thread block, then the row copy.
-// Larger batches use three kernels.  All deterministic (no order-dependent
-// atomics):
+// Decode-sized batches (T <= 1024 tokens, S <= 256 slots) run steps 1-3's
+// index work in a single 1024-thread block.  Larger batches use three
+// kernels.  All deterministic (no order-dependent atomics):
 //  1. rank:    one wave per 64-token chunk.  Each (token, k) sets its lane bit
 //              in a per-slot 64-bit LDS mask (an OR, so arrival order cannot
 //              matter); the pair's rank inside the chunk is the popcount of
 //              the mask bits of lower lanes, the chunk's count the popcount.
 //  2. scan:    per slot, exclusive scan over chunks; then an exclusive scan
 //              over slots gives offsets.  chunk_counts becomes chunk_base.
-//  3. scatter: one wave per pair: row = chunk_base + rank; writes inv_pos,
-//              perm_src and copies (or quantises) the 14 KB hidden row with
-//              16-byte lane accesses.
+//  3. index:   one thread per pair: row = chunk_base + rank -> inv_pos,
+//              perm_src.
+// When the rows are materialised (x_perm given: fp8 codes, or a caller that
+// wants the permuted copy) one wave per token then reads its hidden row once
+// and writes it, or its E4M3 codes and scale, to each of its local rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -76,49 +77,84 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchArgs a) {
         for (int s = lane; s < a.S; s += 64) a.chunk_counts[(size_t)chunk * a.S + s] = __popcll(m[s]);
 }
 
-// Single block of 1024 threads; S <= 1024.
+// Single block of 1024 threads; S <= 1024.  P = 1024 / SP threads serve
+// each slot (SP = S rounded up to a power of two), thread j of a slot owning
+// a contiguous run of chunks:
+//  1. per thread: sum of its chunks' counts; exclusive scan over the slot's
+//     threads (segmented Hillis-Steele in LDS) and the slot total;
+//  2. exclusive scan of the slot totals over slots -> counts, offsets;
+//  3. per thread: chunk_counts of its chunks become absolute row bases
+//     (slot offset + rows of the slot's earlier chunks).
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(DispatchArgs a) {
     __shared__ int buf[2][1024];
+    __shared__ int slot_tot[1024];
     const int C = (a.T + 63) / 64;
-    const int s = threadIdx.x;
-    // 1. per slot: exclusive scan over chunks (in place) and the slot total
-    int tot = 0;
-    if (s < a.S) {
-        int c = 0;
-        for (; c + 8 <= C; c += 8) {
-            int v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = a.chunk_counts[(size_t)(c + u) * a.S + s];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                a.chunk_counts[(size_t)(c + u) * a.S + s] = tot;
-                tot += v[u];
-            }
-        }
-        for (; c < C; ++c) {
-            const int v = a.chunk_counts[(size_t)c * a.S + s];
-            a.chunk_counts[(size_t)c * a.S + s] = tot;
-            tot += v;
-        }
-        a.counts[s] = tot;
+    int SP = 1;
+    while (SP < a.S) SP <<= 1;
+    const int P = 1024 / SP;
+    const int tid = threadIdx.x;
+    const int s = tid / P, j = tid % P;
+    const bool live = s < a.S;
+    const int cpt = (C + P - 1) / P;
+    const int c0 = min(C, j * cpt), c1 = min(C, c0 + cpt);
+    int sum = 0;
+    if (live) {
+#pragma unroll 8
+        for (int c = c0; c < c1; ++c) sum += a.chunk_counts[(size_t)c * a.S + s];
     }
-    // 2. exclusive scan of the totals over slots (Hillis-Steele in LDS)
+    // 1. inclusive scan of the per-thread sums within each slot's P threads
     int cur = 0;
-    buf[0][s] = tot;
+    buf[0][tid] = sum;
     __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-        const int v = buf[cur][s] + (s >= o ? buf[cur][s - o] : 0);
-        buf[cur ^ 1][s] = v;
+    for (int o = 1; o < P; o <<= 1) {
+        const int v = buf[cur][tid] + (j >= o ? buf[cur][tid - o] : 0);
+        buf[cur ^ 1][tid] = v;
         cur ^= 1;
         __syncthreads();
     }
-    const int incl = buf[cur][s];
-    if (s < a.S) {
-        const int off = incl - tot;
-        a.offsets[s] = off;
-        for (int c = 0; c < C; ++c) a.chunk_counts[(size_t)c * a.S + s] += off;
-        if (s == a.S - 1) a.offsets[a.S] = incl;
+    const int excl_j = buf[cur][tid] - sum;
+    if (j == P - 1) slot_tot[s] = buf[cur][tid];
+    __syncthreads();
+    // 2. exclusive scan of the slot totals (entries past S are 0)
+    int cs = 0;
+    if (tid < SP) buf[0][tid] = slot_tot[tid];
+    __syncthreads();
+    for (int o = 1; o < SP; o <<= 1) {
+        if (tid < SP) buf[cs ^ 1][tid] = buf[cs][tid] + (tid >= o ? buf[cs][tid - o] : 0);
+        cs ^= 1;
+        __syncthreads();
     }
+    if (tid < a.S) {
+        const int inc = buf[cs][tid], tot = slot_tot[tid];
+        a.counts[tid] = tot;
+        a.offsets[tid] = inc - tot;
+        if (tid == a.S - 1) a.offsets[a.S] = inc;
+    }
+    // 3. absolute row base of every chunk of this thread
+    if (live) {
+        int run = buf[cs][s] - slot_tot[s] + excl_j;
+#pragma unroll 8
+        for (int c = c0; c < c1; ++c) {
+            const int v = a.chunk_counts[(size_t)c * a.S + s];
+            a.chunk_counts[(size_t)c * a.S + s] = run;
+            run += v;
+        }
+    }
+}
+
+// Index outputs of the large-batch path, one thread per (token, k) pair.
+__global__ __launch_bounds__(256) void dispatch_index_kernel(DispatchArgs a) {
+    const size_t p = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= (size_t)a.T * a.K) return;
+    const int code = a.pair_code[p];
+    if (code < 0) {
+        a.inv_pos[p] = -1;
+        return;
+    }
+    const int t = (int)(p / a.K);
+    const int row = a.chunk_counts[(size_t)(t >> 6) * a.S + (code >> 6)] + (code & 63);
+    a.inv_pos[p] = row;
+    a.perm_src[row] = (int32_t)p;
 }
 
 // Decode-sized batches (T <= 1024, S <= 256): rank, scan and the index
@@ -141,7 +177,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
     __shared__ int rslot[kSmallNnz];
     const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
     const int C = (a.T + 63) / 64;
-    for (int i = tid; i < (kSmallT / 64) * kSmallS; i += 1024) (&masks[0][0])[i] = 0ull;
+    for (int i = tid; i < C * kSmallS; i += 1024) (&masks[0][0])[i] = 0ull;  // chunks in use
     for (int i = tid; i <= a.E; i += 1024) roff[i] = a.rep_off[i];
     const int nnz = a.rep_off[a.E];
     const bool table_in_lds = nnz >= 0 && nnz <= kSmallNnz;
@@ -150,6 +186,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
     __syncthreads();
     const int t = tid;
     const unsigned long long bit = 1ull << lane;
+    int sls[KMAX];  // this thread's slots, kept for the final pass
     if (t < a.T) {
         int ex[KMAX];
 #pragma unroll
@@ -170,7 +207,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
                     if (sl < 0 || sl >= a.S) sl = -1;
                 }
             }
-            a.pair_code[(size_t)t * K + k] = sl;
+            sls[k] = sl;
             if (sl >= 0) atomicOr(&masks[wave][sl], bit);
         }
     }
@@ -208,7 +245,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
         for (int k = 0; k < KMAX; ++k) {
             if (k >= K) break;
             const size_t p = (size_t)t * K + k;
-            const int sl = a.pair_code[p];  // written by this thread above
+            const int sl = sls[k];
             if (sl < 0) {
                 a.inv_pos[p] = -1;
                 continue;
@@ -235,31 +272,16 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
     return sign | (q - ((127u - 7u) << 3));
 }
 
-// FROM_INV: rows were already placed (small path): read them from inv_pos.
-template <typename T, int XM, bool FROM_INV>
+// Row copy for rows placed already (inv_pos written), one wave per pair:
+// the fallback for rows longer than dispatch_rows_kernel holds.
+template <typename T, int XM>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(DispatchArgs a) {
     const size_t p = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (p >= (size_t)a.T * a.K) return;
     const int lane = lane_id();
     const int t = (int)(p / a.K);
-    int row;
-    if (FROM_INV) {
-        row = __builtin_amdgcn_readfirstlane(a.inv_pos[p]);
-        if (row < 0) return;
-    } else {
-        const int code = __builtin_amdgcn_readfirstlane(a.pair_code[p]);
-        if (code < 0) {
-            if (lane == 0) a.inv_pos[p] = -1;
-            return;
-        }
-        const int s = code >> 6, rank = code & 63;
-        row = __builtin_amdgcn_readfirstlane(a.chunk_counts[(size_t)(t >> 6) * a.S + s] + rank);
-        if (lane == 0) {
-            a.inv_pos[p] = row;
-            a.perm_src[row] = (int32_t)p;
-        }
-    }
-    if (!a.x_perm) return;  // indices only: the GEMM gathers the rows itself
+    const int row = __builtin_amdgcn_readfirstlane(a.inv_pos[p]);
+    if (row < 0) return;
     constexpr int EL = Frag<T>::kElems;
     const T *src = reinterpret_cast<const T *>(a.h) + (size_t)t * a.H;
     if (XM != DT_FP8) {
@@ -298,6 +320,81 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(DispatchArgs a) {
     }
 }
 
+// One wave per token: the token's hidden row is read once into registers
+// (every load issued before the first use) and written -- copied, or
+// quantised once to E4M3 codes with one scale -- to each local row the token
+// was dispatched to.  Tokens with no local pair read nothing.
+// H <= 64 * EL * kRowChunks.
+constexpr int kRowChunks = 16;
+
+template <typename T, int XM>
+__global__ __launch_bounds__(256) void dispatch_rows_kernel(DispatchArgs a) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.T) return;
+    const int lane = lane_id();
+    const int myrow = lane < a.K ? a.inv_pos[(size_t)t * a.K + lane] : -1;
+    uint64_t todo = __ballot(myrow >= 0);
+    if (!todo) return;
+    constexpr int EL = Frag<T>::kElems;
+    typedef typename Frag<T>::vec V;
+    const T *src = reinterpret_cast<const T *>(a.h) + (size_t)t * a.H;
+    V v[kRowChunks];
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i) {
+        const int c = (i * 64 + lane) * EL;
+        if (c < a.H) v[i] = load16(src + c);
+    }
+    if (XM != DT_FP8) {
+        while (todo) {
+            const int k = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const int row = __builtin_amdgcn_readlane(myrow, k);
+            T *dst = reinterpret_cast<T *>(a.x_perm) + (size_t)row * a.H;
+#pragma unroll
+            for (int i = 0; i < kRowChunks; ++i) {
+                const int c = (i * 64 + lane) * EL;
+                if (c < a.H) *reinterpret_cast<V *>(dst + c) = v[i];
+            }
+        }
+        return;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i)
+        if ((i * 64 + lane) * EL < a.H)
+#pragma unroll
+            for (int j = 0; j < EL; ++j) amax = fmaxf(amax, fabsf((float)v[i][j]));
+    amax = wave_max(amax);
+    // amax == 0: all codes and the scale are 0
+    const float inv = amax == 0.0f ? 0.0f : __fdiv_rn(448.0f, amax);
+    const float scale = amax == 0.0f ? 0.0f : __fdiv_rn(amax, 448.0f);
+    u32x2 codes[kRowChunks];
+#pragma unroll
+    for (int i = 0; i < kRowChunks; ++i) {
+        uint32_t w[2] = {0u, 0u};
+        if (amax != 0.0f)
+#pragma unroll
+            for (int j = 0; j < EL; ++j) {
+                float q = __fmul_rn((float)v[i][j], inv);
+                q = fminf(fmaxf(q, -448.0f), 448.0f);
+                w[j >> 2] |= e4m3_rne(q) << (8 * (j & 3));
+            }
+        codes[i] = u32x2{w[0], w[1]};
+    }
+    while (todo) {
+        const int k = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int row = __builtin_amdgcn_readlane(myrow, k);
+        uint8_t *dst = reinterpret_cast<uint8_t *>(a.x_perm) + (size_t)row * a.H;
+#pragma unroll
+        for (int i = 0; i < kRowChunks; ++i) {
+            const int c = (i * 64 + lane) * EL;
+            if (c < a.H) *reinterpret_cast<u32x2 *>(dst + c) = codes[i];
+        }
+        if (lane == 0) a.x_scale[row] = scale;
+    }
+}
+
 }  // namespace
 
 size_t dispatch_scratch_bytes(int T, int K, int S) {
@@ -307,16 +404,27 @@ size_t dispatch_scratch_bytes(int T, int K, int S) {
     return a;
 }
 
-template <bool FROM_INV>
-hipError_t launch_scatter(const DispatchArgs &a, hipStream_t s) {
+// Row copies once inv_pos is written (x_perm != NULL).
+hipError_t launch_rows(const DispatchArgs &a, hipStream_t s) {
+    const int EL = a.dtype == DT_F32 ? 4 : 8;
+    if (a.H <= 64 * EL * kRowChunks) {
+        dim3 grid((unsigned)((a.T + 3) / 4));
+        if (a.dtype == DT_F32)
+            hipLaunchKernelGGL((dispatch_rows_kernel<float, DT_F32>), grid, dim3(256), 0, s, a);
+        else if (a.x_dtype == DT_FP8)
+            hipLaunchKernelGGL((dispatch_rows_kernel<f16, DT_FP8>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((dispatch_rows_kernel<f16, DT_F16>), grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     const size_t pairs = (size_t)a.T * a.K;
     dim3 grid((unsigned)((pairs + 3) / 4));
     if (a.dtype == DT_F32)
-        hipLaunchKernelGGL((dispatch_scatter_kernel<float, DT_F32, FROM_INV>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((dispatch_scatter_kernel<float, DT_F32>), grid, dim3(256), 0, s, a);
     else if (a.x_dtype == DT_FP8)
-        hipLaunchKernelGGL((dispatch_scatter_kernel<f16, DT_FP8, FROM_INV>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((dispatch_scatter_kernel<f16, DT_FP8>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((dispatch_scatter_kernel<f16, DT_F16, FROM_INV>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((dispatch_scatter_kernel<f16, DT_F16>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -334,7 +442,7 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (!a.x_perm) return hipSuccess;  // rows are gathered by the GEMM instead
-        return launch_scatter<true>(a, s);
+        return launch_rows(a, s);
     }
     if (C > 0) {
         hipLaunchKernelGGL(dispatch_rank_kernel, dim3((C + 3) / 4), dim3(256),
@@ -347,7 +455,12 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.T == 0) return hipSuccess;
-    return launch_scatter<false>(a, s);
+    const size_t pairs = (size_t)a.T * a.K;
+    hipLaunchKernelGGL(dispatch_index_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
+                       s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || !a.x_perm) return e;
+    return launch_rows(a, s);
 }
 
 }  // namespace moe

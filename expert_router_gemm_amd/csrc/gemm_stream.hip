@@ -10,16 +10,23 @@
 //   out[r][n] = epilogue( sum_k W[g][n][k] * x[r][k] )   for rows r of group g
 //
 // Work decomposition
-//   blockIdx.x  4 waves x (16 features, or 16*NM for the plain GEMM)
+//   blockIdx.x  a block of features: 4 waves x 16*NSUB features each (KW = 1;
+//               the router), or 16*NSUB = 64 features shared by the 4 waves
+//               (KW = 4; SwiGLU reads a gate and an up tile per 16-feature
+//               subtile)
 //   blockIdx.y  group g (expert slot)
 //   blockIdx.z  (first row block) * ksplit + K slice; row blocks of 64 rows
 //               are strided by gridDim.z / ksplit.  ksplit > 1 (router only)
 //               writes one fp32 partial per K slice; the top-K kernel sums
 //               them in slice order, so the result stays deterministic.
-// Each wave owns its features and runs the whole K loop for them, so no
-// cross-wave reduction is needed.  The 64 rows of a row block are processed
-// in MT = 1, 2 or 4 tiles of 16, chosen from the rows actually present, so
-// one pass over the weights serves every row of a decode-sized group.
+// KW = 4 (the expert FFN): wave w of a block runs quarter w of K for all 64
+// features, so each activation fragment it loads feeds 4 (down) or 8
+// (gate/up) MFMAs, while a block still covers only 64 features (fine-grained
+// blocks keep the tail of an uneven grid short).  The 4 partial tiles meet
+// in LDS and are summed in K order (deterministic); wave w then applies the
+// epilogue to subtile w.  The 64 rows of a row block are processed in MT =
+// 1, 2 or 4 tiles of 16, chosen from the rows actually present, so one pass
+// over the weights serves every row of a decode-sized group.
 //
 // MFMA mapping (v_mfma_f32_16x16x32_f16, or 4x v_mfma_f32_16x16x4_f32 for
 // fp32): A = 16 weight rows (features), B = x^T (16 rows = tokens).  Lane l
@@ -50,11 +57,38 @@
 #define MOE_STREAM_NT 0
 #endif
 //   MOE_STREAM_STORE_WIDE_ROWS  expected rows per group from which the plain
-//       (down projection) GEMM gives each wave two 16-feature subtiles that
-//       share every activation fragment (one subtile below: measured faster
-//       at ~8 rows per group, two at ~16-50)
+//       (down projection) GEMM takes the wide shape below (measured faster
+//       from ~8 rows per group; one subtile per wave for fewer rows)
+//   MOE_STREAM_STORE_NSUB_WIDE, MOE_STREAM_STORE_U_WIDE  subtiles per wave
+//       and K chunks per buffer of that wide shape
+//   MOE_STREAM_SWIGLU_NSUB  16-feature subtiles per wave of the SwiGLU GEMM
+//   MOE_STREAM_SWIGLU_U     its K chunks per register buffer
+//   MOE_STREAM_U_MT2        K chunks per buffer for 17-32 rows per pass
+//   MOE_STREAM_SWIGLU_KW, MOE_STREAM_STORE_KW  4: the waves of a block split
+//       K and share 4 subtiles (NSUB must be 4); 1: each wave its own
 #ifndef MOE_STREAM_STORE_WIDE_ROWS
-#define MOE_STREAM_STORE_WIDE_ROWS 12
+#define MOE_STREAM_STORE_WIDE_ROWS 6
+#endif
+#ifndef MOE_STREAM_STORE_NSUB_WIDE
+#define MOE_STREAM_STORE_NSUB_WIDE 4
+#endif
+#ifndef MOE_STREAM_STORE_U_WIDE
+#define MOE_STREAM_STORE_U_WIDE 4
+#endif
+#ifndef MOE_STREAM_SWIGLU_KW
+#define MOE_STREAM_SWIGLU_KW 4
+#endif
+#ifndef MOE_STREAM_STORE_KW
+#define MOE_STREAM_STORE_KW 4
+#endif
+#ifndef MOE_STREAM_SWIGLU_NSUB
+#define MOE_STREAM_SWIGLU_NSUB 4
+#endif
+#ifndef MOE_STREAM_SWIGLU_U
+#define MOE_STREAM_SWIGLU_U 2
+#endif
+#ifndef MOE_STREAM_U_MT2
+#define MOE_STREAM_U_MT2 MOE_STREAM_U
 #endif
 #if MOE_STREAM_MAX_WAVES > 0
 #define MOE_STREAM_OCC __attribute__((amdgpu_waves_per_eu(1, MOE_STREAM_MAX_WAVES)))
@@ -96,9 +130,19 @@ __device__ __forceinline__ typename Frag<T>::vec wload16(const T *p) {
 #endif
 }
 
-template <typename TW, int XM, int NM, int EPI, int MT, int U>
+// NSUB 16-feature subtiles per wave; NM = weight tiles per K chunk (SwiGLU:
+// gate subtiles 0..NSUB-1, then the up subtiles; otherwise NM = NSUB).
+// KW == 1: the wave runs K slice kz of ksplit and finishes its features.
+// KW == 4: the block's 4 waves share the same NSUB = 4 subtiles, wave w
+// runs quarter w of K; the partials meet in LDS (red) and are summed in K
+// order, then wave w finishes subtile w.  Every activation fragment then
+// serves 4x as many weight rows while a block still streams 64 features.
+template <typename TW, int XM, int NSUB, int EPI, int KW, int MT, int U>
 __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, int rstart,
-                                            int r0, int r1, int kz) {
+                                            int r0, int r1, int kz, f32x4 *red) {
+    constexpr bool SW = EPI == EPI_SWIGLU;
+    constexpr int NM = SW ? 2 * NSUB : NSUB;
+    static_assert(KW == 1 || (KW == 4 && NSUB == 4 && EPI != EPI_LOGITS), "K split shape");
     typedef typename Frag<TW>::vec V;
     typedef XFrag<TW, XM> XF;
     typedef typename XF::raw XR;
@@ -107,21 +151,22 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
     const int lane = lane_id();
     const int lr = lane & 15, lg = lane >> 4;
     const int K = a.K;
-    const int KS = K / a.ksplit;  // this block's K slice: [kz*KS, (kz+1)*KS)
+    const int wk = KW > 1 ? (int)(threadIdx.x >> 6) : 0;
+    const int KS = K / (a.ksplit * KW);  // this wave's K slice: [ksl*KS, (ksl+1)*KS)
+    const int ksl = kz * KW + wk;
     const int NC = KS / CK;
 
-    // weight rows (clamped: rows past N are read but never stored).  SwiGLU:
-    // subtile m is matrix m (gate, up) at rows f0..f0+15; otherwise subtile m
-    // is rows f0 + 16m .. +15 of the one matrix.
-    constexpr bool SAME = EPI != EPI_SWIGLU;
+    // weight rows (clamped: rows past N are read but never stored).  Tile m
+    // covers rows f0 + 16 * (m % NSUB) .. +15 of the gate matrix (w0) for
+    // m < NSUB and of the up matrix (w1) above (SwiGLU).
     const TW *wp[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-        int wrow = f0 + (SAME ? 16 * m : 0) + lr;
+        int wrow = f0 + 16 * (m % NSUB) + lr;
         if (wrow > a.N - 1) wrow = a.N - 1;
-        const size_t off = (size_t)g * a.w_group_stride + (size_t)wrow * K + (size_t)kz * KS +
+        const size_t off = (size_t)g * a.w_group_stride + (size_t)wrow * K + (size_t)ksl * KS +
                            (size_t)lg * EL;
-        wp[m] = reinterpret_cast<const TW *>(SAME || m == 0 ? a.w0 : a.w1) + off;
+        wp[m] = reinterpret_cast<const TW *>(m < NSUB ? a.w0 : a.w1) + off;
     }
     // token rows (clamped to the group's last row; extra columns are dropped)
     size_t xo[MT];
@@ -132,7 +177,7 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
         rows[t] = r;
         int rc = r < r1 ? r : r1 - 1;
         int xr = a.gather ? a.gather[rc] / a.gather_div : (a.x_broadcast ? rc - r0 : rc);
-        xo[t] = (size_t)xr * K + (size_t)kz * KS + (size_t)lg * EL;
+        xo[t] = (size_t)xr * K + (size_t)ksl * KS + (size_t)lg * EL;
     }
 
     f32x4 acc[NM][MT];
@@ -178,6 +223,43 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
 #undef MOE_LOAD
 #undef MOE_COMPUTE
 
+    if (KW > 1) {
+        // partials of the 4 K quarters -> wave wk finishes subtile wk
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) red[(wk * NM + m) * 64 + lane] = acc[m][t];
+            __syncthreads();
+            f32x4 s0 = red[wk * 64 + lane];
+            f32x4 s1 = SW ? red[(NSUB + wk) * 64 + lane] : s0;
+#pragma unroll
+            for (int v = 1; v < KW; ++v) {
+                s0 += red[(v * NM + wk) * 64 + lane];
+                if (SW) s1 += red[(v * NM + NSUB + wk) * 64 + lane];
+            }
+            __syncthreads();
+            const int r = rows[t];
+            if (r < r1) {
+                float sc = 1.0f;
+                if (XM == DT_FP8) sc = a.x_scale[r] * 256.0f;  // undo the 2^-8 of the decode
+                const int fb = f0 + 16 * wk + 4 * lg;
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = SW ? siluf_(s0[j] * sc) * (s1[j] * sc) : s0[j] * sc;
+                TW *o = reinterpret_cast<TW *>(a.out) + (size_t)r * a.out_ld + fb;
+                if (fb < a.N) {
+                    if (sizeof(TW) == 2) {
+                        f16x4 h4 = {to_f16(v[0]), to_f16(v[1]), to_f16(v[2]), to_f16(v[3])};
+                        *reinterpret_cast<f16x4 *>(o) = h4;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
+                    }
+                }
+            }
+        }
+        return;
+    }
+
     // epilogue: lane holds features f0 (+16m) + 4*lg + j (j = 0..3) of token rows[t]
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -185,9 +267,8 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
         if (r >= r1) continue;
         float sc = 1.0f;
         if (XM == DT_FP8) sc = a.x_scale[r] * 256.0f;  // undo the 2^-8 of the decode
-        constexpr int NOUT = SAME ? NM : 1;  // 16-feature output blocks per wave
 #pragma unroll
-        for (int m = 0; m < NOUT; ++m) {
+        for (int m = 0; m < NSUB; ++m) {  // 16-feature output blocks
             const int fb = f0 + 16 * m + 4 * lg;
             if (EPI == EPI_LOGITS) {
                 float *o = reinterpret_cast<float *>(a.out) + (size_t)kz * a.split_stride +
@@ -202,8 +283,8 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
                 float v[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    if (EPI == EPI_SWIGLU) {
-                        const float ga = acc[0][t][j] * sc, ub = acc[NM - 1][t][j] * sc;
+                    if (SW) {
+                        const float ga = acc[m][t][j] * sc, ub = acc[NSUB + m][t][j] * sc;
                         v[j] = siluf_(ga) * ub;
                     } else {
                         v[j] = acc[m][t][j] * sc;
@@ -221,15 +302,14 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
     }
 }
 
-template <int NM, int EPI>
-constexpr int features_per_wave() { return EPI == EPI_SWIGLU ? 16 : 16 * NM; }
-
-template <typename TW, int XM, int NM, int EPI, int U>
+template <typename TW, int XM, int NSUB, int EPI, int KW, int U>
 __global__ __launch_bounds__(256) MOE_STREAM_OCC void stream_gemm_kernel(StreamArgs a) {
-    constexpr int FPW = features_per_wave<NM, EPI>();
+    constexpr int FPW = 16 * NSUB;  // features per wave
+    constexpr int NM = EPI == EPI_SWIGLU ? 2 * NSUB : NSUB;
+    __shared__ f32x4 red[KW > 1 ? KW * NM * 64 : 1];
     const int wave = threadIdx.x >> 6;
-    const int f0 = blockIdx.x * (4 * FPW) + wave * FPW;
-    if (f0 >= a.N) return;
+    const int f0 = KW > 1 ? blockIdx.x * FPW : blockIdx.x * (4 * FPW) + wave * FPW;
+    if (f0 >= a.N) return;  // block-uniform when KW > 1
     const int kz = blockIdx.z % a.ksplit;  // K slice
     const int zr = blockIdx.z / a.ksplit;  // first row block
     const int zn = gridDim.z / a.ksplit;   // row-block stride
@@ -256,26 +336,28 @@ __global__ __launch_bounds__(256) MOE_STREAM_OCC void stream_gemm_kernel(StreamA
     for (int rb = zr; r0 + rb * 64 < r1; rb += zn) {
         const int rs = r0 + rb * 64;
         const int n = r1 - rs;
+        constexpr int U2 = U > MOE_STREAM_U_MT2 ? MOE_STREAM_U_MT2 : U;
+        constexpr int U4 = KW > 1 ? 1 : (U > 2 ? 2 : U);
         if (n <= 16)
-            stream_pass<TW, XM, NM, EPI, 1, U>(b, g, f0, rs, r0, r1, kz);
+            stream_pass<TW, XM, NSUB, EPI, KW, 1, U>(b, g, f0, rs, r0, r1, kz, red);
         else if (n <= 32)
-            stream_pass<TW, XM, NM, EPI, 2, U>(b, g, f0, rs, r0, r1, kz);
+            stream_pass<TW, XM, NSUB, EPI, KW, 2, U2>(b, g, f0, rs, r0, r1, kz, red);
         else
-            stream_pass<TW, XM, NM, EPI, 4, (U > 2 ? 2 : U)>(b, g, f0, rs, r0, r1, kz);
+            stream_pass<TW, XM, NSUB, EPI, KW, 4, U4>(b, g, f0, rs, r0, r1, kz, red);
     }
 }
 
-template <typename TW, int XM, int NM, int EPI>
+template <typename TW, int XM, int NSUB, int EPI, int U = MOE_STREAM_U, int KW = 1>
 hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t s) {
-    constexpr int FPB = 4 * features_per_wave<NM, EPI>();  // features per block
+    constexpr int FPB = (KW > 1 ? 1 : 4) * 16 * NSUB;  // features per block
     dim3 grid((a.N + FPB - 1) / FPB, n_groups + a.n_sec, zblocks * a.ksplit);
     constexpr int CK = 4 * Frag<TW>::kElems;
-    const int NC = a.K / a.ksplit / CK;
-    if (a.ksplit < 1 || a.K % (a.ksplit * 4 * CK) != 0) return hipErrorInvalidValue;
-    if (NC % (2 * MOE_STREAM_U) == 0)
-        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NM, EPI, MOE_STREAM_U>), grid, dim3(256), 0, s, a);
+    const int NC = a.K / (a.ksplit * KW) / CK;
+    if (a.ksplit < 1 || a.K % (a.ksplit * KW * 4 * CK) != 0) return hipErrorInvalidValue;
+    if (NC % (2 * U) == 0)
+        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NSUB, EPI, KW, U>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NM, EPI, 2>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NSUB, EPI, KW, 2>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -286,18 +368,28 @@ hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int m
     if (n_groups + a.n_sec <= 0 || zblocks <= 0) return hipSuccess;
     if (n_groups + a.n_sec > 65535) return hipErrorInvalidValue;
     if (dtype == DT_F16) {
+        // the K-split shapes need K to hold 4 quarters of 4 chunks of 32
+        const bool kw_ok = a.K % (a.ksplit * 4 * 4 * 32) == 0;
         if (mode == STREAM_SWIGLU) {
-            if (x_dtype == DT_FP8) return launch_t<f16, DT_FP8, 2, EPI_SWIGLU>(a, n_groups, zblocks, s);
-            return launch_t<f16, DT_F16, 2, EPI_SWIGLU>(a, n_groups, zblocks, s);
+            constexpr int NS = MOE_STREAM_SWIGLU_NSUB, U = MOE_STREAM_SWIGLU_U;
+            constexpr int KW = MOE_STREAM_SWIGLU_KW;
+            if (x_dtype == DT_FP8)
+                return kw_ok ? launch_t<f16, DT_FP8, NS, EPI_SWIGLU, U, KW>(a, n_groups, zblocks, s)
+                             : launch_t<f16, DT_FP8, 1, EPI_SWIGLU>(a, n_groups, zblocks, s);
+            return kw_ok ? launch_t<f16, DT_F16, NS, EPI_SWIGLU, U, KW>(a, n_groups, zblocks, s)
+                         : launch_t<f16, DT_F16, 1, EPI_SWIGLU>(a, n_groups, zblocks, s);
         }
         if (mode == STREAM_STORE) {
             if (est_rows >= MOE_STREAM_STORE_WIDE_ROWS)
-                return launch_t<f16, DT_F16, 2, EPI_STORE>(a, n_groups, zblocks, s);
+                return kw_ok ? launch_t<f16, DT_F16, MOE_STREAM_STORE_NSUB_WIDE, EPI_STORE,
+                                        MOE_STREAM_STORE_U_WIDE, MOE_STREAM_STORE_KW>(
+                                   a, n_groups, zblocks, s)
+                             : launch_t<f16, DT_F16, 2, EPI_STORE>(a, n_groups, zblocks, s);
             return launch_t<f16, DT_F16, 1, EPI_STORE>(a, n_groups, zblocks, s);
         }
         return launch_t<f16, DT_F16, 1, EPI_LOGITS>(a, n_groups, zblocks, s);
     }
-    if (mode == STREAM_SWIGLU) return launch_t<float, DT_F32, 2, EPI_SWIGLU>(a, n_groups, zblocks, s);
+    if (mode == STREAM_SWIGLU) return launch_t<float, DT_F32, 1, EPI_SWIGLU>(a, n_groups, zblocks, s);
     if (mode == STREAM_STORE) return launch_t<float, DT_F32, 1, EPI_STORE>(a, n_groups, zblocks, s);
     return launch_t<float, DT_F32, 1, EPI_LOGITS>(a, n_groups, zblocks, s);
 }

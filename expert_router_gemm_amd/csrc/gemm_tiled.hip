@@ -167,8 +167,8 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
     // multiple of 2*BK*ksplit).  The loop body is branch-free so the
     // compiler's wait counts stay exact (a prefetch past the end re-reads the
     // last step and is never used).
-    const int nk = K / BK / a.ksplit;
-    const int k0 = kz * nk * BK;
+    const int nk = EPI == 2 ? K / BK / a.ksplit : K / BK;
+    const int k0 = EPI == 2 ? kz * nk * BK : 0;
     MOE_GLOAD(ra0, rb0, k0);
     MOE_GLOAD(ra1, rb1, k0 + BK);
     MOE_LSTORE(ra0, rb0, 0);
@@ -258,12 +258,13 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
     }
     if (tid == 0) tstart[n_groups] = carry;
     __syncthreads();
-    const int total = carry * n_ntiles * a.ksplit;
+    const int ks = EPI == 2 ? a.ksplit : 1;  // K slices (logits only)
+    const int total = carry * n_ntiles * ks;
 
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int kz = item % a.ksplit;
-        const int tile = item / a.ksplit / n_ntiles;
-        const int nt = (item / a.ksplit) % n_ntiles;
+        const int kz = EPI == 2 ? item % ks : 0;
+        const int tile = item / ks / n_ntiles;
+        const int nt = (item / ks) % n_ntiles;
         // group holding this row tile: last g with tstart[g] <= tile
         int lo = 0, hi = n_groups - 1;
         while (lo < hi) {
@@ -299,7 +300,7 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
         per_cu = 1;
     // every resident workgroup slot, never more than the items
     long grid = (long)cus * per_cu;
-    const long items = max_tiles * n_ntiles * a.ksplit;
+    const long items = max_tiles * n_ntiles * (EPI == 2 ? a.ksplit : 1);
     if (items < grid) grid = items > 0 ? items : 1;
     hipLaunchKernelGGL((tiled_gemm_kernel<NM, EPI, GATHER>), dim3((unsigned)grid), dim3(kThreads),
                        lds, s, a, n_ntiles, n_groups);

@@ -26,6 +26,11 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline int act_bytes(const moe_shape &s) { return s.act == MOE_F32 ? 4 : 2; }
 inline int has_gate(const moe_shape &s) { return (s.flags & MOE_F_SHARED) ? 1 : 0; }
 
+// Largest router K split (compile-time tuning knob).
+#ifndef MOE_ROUTER_MAX_SPLIT
+#define MOE_ROUTER_MAX_SPLIT 16
+#endif
+
 // Router plan.  Large batches (T >= 2048, fp16) use the LDS-tiled kernel
 // and small ones the weight-stream kernel; either way K is split (slices a
 // multiple of the kernel's K granularity) until there are at least 256
@@ -43,7 +48,7 @@ RouterPlan router_plan(const moe_shape &s, int T) {
                               : (long)((N + 63) / 64) * ((T + 63) / 64);
     const int gran = p.tiled ? 128 : 4 * (s.act == MOE_F32 ? 16 : 32);
     p.ksplit = 1;
-    for (int d = 1; d <= 16; ++d) {
+    for (int d = 1; d <= MOE_ROUTER_MAX_SPLIT; ++d) {
         if (s.hidden % (d * gran)) continue;
         p.ksplit = d;
         if (base * d >= 256) break;

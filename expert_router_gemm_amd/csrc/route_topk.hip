@@ -8,10 +8,13 @@
 // shared gate is sigmoid(h . w_sg), whose logit the router GEMM writes as an
 // extra column after the E expert columns.
 //
-// One wave per token.  Lane l holds logits e = l + 64*j (coalesced loads);
-// each of the K rounds finds the wave-wide best (larger logit, then smaller
-// id) with a butterfly of shuffles, so every lane agrees on the winner and
-// the owning lane retires it.
+// One wave per token.  Lane l holds logits e = l + 64*j (coalesced loads).
+// Each of the K selection rounds is one wave-wide maximum of a 64-bit key
+// (order-preserving bits of the logit above the complement of the id, so a
+// larger logit wins and equal logits go to the smaller id), reduced with DPP
+// row shifts and row broadcasts into lane 63 and read back as a scalar; the
+// owning lane retires the winner.  Lane k keeps the k-th selection, so the
+// K indices and gates leave in one coalesced store each.
 #include <math.h>
 
 #include "common.h"
@@ -19,6 +22,40 @@
 
 namespace moe {
 namespace {
+
+// One DPP step of a wave-wide maximum: this lane's key against the key of
+// the lane CTRL names (lanes with no source, or masked off, keep their own).
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ void dpp_max_step(uint32_t &hi, uint32_t &lo) {
+    const uint32_t oh = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, BANK_MASK, false);
+    const uint32_t ol = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, BANK_MASK, false);
+    const bool gt = oh > hi || (oh == hi && ol > lo);
+    hi = gt ? oh : hi;
+    lo = gt ? ol : lo;
+}
+
+// Wave-wide maximum of the 64-bit key (hi, lo), returned in every lane:
+// row_shr 1, 2, 4, 8 leave each 16-lane row's maximum in its lane 15,
+// row_bcast 15 and 31 carry it across rows into lane 63.
+__device__ __forceinline__ void wave_max_key(uint32_t &hi, uint32_t &lo) {
+    dpp_max_step<0x111, 0xf, 0xf>(hi, lo);  // row_shr:1
+    dpp_max_step<0x112, 0xf, 0xf>(hi, lo);  // row_shr:2
+    dpp_max_step<0x114, 0xf, 0xf>(hi, lo);  // row_shr:4
+    dpp_max_step<0x118, 0xf, 0xf>(hi, lo);  // row_shr:8
+    dpp_max_step<0x142, 0xa, 0xf>(hi, lo);  // row_bcast:15 into rows 1, 3
+    dpp_max_step<0x143, 0xc, 0xf>(hi, lo);  // row_bcast:31 into rows 2, 3
+    hi = __builtin_amdgcn_readlane(hi, 63);
+    lo = __builtin_amdgcn_readlane(lo, 63);
+}
+
+// Order-preserving map of a finite float to uint32 (-0 and +0 map alike).
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+    const uint32_t b = v == 0.0f ? 0u : __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
 
 // NS > 0: the number of K-slice partials, known at compile time (all loads
 // issued up front, no branches); NS == 0: any count, runtime loop.
@@ -66,42 +103,41 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ par
         }
     }
 
-    float m = -INFINITY;
+    // K rounds; round 0 yields the maximum logit m.  Keys of absent experts
+    // and of experts already taken are 0, below every finite logit's key.
+    uint32_t taken = 0;
+    int my_id = 0;
+    float my_v = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        uint32_t hi = 0, lo = 0;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) m = fmaxf(m, v[j]);
-    m = wave_max(m);
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + 64 * j;
+            if (e < E && !((taken >> j) & 1u)) {
+                const uint32_t h = ordered_bits(v[j]), l = ~(uint32_t)e;
+                if (h > hi || (h == hi && l > lo)) {
+                    hi = h;
+                    lo = l;
+                }
+            }
+        }
+        wave_max_key(hi, lo);
+        const int bi = (int)~lo;
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (lane == k) {
+            my_id = bi;
+            my_v = from_ordered_bits(hi);
+        }
+    }
+    const float m = __shfl(my_v, 0, kWave);
     float z = 0.0f;
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
         if (lane + 64 * j < E) z += expf(v[j] - m);
     z = wave_sum(z);
-
-    uint32_t taken = 0;
-    for (int k = 0; k < K; ++k) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int e = lane + 64 * j;
-            if (e < E && !((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < bi))) {
-                bv = v[j];
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, kWave);
-            const int oi = __shfl_xor(bi, o, kWave);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        if (lane == 0) {
-            topk_idx[(size_t)t * K + k] = bi;
-            topk_w[(size_t)t * K + k] = expf(bv - m) / z;
-        }
+    if (lane < K) {
+        topk_idx[(size_t)t * K + lane] = my_id;
+        topk_w[(size_t)t * K + lane] = expf(my_v - m) / z;
     }
     if (has_gate && shared_gate && lane == 0) {
         float zg = l[E];
