@@ -22,8 +22,8 @@
 //  3. index:   one thread per pair: row = chunk_base + rank -> inv_pos,
 //              perm_src.
 // When the rows are materialised (x_perm given: fp8 codes, or a caller that
-// wants the permuted copy) one wave per token then reads its hidden row once
-// and writes it, or its E4M3 codes and scale, to each of its local rows.
+// wants the permuted copy) one block per token then reads its hidden row
+// once and writes it, or its E4M3 codes and scale, to each of its local rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -320,28 +320,29 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(DispatchArgs a) {
     }
 }
 
-// One wave per token: the token's hidden row is read once into registers
-// (every load issued before the first use) and written -- copied, or
-// quantised once to E4M3 codes with one scale -- to each local row the token
-// was dispatched to.  Tokens with no local pair read nothing.
-// H <= 64 * EL * kRowChunks.
-constexpr int kRowChunks = 16;
+// One block of 256 threads per token: the token's hidden row is read once
+// into registers (every load issued before the first use) and written --
+// copied, or quantised once to E4M3 codes with one scale -- to each local
+// row the token was dispatched to.  Tokens with no local pair read nothing.
+// H <= 256 * EL * kRowSteps.
+constexpr int kRowSteps = 4;
 
 template <typename T, int XM>
 __global__ __launch_bounds__(256) void dispatch_rows_kernel(DispatchArgs a) {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= a.T) return;
-    const int lane = lane_id();
+    __shared__ float wmax[4];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    // every wave reads the token's K row indices: the same ballot in all 4
     const int myrow = lane < a.K ? a.inv_pos[(size_t)t * a.K + lane] : -1;
     uint64_t todo = __ballot(myrow >= 0);
-    if (!todo) return;
+    if (!todo) return;  // block-uniform
     constexpr int EL = Frag<T>::kElems;
     typedef typename Frag<T>::vec V;
     const T *src = reinterpret_cast<const T *>(a.h) + (size_t)t * a.H;
-    V v[kRowChunks];
+    V v[kRowSteps];
 #pragma unroll
-    for (int i = 0; i < kRowChunks; ++i) {
-        const int c = (i * 64 + lane) * EL;
+    for (int i = 0; i < kRowSteps; ++i) {
+        const int c = (i * 256 + tid) * EL;
         if (c < a.H) v[i] = load16(src + c);
     }
     if (XM != DT_FP8) {
@@ -351,8 +352,8 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(DispatchArgs a) {
             const int row = __builtin_amdgcn_readlane(myrow, k);
             T *dst = reinterpret_cast<T *>(a.x_perm) + (size_t)row * a.H;
 #pragma unroll
-            for (int i = 0; i < kRowChunks; ++i) {
-                const int c = (i * 64 + lane) * EL;
+            for (int i = 0; i < kRowSteps; ++i) {
+                const int c = (i * 256 + tid) * EL;
                 if (c < a.H) *reinterpret_cast<V *>(dst + c) = v[i];
             }
         }
@@ -360,19 +361,22 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(DispatchArgs a) {
     }
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kRowChunks; ++i)
-        if ((i * 64 + lane) * EL < a.H)
+    for (int i = 0; i < kRowSteps; ++i)
+        if ((i * 256 + tid) * EL < a.H)
 #pragma unroll
             for (int j = 0; j < EL; ++j) amax = fmaxf(amax, fabsf((float)v[i][j]));
     amax = wave_max(amax);
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     // amax == 0: all codes and the scale are 0
     const float inv = amax == 0.0f ? 0.0f : __fdiv_rn(448.0f, amax);
     const float scale = amax == 0.0f ? 0.0f : __fdiv_rn(amax, 448.0f);
-    u32x2 codes[kRowChunks];
+    u32x2 codes[kRowSteps];
 #pragma unroll
-    for (int i = 0; i < kRowChunks; ++i) {
+    for (int i = 0; i < kRowSteps; ++i) {
         uint32_t w[2] = {0u, 0u};
-        if (amax != 0.0f)
+        if (amax != 0.0f && (i * 256 + tid) * EL < a.H)
 #pragma unroll
             for (int j = 0; j < EL; ++j) {
                 float q = __fmul_rn((float)v[i][j], inv);
@@ -387,11 +391,11 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(DispatchArgs a) {
         const int row = __builtin_amdgcn_readlane(myrow, k);
         uint8_t *dst = reinterpret_cast<uint8_t *>(a.x_perm) + (size_t)row * a.H;
 #pragma unroll
-        for (int i = 0; i < kRowChunks; ++i) {
-            const int c = (i * 64 + lane) * EL;
+        for (int i = 0; i < kRowSteps; ++i) {
+            const int c = (i * 256 + tid) * EL;
             if (c < a.H) *reinterpret_cast<u32x2 *>(dst + c) = codes[i];
         }
-        if (lane == 0) a.x_scale[row] = scale;
+        if (tid == 0) a.x_scale[row] = scale;
     }
 }
 
@@ -407,8 +411,8 @@ size_t dispatch_scratch_bytes(int T, int K, int S) {
 // Row copies once inv_pos is written (x_perm != NULL).
 hipError_t launch_rows(const DispatchArgs &a, hipStream_t s) {
     const int EL = a.dtype == DT_F32 ? 4 : 8;
-    if (a.H <= 64 * EL * kRowChunks) {
-        dim3 grid((unsigned)((a.T + 3) / 4));
+    if (a.H <= 256 * EL * kRowSteps) {
+        dim3 grid((unsigned)a.T);
         if (a.dtype == DT_F32)
             hipLaunchKernelGGL((dispatch_rows_kernel<float, DT_F32>), grid, dim3(256), 0, s, a);
         else if (a.x_dtype == DT_FP8)

@@ -34,7 +34,8 @@ inline int has_gate(const moe_shape &s) { return (s.flags & MOE_F_SHARED) ? 1 : 
 // Router plan.  Large batches (T >= 2048, fp16) use the LDS-tiled kernel
 // and small ones the weight-stream kernel; either way K is split (slices a
 // multiple of the kernel's K granularity) until there are at least 256
-// workgroups, at most 16 slices.  The top-K kernel sums the slices in order.
+// workgroups, at most MOE_ROUTER_MAX_SPLIT slices.  The top-K kernel sums
+// the slices in order.
 struct RouterPlan {
     bool tiled;
     int ksplit;
