@@ -115,8 +115,25 @@ void oref_router_logits(int T, int H, int E, int dtype, const void *h,
  * the K selected probabilities are used as they are (not renormalised);
  * selection orders experts by logit, larger first, and the lower id wins a
  * tie.  topk_idx[t][0..K-1] lists the winners in that order. */
+/* Group-limited top-K: the large-EP outlook of the expert-parallelism blog
+ * page (section 八) routes to groups of experts first, then to experts
+ * inside the chosen groups.  Reading taken: G contiguous groups of E/G
+ * experts (the contiguous placement of section 2.1, so a group is one EP
+ * rank); a group's score is its largest logit; the M groups with the
+ * largest scores are kept (ties: lower group id); the K experts are then
+ * picked among the kept groups' experts exactly as above; gates stay the
+ * softmax over all E logits.  G == 0 means no group limit. */
+void oref_softmax_topk_grouped(int T, int E, int K, int G, int M, const float *logits,
+                               int32_t *topk_idx, float *topk_w);
+
 void oref_softmax_topk(int T, int E, int K, const float *logits,
                        int32_t *topk_idx, float *topk_w)
+{
+    oref_softmax_topk_grouped(T, E, K, 0, 0, logits, topk_idx, topk_w);
+}
+
+void oref_softmax_topk_grouped(int T, int E, int K, int G, int M, const float *logits,
+                               int32_t *topk_idx, float *topk_w)
 {
     double *p = (double *)malloc(sizeof(double) * (size_t)E);
     char *taken = (char *)malloc((size_t)E);
@@ -134,6 +151,33 @@ void oref_softmax_topk(int T, int E, int K, const float *logits,
         for (int e = 0; e < E; ++e)
             p[e] /= z;
         memset(taken, 0, (size_t)E);
+        if (G > 0) {
+            /* pick M groups by their best logit; experts of the other
+             * groups are marked taken so the expert rounds skip them */
+            const int gs = E / G;
+            char *gsel = (char *)calloc((size_t)G, 1);
+            for (int r = 0; r < M; ++r) {
+                int bg = -1;
+                float bs = 0.0f;
+                for (int g = 0; g < G; ++g) {
+                    if (gsel[g])
+                        continue;
+                    float sc = l[g * gs];
+                    for (int e = g * gs + 1; e < (g + 1) * gs; ++e)
+                        if (l[e] > sc)
+                            sc = l[e];
+                    if (bg < 0 || sc > bs) { /* strict '>': lower group id on ties */
+                        bg = g;
+                        bs = sc;
+                    }
+                }
+                gsel[bg] = 1;
+            }
+            for (int e = 0; e < E; ++e)
+                if (!gsel[e / gs])
+                    taken[e] = 1;
+            free(gsel);
+        }
         for (int k = 0; k < K; ++k) {
             int best = -1;
             for (int e = 0; e < E; ++e) {
@@ -393,6 +437,7 @@ void oref_combine(int T, int K, int H, int n_shared, const float *y,
 
 typedef struct {
     int32_t T, H, I, E, K, S, n_shared, dtype, fp8_dispatch;
+    int32_t n_groups, topk_groups; /* group-limited routing (0: none) */
 } oref_dims;
 
 /* One MoE layer forward for T tokens.
@@ -424,7 +469,7 @@ int oref_layer_forward(const oref_dims *d, const void *h, const int32_t *tok_ids
     int rc = 0;
 
     oref_router_logits(T, H, E, d->dtype, h, w_router, bias, logits);
-    oref_softmax_topk(T, E, K, logits, idx, w);
+    oref_softmax_topk_grouped(T, E, K, d->n_groups, d->topk_groups, logits, idx, w);
     oref_slot_map(T, K, idx, tok_ids, rep_off, rep_slot, seed, slot);
 
     for (size_t j = 0; j < (size_t)T * H; ++j)

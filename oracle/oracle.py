@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Pins (tests/test_oracle_pins.py) per function:
   router_logits   fp64 recomputation error bound; duplicate rows tie; bias
-  softmax_topk    lexsort brute force; shift invariance; sum of all probs = 1
+  softmax_topk    lexsort brute force; shift invariance; sum of all probs = 1;
+                  group-limited: hand-worked cases, brute force over kept
+                  groups + masked plain top-K, M = G reduces to plain
   shared_gate     w_sg = 0 gives exactly 0.5; closed form on tiny inputs
   slot_map        the blog page's worked example (section 2.2, Step 1);
                   replica choice against a Python SplitMix64 from the paper
@@ -67,7 +69,8 @@ def lib():
 
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("T", "H", "I", "E", "K", "S", "n_shared", "dtype", "fp8_dispatch")]
+                ("T", "H", "I", "E", "K", "S", "n_shared", "dtype", "fp8_dispatch",
+                 "n_groups", "topk_groups")]
 
 
 _p = ctypes.c_void_p
@@ -80,6 +83,7 @@ def _declare(L):
     L.oref_f16_to_double.restype = ctypes.c_double
     L.oref_router_logits.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p]
     L.oref_softmax_topk.argtypes = [_i, _i, _i, _p, _p, _p]
+    L.oref_softmax_topk_grouped.argtypes = [_i, _i, _i, _i, _i, _p, _p, _p]
     L.oref_shared_gate.argtypes = [_i, _i, _i, _p, _p, _p]
     L.oref_splitmix64.argtypes = [_u64]
     L.oref_splitmix64.restype = _u64
@@ -132,13 +136,19 @@ def router_logits(h: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
     return out
 
 
-def softmax_topk(logits: np.ndarray, K: int):
-    """Softmax over all experts, top-K by (logit desc, id asc)."""
+def softmax_topk(logits: np.ndarray, K: int, groups=None):
+    """Softmax over all experts, top-K by (logit desc, id asc).  groups =
+    (G, M): group-limited routing (M of G contiguous groups, by their best
+    logit), see oref_softmax_topk_grouped."""
     logits = _c(logits, np.float32)
     T, E = logits.shape
     idx = np.empty((T, K), np.int32)
     w = np.empty((T, K), np.float32)
-    lib().oref_softmax_topk(T, E, K, _ptr(logits), _ptr(idx), _ptr(w))
+    if groups:
+        G, M = groups
+        lib().oref_softmax_topk_grouped(T, E, K, G, M, _ptr(logits), _ptr(idx), _ptr(w))
+    else:
+        lib().oref_softmax_topk(T, E, K, _ptr(logits), _ptr(idx), _ptr(w))
     return idx, w
 
 
@@ -277,12 +287,13 @@ def gpu_of_expert(e: int, E: int = 256, ep_size: int = 8) -> int:
 def layer_forward(*, h: np.ndarray, w_router: np.ndarray, bias, w_sg,
                   slot_weights: Sequence, shared: Optional[Sequence],
                   rep_off, rep_slot, seed: int, K: int, fp8_dispatch: bool,
-                  tok_ids=None, I: Optional[int] = None):
+                  tok_ids=None, I: Optional[int] = None, groups=None):
     """Whole-layer oracle (Steps 1-5) for the tokens in ``h``.
 
     slot_weights: list over local slots of (gate [I,H], up [I,H], down [H,I])
     tuples or None (weights not supplied; an error if a pair lands there).
     shared: (gate [n,I,H], up [n,I,H], down [n,H,I]) or None.
+    groups: (G, M) for group-limited routing, or None.
     Returns dict(out, topk_idx, topk_w, slot, logits, shared_gate).
     """
     h = _c(h)
@@ -299,7 +310,8 @@ def layer_forward(*, h: np.ndarray, w_router: np.ndarray, bias, w_sg,
             I = shared[0].shape[1]
     I = int(I or 0)
     n_sh = 0 if shared is None else int(shared[0].shape[0])
-    d = Dims(T, H, I, E, K, S, n_sh, dt, 1 if fp8_dispatch else 0)
+    G, M = groups if groups else (0, 0)
+    d = Dims(T, H, I, E, K, S, n_sh, dt, 1 if fp8_dispatch else 0, G, M)
     keep = []
 
     def arr(ptrs):

@@ -41,6 +41,9 @@ MUTANTS = {
     "splitmix_shift": ("z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;",
                        "z = (z ^ (z >> 28)) * 0x94D049BB133111EBull;"),
     "f16_exponent_bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
+    "group_tie_to_higher_id": ("if (bg < 0 || sc > bs)", "if (bg < 0 || sc >= bs)"),
+    "group_score_first_expert": ("                            sc = l[e];", "                            sc = sc;"),
+    "group_mask_wrong_group": ("if (!gsel[e / gs])", "if (!gsel[e % G])"),
     "combine_skips_last_k": ("            for (int k = 0; k < K; ++k) {\n                int r = inv_pos",
                              "            for (int k = 0; k < K - 1; ++k) {\n                int r = inv_pos"),
 }

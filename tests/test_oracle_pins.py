@@ -204,6 +204,54 @@ def test_topk_matches_lexsort_and_softmax_closed_forms():
     assert np.allclose(w4[0], (idx4[0] + 1) / (E * (E + 1) / 2), rtol=1e-6)
 
 
+def test_group_limited_topk_worked_cases():
+    """Group-limited routing (expert-parallelism blog page, section 八: route
+    to expert groups first, then to experts): hand-worked cases."""
+    # E = 8 in G = 4 groups {0,1} {2,3} {4,5} {6,7}; group scores (best logit)
+    # 5, 4, 9, 1 -> keep groups 2 and 0 (M = 2); top-3 among {0,1,4,5}.
+    lg = np.array([[5, 0, 4, 4, 9, -1, 1, 1]], np.float32)
+    idx, w = oracle.softmax_topk(lg, 3, groups=(4, 2))
+    assert idx.tolist() == [[4, 0, 1]]
+    assert oracle.softmax_topk(lg, 3)[0].tolist() == [[4, 0, 2]]  # without the limit
+    # the gates stay the softmax over all 8 logits
+    p = np.exp(lg[0].astype(np.float64) - 9.0)
+    p /= p.sum()
+    assert np.allclose(w[0], p[[4, 0, 1]], rtol=1e-6, atol=0)
+    # a group's score is its best logit, not its first
+    lg = np.array([[1, 0, 0, 8, 2, 2, 0, 0]], np.float32)
+    assert oracle.softmax_topk(lg, 2, groups=(4, 1))[0].tolist() == [[3, 2]]
+    # groups 0 and 2 tie on their best logit: the lower group id is kept
+    lg = np.array([[3, 1, 0, 0, 3, 2, 0, 0]], np.float32)
+    assert oracle.softmax_topk(lg, 2, groups=(4, 1))[0].tolist() == [[0, 1]]
+
+
+def test_group_limited_topk_against_brute_force():
+    """Random logits with ties: the kept groups are the top-M of the group
+    maxima (ties to the lower group), the experts are the plain top-K of
+    the logits with every other group masked out, at most M groups are
+    used, and M = G is the plain top-K."""
+    rng = np.random.default_rng(11)
+    T, E, G, M, K = 400, 64, 8, 3, 6
+    gs = E // G
+    lg = (rng.integers(-20, 20, (T, E)) / 4.0).astype(np.float32)  # many exact ties
+    idx, w = oracle.softmax_topk(lg, K, groups=(G, M))
+    i0, w0 = oracle.softmax_topk(lg, K)
+    iG, wG = oracle.softmax_topk(lg, K, groups=(G, G))
+    assert np.array_equal(iG, i0) and np.array_equal(wG, w0)
+    for t in range(T):
+        score = lg[t].reshape(G, gs).max(1)
+        keep = sorted(range(G), key=lambda g: (-float(score[g]), g))[:M]
+        masked = np.full(E, -np.inf, np.float32)
+        for g in keep:
+            masked[g * gs:(g + 1) * gs] = lg[t, g * gs:(g + 1) * gs]
+        order = np.lexsort((np.arange(E), -masked.astype(np.float64)))[:K]
+        assert np.array_equal(idx[t], order), t
+        assert len(set((idx[t] // gs).tolist())) <= M
+    from scipy.special import softmax
+    p = softmax(lg.astype(np.float64), axis=1)
+    assert np.allclose(w, np.take_along_axis(p, idx, 1), rtol=1e-6, atol=0)
+
+
 def test_shared_gate_closed_forms():
     h = np.ones((3, 8), np.float32)
     assert np.all(oracle.shared_gate(h, np.zeros(8, np.float32)) == np.float32(0.5))
