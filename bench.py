@@ -57,7 +57,7 @@ def log(msg):
 # ------------------------------------------------------------------ setup
 
 
-def setup(n: int, keep_host: bool = True):
+def setup(n: int, keep_host: bool = True, groups=None):
     import numpy as np
     import torch
 
@@ -65,6 +65,8 @@ def setup(n: int, keep_host: bool = True):
     import moe_synth
 
     cfg = moe_synth.config(n)
+    if groups:
+        cfg = moe_synth.config(n, n_groups=groups[0], topk_groups=groups[1])
     dev = "cuda:0"
     rep = moe_synth.replica_expert(cfg)
     rep_off, rep_slot, slot_experts = moe.build_slot_map(cfg.E, cfg.ep_size, cfg.ep_rank,
@@ -97,7 +99,8 @@ def setup(n: int, keep_host: bool = True):
     shape = moe.make_shape(hidden=cfg.H, inter=cfg.I, n_experts=cfg.E, top_k=cfg.K, n_slots=S,
                            n_shared=cfg.n_shared,
                            act=moe.MOE_F32 if cfg.dtype == "f32" else moe.MOE_F16,
-                           dispatch=moe.MOE_FP8_E4M3 if fp8 else None, shared=cfg.n_shared > 0)
+                           dispatch=moe.MOE_FP8_E4M3 if fp8 else None, shared=cfg.n_shared > 0,
+                           n_groups=cfg.n_groups, topk_groups=cfg.topk_groups)
     T, K = cfg.T, cfg.K
     bufs = dict(
         ws=torch.empty(moe.moe_workspace_bytes(shape, T), dtype=torch.uint8, device=dev),
@@ -237,7 +240,7 @@ def cpu_baseline(ctx, budget_s: float = 20.0):
                              bias=ctx["bias"], w_sg=ctx["wr"][cfg.E] if cfg.n_shared else None,
                              slot_weights=sw, shared=ctx["shared"], rep_off=ro, rep_slot=rs,
                              seed=cfg.seed, K=cfg.K, fp8_dispatch=cfg.dispatch == "fp8",
-                             tok_ids=tok)
+                             tok_ids=tok, groups=cfg.groups)
         t_used += time.perf_counter() - t0
         done += n
         n *= 2
@@ -324,7 +327,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (PMC scale)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--groups", metavar="G,M", default=None,
+                    help="group-limited routing: keep M of G contiguous expert groups")
     args = ap.parse_args()
+    groups = tuple(int(v) for v in args.groups.split(",")) if args.groups else None
 
     if args.summarize_pmc:
         import moe_synth
@@ -341,7 +347,7 @@ def main():
         return 1
     import expert_router_gemm_amd as moe
     moe.lib()
-    ctx = setup(args.workload)
+    ctx = setup(args.workload, groups=groups)
     cfg = ctx["cfg"]
 
     for _ in range(args.warmup):
@@ -441,11 +447,15 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "inter": cfg.I,
                    "experts": cfg.E, "top_k": cfg.K, "local_slots": ctx["S"],
                    "shared_experts": cfg.n_shared, "dispatch": cfg.dispatch,
-                   "ep_size": cfg.ep_size, "ep_rank": cfg.ep_rank},
+                   "ep_size": cfg.ep_size, "ep_rank": cfg.ep_rank,
+                   "group_limit": list(groups) if groups else None},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer": {"entry": "moe_layer_forward_profiled", "hbm_gbs": round(layer_gbs, 1),
                   "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                  "mfma_tflops": round(work["layer_flops"] / (ms_per_step / 1e3) / 1e12, 1),
+                  "mfma_frac": round(work["layer_flops"] / (ms_per_step / 1e3) / 1e12
+                                     / MFMA_F16_PEAK_TFLOPS, 4),
                   "algorithmic_bytes": work["layer_bytes"], "rows": work["P"],
                   "touched_slots": work["touched"], "no_events_ms": round(plain_ms, 4),
                   "staged_calls_ms": round(staged_ms, 4), "staged_equals_fused": same,

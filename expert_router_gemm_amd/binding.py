@@ -36,7 +36,8 @@ class Shape(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_slots", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("dispatch", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32)]
 
     def __repr__(self):
         return "Shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -134,9 +135,10 @@ def _check(fn: str, st: int):
 
 
 def make_shape(*, hidden, inter, n_experts, top_k, n_slots, n_shared=0, act=MOE_F16,
-               dispatch=None, shared=False) -> Shape:
+               dispatch=None, shared=False, n_groups=0, topk_groups=0) -> Shape:
     return Shape(hidden, inter, n_experts, top_k, n_slots, n_shared, act,
-                 act if dispatch is None else dispatch, MOE_F_SHARED if shared else 0)
+                 act if dispatch is None else dispatch, MOE_F_SHARED if shared else 0,
+                 n_groups, topk_groups)
 
 
 def moe_workspace_bytes(shape: Shape, T: int) -> int:

@@ -40,9 +40,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
+# Per-file extra hipcc flags (none at present).
+FILE_FLAGS = {}
+
+
 def _compile(src: str, bdir: str = BUILD, extra=()) -> str:
     obj = os.path.join(bdir, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPFLAGS, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -54,9 +54,11 @@ hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long m
 // ---------------------------------------------------------------- routing
 // Partial logits parts[z][T][ld] fp32, z < nsplit (E expert columns, then
 // the shared-gate column if has_gate), summed in z order, plus bias ->
-// topk_idx/topk_w [T][K], shared_gate [T], logits_out [T][E].
+// topk_idx/topk_w [T][K], shared_gate [T], logits_out [T][E].  G > 0:
+// group-limited selection (M of G groups), see moe_shape.n_groups.
 hipError_t launch_topk(const float *parts, int nsplit, size_t split_stride, int ld, int T,
-                       int E, int K, int has_gate, const float *bias, int32_t *topk_idx,
+                       int E, int K, int has_gate, int G, int M, const float *bias,
+                       int32_t *topk_idx,
                        float *topk_w, float *shared_gate, float *logits_out, hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch

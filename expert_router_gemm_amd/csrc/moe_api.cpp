@@ -19,6 +19,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxSlots = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxShared = 16;
+constexpr int kMaxGroupsRoute = 64;  // expert groups of group-limited routing
 constexpr int64_t kMaxTokens = 1 << 20;
 
 inline size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -74,6 +75,14 @@ moe_status check_shape(const moe_shape *s) {
     if ((s->flags & MOE_F_SHARED) && s->n_shared < 1) return MOE_ERR_SHAPE;
     if (s->act != MOE_F32 && s->act != MOE_F16) return MOE_ERR_DTYPE;
     if (s->dispatch != s->act && !(s->dispatch == MOE_FP8_E4M3 && s->act == MOE_F16)) return MOE_ERR_DTYPE;
+    if (s->n_groups != 0) {
+        if (s->n_groups < 0 || s->n_groups > kMaxGroupsRoute || s->n_experts % s->n_groups)
+            return MOE_ERR_SHAPE;
+        if (s->topk_groups < 1 || s->topk_groups > s->n_groups) return MOE_ERR_SHAPE;
+        if ((long)s->top_k > (long)s->topk_groups * (s->n_experts / s->n_groups)) return MOE_ERR_SHAPE;
+    } else if (s->topk_groups != 0) {
+        return MOE_ERR_SHAPE;
+    }
     return MOE_OK;
 }
 
@@ -204,6 +213,7 @@ hipError_t route_impl(const moe_shape &s, int T, const void *h, const void *w_ro
     }
     if (e != hipSuccess) return e;
     return launch_topk(logits_buf, a.ksplit, a.split_stride, N, T, s.n_experts, s.top_k, gate,
+                       s.n_groups, s.topk_groups,
                        bias, topk_idx, topk_w, shared_gate, logits_user, st);
 }
 

@@ -62,7 +62,7 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
 template <int EPL, int NS>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ parts, int nsplit,
                                                    size_t split_stride, int ld, int T, int E,
-                                                   int K, int has_gate,
+                                                   int K, int has_gate, int G, int M,
                                                    const float *__restrict__ bias,
                                                    int32_t *__restrict__ topk_idx,
                                                    float *__restrict__ topk_w,
@@ -103,9 +103,46 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ par
         }
     }
 
+    // Group-limited routing (G > 0): G contiguous groups of E/G experts; a
+    // group's score is its best logit; the M best groups (ties: lower group
+    // id) stay eligible.  Lane g ends up holding group g's key.
+    uint32_t allowed = 0xffffffffu;  // bit j: expert lane + 64 j is eligible
+    if (G > 0) {
+        const int gs = E / G;
+        uint32_t g_hi = 0, g_lo = 0;
+        for (int g = 0; g < G; ++g) {
+            uint32_t hi = 0, lo = 0;
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) {
+                const int e = lane + 64 * j;
+                if (e < E && e / gs == g) hi = max(hi, ordered_bits(v[j]));
+            }
+            wave_max_key(hi, lo);
+            if (lane == g) {
+                g_hi = hi;
+                g_lo = ~(uint32_t)g;
+            }
+        }
+        uint64_t keep = 0;
+        for (int r = 0; r < M; ++r) {
+            uint32_t hi = g_hi, lo = g_lo;
+            wave_max_key(hi, lo);
+            const int bg = (int)~lo;
+            keep |= 1ull << bg;
+            if (lane == bg) g_hi = g_lo = 0;
+        }
+        allowed = 0;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + 64 * j;
+            if (e < E && ((keep >> (e / gs)) & 1ull)) allowed |= 1u << j;
+        }
+    }
+
     // K rounds; round 0 yields the maximum logit m.  Keys of absent experts
-    // and of experts already taken are 0, below every finite logit's key.
-    uint32_t taken = 0;
+    // and of experts already taken or not eligible are 0, below every
+    // finite logit's key.
+    uint32_t taken = ~allowed;
     int my_id = 0;
     float my_v = 0.0f;
     for (int k = 0; k < K; ++k) {
@@ -148,11 +185,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ par
 
 template <int EPL>
 hipError_t launch_e(dim3 grid, const float *logits, int nsplit, size_t split_stride, int ld,
-                    int T, int E, int K, int has_gate, const float *bias, int32_t *topk_idx,
+                    int T, int E, int K, int has_gate, int G, int M, const float *bias,
+                    int32_t *topk_idx,
                     float *topk_w, float *shared_gate, float *logits_out, hipStream_t s) {
 #define MOE_TOPK(NS)                                                                          \
     hipLaunchKernelGGL((topk_kernel<EPL, NS>), grid, dim3(256), 0, s, logits, nsplit,         \
-                       split_stride, ld, T, E, K, has_gate, bias, topk_idx, topk_w,            \
+                       split_stride, ld, T, E, K, has_gate, G, M, bias, topk_idx, topk_w,      \
                        shared_gate, logits_out)
     switch (nsplit) {  // the splits the router picks for common hidden sizes
     case 1: MOE_TOPK(1); break;
@@ -170,23 +208,24 @@ hipError_t launch_e(dim3 grid, const float *logits, int nsplit, size_t split_str
 }  // namespace
 
 hipError_t launch_topk(const float *logits, int nsplit, size_t split_stride, int ld, int T,
-                       int E, int K, int has_gate, const float *bias, int32_t *topk_idx,
+                       int E, int K, int has_gate, int G, int M, const float *bias,
+                       int32_t *topk_idx,
                        float *topk_w, float *shared_gate, float *logits_out, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     dim3 grid((T + 3) / 4);
     if (E <= 64)
-        return launch_e<1>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, bias,
+        return launch_e<1>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, G, M, bias,
                            topk_idx, topk_w, shared_gate, logits_out, s);
     if (E <= 128)
-        return launch_e<2>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, bias,
+        return launch_e<2>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, G, M, bias,
                            topk_idx, topk_w, shared_gate, logits_out, s);
     if (E <= 256)
-        return launch_e<4>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, bias,
+        return launch_e<4>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, G, M, bias,
                            topk_idx, topk_w, shared_gate, logits_out, s);
     if (E <= 512)
-        return launch_e<8>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, bias,
+        return launch_e<8>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, G, M, bias,
                            topk_idx, topk_w, shared_gate, logits_out, s);
-    return launch_e<16>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, bias,
+    return launch_e<16>(grid, logits, nsplit, split_stride, ld, T, E, K, has_gate, G, M, bias,
                         topk_idx, topk_w, shared_gate, logits_out, s);
 }
 

@@ -83,6 +83,16 @@ typedef struct {
     int32_t act;       /* moe_dtype of h, weights and outputs: F32 or F16 */
     int32_t dispatch;  /* moe_dtype of dispatched rows: == act, or FP8_E4M3 */
     uint32_t flags;    /* MOE_F_SHARED */
+    /* Group-limited routing (the outlook of section 八: route to expert
+     * groups first, then to experts).  n_groups = 0: off.  Otherwise the E
+     * experts form n_groups contiguous groups of E / n_groups (a group is
+     * one EP rank's range, section 2.1); a group's score is its largest
+     * logit; only the topk_groups best groups (ties: lower group id) are
+     * eligible for the top-K.  Gates stay the softmax over all E logits.
+     * Limits: n_groups divides E, n_groups <= 64,
+     * 1 <= topk_groups <= n_groups, top_k <= topk_groups * E / n_groups. */
+    int32_t n_groups;
+    int32_t topk_groups;
 } moe_shape;
 
 /* Expert -> local slot table (device arrays), sections 2.1 and 6.3.
@@ -113,7 +123,8 @@ typedef struct {
 /* Step 1 (section 2.2): router linear and top-K.
  *   logits[t][e] = fp32(sum_i h[t][i] * w_router[e][i]) + bias[e]
  *   p[t] = softmax over all E logits; the K experts with the largest logits
- *   (ties: lower id first) are written to topk_idx[t][0..K) in that order
+ *   (ties: lower id first; with shape.n_groups > 0 only experts of the
+ *   topk_groups best groups) are written to topk_idx[t][0..K) in that order
  *   and their probabilities, not renormalised, to topk_w[t][0..K).
  *   With MOE_F_SHARED, shared_gate[t] = sigmoid(h[t] . w_router[E]).
  * h [T][H] (act); topk_idx int32 [T][K]; topk_w fp32 [T][K];

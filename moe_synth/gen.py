@@ -65,6 +65,12 @@ class MoEConfig:
     long_tail: bool        # per-expert logit bias
     seed: int
     prompts: int = 1       # prefill batches: T = prompts * tokens per prompt
+    n_groups: int = 0      # group-limited routing: expert groups (0 = off)
+    topk_groups: int = 0   # groups kept per token
+
+    @property
+    def groups(self):
+        return (self.n_groups, self.topk_groups) if self.n_groups else None
 
     @property
     def np_dtype(self):

@@ -117,7 +117,8 @@ def build_layer(cfg, *, rank: Optional[int] = None, T: Optional[int] = None,
     shape = moe.make_shape(hidden=cfg.H, inter=cfg.I, n_experts=cfg.E, top_k=cfg.K, n_slots=S,
                            n_shared=cfg.n_shared, act=act_code(cfg),
                            dispatch=moe.MOE_FP8_E4M3 if cfg.dispatch == "fp8" else None,
-                           shared=cfg.n_shared > 0)
+                           shared=cfg.n_shared > 0, n_groups=cfg.n_groups,
+                           topk_groups=cfg.topk_groups)
     wmap = moe.make_weights(w_router=d["wr"], bias=d["bias"], w_gate=G, w_up=U, w_down=D,
                             sh_gate=d.get("SG"), sh_up=d.get("SU"), sh_down=d.get("SD"))
     seed = cfg.seed if slot_seed is None else slot_seed
@@ -206,7 +207,7 @@ def oracle_forward(L: Layer, tokens: Optional[np.ndarray] = None):
     ro, rs, se = oracle.placement(cfg.E, cfg.ep_size, L.rank, replica_of=rep)
     # which slots will be touched: route this sample first
     lg = oracle.router_logits(h, L.wr[: cfg.E], L.bias)
-    idx, _ = oracle.softmax_topk(lg, cfg.K)
+    idx, _ = oracle.softmax_topk(lg, cfg.K, groups=cfg.groups)
     slot = oracle.slot_map(idx, ro, rs, L.seed, tok_ids=tok_ids)
     need = set(int(s) for s in np.unique(slot) if s >= 0)
     missing = [int(se[s]) for s in sorted(need) if int(se[s]) not in L.experts]
@@ -216,7 +217,8 @@ def oracle_forward(L: Layer, tokens: Optional[np.ndarray] = None):
     res = oracle.layer_forward(h=h, w_router=L.wr[: cfg.E], bias=L.bias,
                                w_sg=L.wr[cfg.E] if cfg.n_shared else None, slot_weights=sw,
                                shared=L.shared, rep_off=ro, rep_slot=rs, seed=L.seed, K=cfg.K,
-                               fp8_dispatch=cfg.dispatch == "fp8", tok_ids=tok_ids)
+                               fp8_dispatch=cfg.dispatch == "fp8", tok_ids=tok_ids,
+                               groups=cfg.groups)
     return res
 
 

@@ -79,9 +79,19 @@ def _route(shape, T=16, **ptr):
     (dict(n_experts=4, top_k=8), 2), (dict(n_experts=2048), 2), (dict(n_slots=0), 2),
     (dict(n_slots=2000), 2), (dict(act=7), 3), (dict(act=0, dispatch=2), 3),
     (dict(shared=True, n_shared=0), 2),
+    (dict(n_groups=7, topk_groups=2), 2), (dict(n_groups=8, topk_groups=0), 2),
+    (dict(n_groups=8, topk_groups=9), 2), (dict(n_groups=128, topk_groups=1), 2),
+    (dict(n_groups=64, topk_groups=1), 2), (dict(n_groups=0, topk_groups=2), 2),
 ])
 def test_route_rejects_bad_shapes(kw, status):
     assert _route(_shape(**kw)) == status
+
+
+def test_route_accepts_group_limits():
+    # 8 groups of 32, 4 kept: K = 8 <= 4 * 32; nothing to do at T = 0
+    assert _route(_shape(n_groups=8, topk_groups=4), T=0, ws=None) == 0
+    assert _route(_shape(n_groups=256, topk_groups=8), T=0, ws=None) == 2  # > 64 groups
+    assert _route(_shape(n_groups=64, topk_groups=2), T=0, ws=None) == 0   # K = 8 <= 2 * 4
 
 
 def test_route_rejects_bad_pointers_and_workspace():

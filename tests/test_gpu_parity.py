@@ -65,11 +65,22 @@ def _check_routing(L, st, tokens=None):
     bound = gh.logit_error_bound(L, tokens)
     err = np.abs(g_lg.astype(np.float64) - ref_lg)
     assert np.all(err <= bound), f"logit error {err.max():.3e} above bound"
-    idx2, w2 = oracle.softmax_topk(g_lg, cfg.K)
+    idx2, w2 = oracle.softmax_topk(g_lg, cfg.K, groups=cfg.groups)
     assert np.array_equal(g_idx, idx2), "top-K kernel differs from the oracle on the same logits"
     assert np.allclose(g_w, w2, rtol=4e-6, atol=1e-9), "gates differ on the same logits"
-    ref_idx, _ = oracle.softmax_topk(ref_lg, cfg.K)
+    ref_idx, _ = oracle.softmax_topk(ref_lg, cfg.K, groups=cfg.groups)
     tie = oracle.near_tie_tokens(ref_lg, cfg.K)
+    if cfg.groups:
+        # near ties among the group scores decide the kept groups, and
+        # near ties inside the kept groups decide the experts
+        G, M = cfg.groups
+        gmax = ref_lg.reshape(len(ref_lg), G, -1).max(2)
+        tie = tie | oracle.near_tie_tokens(gmax, M)
+        order = np.lexsort((np.broadcast_to(np.arange(G), gmax.shape), -gmax), axis=1)
+        kept = np.zeros_like(gmax, dtype=bool)
+        np.put_along_axis(kept, order[:, :M], True, axis=1)
+        masked = np.where(np.repeat(kept, ref_lg.shape[1] // G, axis=1), ref_lg, -1e30)
+        tie = tie | oracle.near_tie_tokens(masked, cfg.K)
     ok = ~tie
     assert np.array_equal(g_idx[ok], ref_idx[ok]), "top-k differs on a non-near-tie token"
     if cfg.n_shared:
@@ -308,13 +319,16 @@ FULL_SAMPLE = {2: 32, 3: 12, 4: 24, 5: 32}
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("n", [2, 5, 4, 3])
-def test_full_size_sampled(n):
-    """Full workload sizes in the launch configuration the benchmark times;
-    routing of a token sample and the whole dispatch are compared exactly,
-    layer outputs on the sample within the output bar."""
+@pytest.mark.parametrize("n,groups", [(2, None), (5, None), (4, None), (3, None), (2, (8, 4))])
+def test_full_size_sampled(n, groups):
+    """Full workload sizes in the launch configuration the benchmark times
+    (with --groups G,M for the group-limited case); routing of a token sample
+    and the whole dispatch are compared exactly, layer outputs on the sample
+    within the output bar."""
     cfg = moe_synth.config(n)
-    print(f"[case] full workload {n} {cfg.name}", flush=True)
+    if groups:
+        cfg = moe_synth.config(n, n_groups=groups[0], topk_groups=groups[1])
+    print(f"[case] full workload {n} {cfg.name} groups={groups}", flush=True)
     L = gh.build_layer(cfg, keep_host_weights=False)
     st = gh.gpu_stages(L)
     out = gh.gpu_forward(L).cpu().numpy()
@@ -372,6 +386,26 @@ def test_tiled_router_k_split_with_shared_gate(H):
     st = gh.gpu_stages(L)
     tie = _check_routing(L, st)
     print(f"[tiled router] H={H} near_ties={int(tie.sum())}")
+
+
+@pytest.mark.parametrize("n,G,M", [(2, 8, 4), (3, 8, 2), (5, 16, 3), (1, 4, 2)])
+def test_group_limited_routing(n, G, M):
+    """Group-limited routing (M of G contiguous expert groups by their best
+    logit): the stages and the layer against the oracle, and every token's
+    experts inside at most M groups."""
+    cfg = small_cfg(n)
+    cfg = moe_synth.scaled_config(n, T=cfg.T, H=cfg.H, I=cfg.I, n_groups=G, topk_groups=M)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    tie = _check_routing(L, st)
+    gsz = cfg.E // G
+    assert all(len(set((row // gsz).tolist())) <= M for row in st["topk_idx"])
+    _check_dispatch(L, st)
+    ref = gh.oracle_forward(L)
+    gh.assert_close(st["out"], ref["out"], "layer output", rows=~tie)
+    out = gh.gpu_forward(L).cpu().numpy()
+    assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8))
+    print(f"[groups {G}/{M}] workload {n} near_ties={int(tie.sum())}")
 
 
 def test_profiled_entry_matches_and_records_stage_events():
