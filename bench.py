@@ -219,6 +219,56 @@ def load_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+# ------------------------------------------------------------------ EPLB-lite
+
+
+def eplb_report(ctx, steps: int = 12):
+    """Monitor cost and balance effect of EPLB-lite on this workload's
+    routing: the device histogram per forward (HIP events), the host
+    observe + rebalance per forward, and the max/mean rank load of the
+    simulated EP group (the workload's own, else 8 ranks) after each
+    forward's rebalance.  The batch repeats, so the loads settle."""
+    import numpy as np
+    import torch
+
+    import expert_router_gemm_amd as moe
+    cfg, shape, d, b = ctx["cfg"], ctx["shape"], ctx["d"], ctx["b"]
+    E, T = cfg.E, cfg.T
+    R = cfg.ep_size if cfg.ep_size > 1 else 8
+    counts = torch.empty(E, dtype=torch.int32, device="cuda:0")
+    moe.moe_route(shape, T, d["h"], d["wr"], d["bias"], b["idx"], b["tw"],
+                  b["sg"] if cfg.n_shared else None, None, b["ws"])
+    for _ in range(3):
+        moe.moe_expert_counts(shape, T, b["idx"], counts)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 50
+    e0.record()
+    for _ in range(n):
+        moe.moe_expert_counts(shape, T, b["idx"], counts)
+    e1.record()
+    torch.cuda.synchronize()
+    counts_us = e0.elapsed_time(e1) * 1e3 / n
+    ecfg = moe.make_eplb_config(n_experts=E, n_ranks=R, window=4, max_moves=2, spare_slots=2)
+    st = np.zeros(moe.moe_eplb_state_bytes(ecfg), np.uint8)
+    moe.moe_eplb_init(ecfg, st)
+    host_us, imb, moves = [], [], []
+    c = counts.cpu().numpy()
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        moe.moe_eplb_observe(st, c)
+        before = moe.moe_eplb_loads(st, R)[1]
+        mv = moe.moe_eplb_rebalance(st, 2)
+        host_us.append((time.perf_counter() - t0) * 1e6)
+        imb.append(round(before, 4))
+        moves += mv
+    final = moe.moe_eplb_loads(st, R)[1]
+    return dict(ranks=R, window=4, max_moves=2, spare_slots=2,
+                counts_kernel_us=round(counts_us, 2),
+                host_observe_rebalance_us=round(statistics.median(host_us), 1),
+                imbalance_per_forward=imb, imbalance_final=round(final, 4),
+                moves=[list(m) for m in moves])
+
+
 # ------------------------------------------------------------------ CPU baseline
 
 
@@ -327,6 +377,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (PMC scale)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--eplb", action="store_true",
+                    help="also report the EPLB-lite monitor cost and rank balance")
     ap.add_argument("--groups", metavar="G,M", default=None,
                     help="group-limited routing: keep M of G contiguous expert groups")
     args = ap.parse_args()
@@ -426,6 +478,8 @@ def main():
         torch.mul(a, 1.0, out=bb)
         torch.cuda.synchronize()
 
+    eplb = eplb_report(ctx) if args.eplb else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(ctx, args.cpu_budget)
@@ -461,6 +515,8 @@ def main():
                   "staged_calls_ms": round(staged_ms, 4), "staged_equals_fused": same,
                   "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}},
     }
+    if eplb:
+        rec["eplb"] = eplb
     print(json.dumps(rec))
     return 0
 

@@ -21,8 +21,11 @@ MOE_X_PERMUTED, MOE_X_SHARED, MOE_X_GATHER = 0, 1, 2
 EXPORTED = (
     "moe_route", "moe_dispatch", "moe_expert_ffn_up", "moe_expert_ffn_down",
     "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_profiled",
-    "moe_workspace_bytes", "moe_status_str", "moe_version",
+    "moe_workspace_bytes", "moe_status_str", "moe_version", "moe_expert_counts",
+    "moe_eplb_state_bytes", "moe_eplb_init", "moe_eplb_observe", "moe_eplb_loads",
+    "moe_eplb_rebalance", "moe_eplb_slot_map",
 )
+_HOST_ONLY = ("moe_workspace_bytes", "moe_status_str", "moe_version", "moe_eplb_state_bytes")
 
 
 class MoEError(RuntimeError):
@@ -50,6 +53,12 @@ class SlotMap(ctypes.Structure):
 
 class Profile(ctypes.Structure):
     _fields_ = [("events", ctypes.c_void_p * 6)]
+
+
+class EplbConfig(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("n_ranks", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("max_moves", ctypes.c_int32),
+                ("spare_slots", ctypes.c_int32), ("threshold", ctypes.c_double)]
 
 
 class Weights(ctypes.Structure):
@@ -84,11 +93,20 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.POINTER(Profile), P]
         L.moe_workspace_bytes.argtypes = [SP, I32]
         L.moe_workspace_bytes.restype = SZ
+        L.moe_expert_counts.argtypes = [SP, I32, P, P, P]
+        EP = ctypes.POINTER(EplbConfig)
+        L.moe_eplb_state_bytes.argtypes = [EP]
+        L.moe_eplb_state_bytes.restype = SZ
+        L.moe_eplb_init.argtypes = [EP, P, SZ]
+        L.moe_eplb_observe.argtypes = [P, P]
+        L.moe_eplb_loads.argtypes = [P, P, P]
+        L.moe_eplb_rebalance.argtypes = [P, P, P]
+        L.moe_eplb_slot_map.argtypes = [P, I32, P, P, P, P]
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_version.restype = ctypes.c_char_p
         for fn in EXPORTED:
-            if fn not in ("moe_workspace_bytes", "moe_status_str", "moe_version"):
+            if fn not in _HOST_ONLY:
                 getattr(L, fn).restype = ctypes.c_int
         _ = U64
         _lib = L
@@ -223,3 +241,71 @@ def make_weights(*, w_router, bias=None, w_gate, w_up, w_down, sh_gate=None, sh_
 
 def make_slot_map(rep_off, rep_slot, seed: int) -> SlotMap:
     return SlotMap(_p(rep_off), _p(rep_slot), seed)
+
+
+# ---------------------------------------------------------------- EPLB-lite
+
+def moe_expert_counts(shape, T, topk_idx, counts, stream=None):
+    _check("moe_expert_counts", lib().moe_expert_counts(
+        ctypes.byref(shape), T, _p(topk_idx), _p(counts), _stream(stream)))
+
+
+def make_eplb_config(*, n_experts, n_ranks, window, max_moves=2, spare_slots=1,
+                     threshold=1.2) -> EplbConfig:
+    return EplbConfig(n_experts, n_ranks, window, max_moves, spare_slots, threshold)
+
+
+def _host(a, dtype):
+    import numpy as np
+    if not (isinstance(a, np.ndarray) and a.dtype == dtype and a.flags.c_contiguous):
+        raise ValueError(f"expected a C-contiguous numpy {np.dtype(dtype).name} array")
+    return a.ctypes.data
+
+
+def moe_eplb_state_bytes(cfg: EplbConfig) -> int:
+    return int(lib().moe_eplb_state_bytes(ctypes.byref(cfg)))
+
+
+def moe_eplb_init(cfg: EplbConfig, state):
+    """state: host numpy uint8 array of moe_eplb_state_bytes(cfg) bytes."""
+    import numpy as np
+    _check("moe_eplb_init", lib().moe_eplb_init(ctypes.byref(cfg), _host(state, np.uint8),
+                                                state.nbytes))
+
+
+def moe_eplb_observe(state, counts):
+    import numpy as np
+    _check("moe_eplb_observe", lib().moe_eplb_observe(_host(state, np.uint8),
+                                                      _host(counts, np.int32)))
+
+
+def moe_eplb_loads(state, n_ranks: int):
+    import numpy as np
+    loads = np.empty(n_ranks, np.float64)
+    imb = ctypes.c_double()
+    _check("moe_eplb_loads", lib().moe_eplb_loads(_host(state, np.uint8), _host(loads, np.float64),
+                                                  ctypes.byref(imb)))
+    return loads, imb.value
+
+
+def moe_eplb_rebalance(state, max_moves: int):
+    import numpy as np
+    n = ctypes.c_int32()
+    moves = np.zeros((max(max_moves, 1), 2), np.int32)
+    _check("moe_eplb_rebalance", lib().moe_eplb_rebalance(_host(state, np.uint8),
+                                                          ctypes.byref(n), _host(moves, np.int32)))
+    return [tuple(int(v) for v in m) for m in moves[: n.value]]
+
+
+def moe_eplb_slot_map(state, cfg: EplbConfig, rank: int):
+    """(rep_off [E+1], rep_slot [nnz], slot_expert [S]) host arrays."""
+    import numpy as np
+    E, R, sp = cfg.n_experts, cfg.n_ranks, cfg.spare_slots
+    off = np.empty(E + 1, np.int32)
+    slot = np.empty(E + R * sp, np.int32)
+    se = np.empty(E // R + sp, np.int32)
+    n = ctypes.c_int32()
+    _check("moe_eplb_slot_map", lib().moe_eplb_slot_map(
+        _host(state, np.uint8), rank, _host(off, np.int32), _host(slot, np.int32),
+        _host(se, np.int32), ctypes.byref(n)))
+    return off, slot[: off[E]].copy(), se[: n.value].copy()

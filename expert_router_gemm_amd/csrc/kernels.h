@@ -81,6 +81,11 @@ struct DispatchArgs {
 size_t dispatch_scratch_bytes(int T, int K, int S);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
 
+// ---------------------------------------------------------------- monitor
+// counts[e] = #{p < pairs : topk_idx[p] == e}, e < E (E <= 1024).
+hipError_t launch_expert_counts(const int32_t *topk_idx, long pairs, int E, int32_t *counts,
+                                hipStream_t s);
+
 // ---------------------------------------------------------------- combine
 struct CombineArgs {
     int T, K, H, n_shared, dtype;

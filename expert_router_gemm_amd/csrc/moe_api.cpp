@@ -506,6 +506,18 @@ MOE_EXPORT moe_status moe_combine(const moe_shape *shape, int32_t T, const void 
     return MOE_OK;
 }
 
+MOE_EXPORT moe_status moe_expert_counts(const moe_shape *shape, int32_t T,
+                                        const int32_t *topk_idx, int32_t *counts, void *stream) {
+    TRY(check_shape(shape));
+    TRY(check_T(T));
+    TRY(need4(counts));
+    if (T > 0) TRY(need4(topk_idx));
+    TRY(device_ok());
+    LAUNCH(launch_expert_counts(topk_idx, (long)T * shape->top_k, shape->n_experts, counts,
+                                (hipStream_t)stream));
+    return MOE_OK;
+}
+
 namespace {
 moe_status layer_forward_impl(const moe_shape *shape, const moe_weights *w,
                               const moe_slot_map *map, int32_t T, const void *h, void *out,

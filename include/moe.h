@@ -222,6 +222,66 @@ moe_status moe_layer_forward_profiled(const moe_shape *shape, const moe_weights 
                                       void *out, void *ws, size_t ws_bytes,
                                       const moe_profile *prof, void *stream);
 
+/* ------------------------------------------------------------------
+ * EPLB-lite: the load balancer of section 6.2 with the redundant copies of
+ * section 6.3, for one EP group of n_ranks GPUs (expert e's home is rank
+ * e / (E / n_ranks), section 2.1).
+ *   monitor  moe_expert_counts (device) gives one forward's per-expert
+ *            token counts; moe_eplb_observe pushes them (host copy) into a
+ *            sliding window of the last `window` forwards.  A rank's load is
+ *            the sum over the copies it holds of count_e / n_copies_e (a
+ *            token picks one of an expert's copies uniformly, section 6.3),
+ *            accumulated in expert order in double precision.
+ *   detect   max rank load / mean rank load > threshold (1.2 on the page).
+ *   migrate  moe_eplb_rebalance: greedily, up to max_moves times, the copy
+ *            with the largest per-copy load on the most loaded rank (ties:
+ *            lower expert id; skipping experts that cannot be placed) gets a
+ *            new copy on the least loaded rank (ties: lower rank) that holds
+ *            none and has one of its spare_slots free.  Home copies stay.
+ *   tables   moe_eplb_slot_map writes one rank's moe_slot_map arrays for
+ *            the current placement: home experts in slots 0..E/R-1, added
+ *            copies after them in the order they were added; each expert
+ *            lists its copies home first, a copy on another rank as -1.
+ *            The new expert weights must be in place before a forward uses
+ *            the new table; keep the old table for work already queued (the
+ *            page's double-buffered routing table).
+ * The monitor state is caller memory of moe_eplb_state_bytes(cfg) bytes;
+ * these calls are host-only and never touch a device.  Calls on one state
+ * must not overlap. */
+typedef struct {
+    int32_t n_experts;   /* E, 1..1024 */
+    int32_t n_ranks;     /* R, 1..64, divides E */
+    int32_t window;      /* forwards in the sliding window, 1..4096 */
+    int32_t max_moves;   /* copies added per triggered rebalance, 0..64 */
+    int32_t spare_slots; /* extra slots per rank for added copies, 0..64 */
+    double threshold;    /* trigger: max / mean rank load > threshold (>= 1) */
+} moe_eplb_config;
+
+/* Per-expert token counts of one forward: counts[e] = #{(t, k): topk_idx[t][k]
+ * == e}, e < E (int32 [E], overwritten; ids outside [0, E) are ignored).
+ * Exact (integer) and independent of the order of the additions. */
+moe_status moe_expert_counts(const moe_shape *shape, int32_t T, const int32_t *topk_idx,
+                             int32_t *counts, void *stream);
+
+/* (host) Bytes of monitor state for cfg; 0 if cfg is invalid. */
+size_t moe_eplb_state_bytes(const moe_eplb_config *cfg);
+/* (host) Initialise the state: empty window, one home copy per expert. */
+moe_status moe_eplb_init(const moe_eplb_config *cfg, void *state, size_t state_bytes);
+/* (host) Push one forward's counts (host int32 [E], each >= 0). */
+moe_status moe_eplb_observe(void *state, const int32_t *counts);
+/* (host) Rank loads over the window (double [R], may be NULL) and max/mean
+ * (0 when every load is 0). */
+moe_status moe_eplb_loads(const void *state, double *loads, double *imbalance);
+/* (host) If max/mean > threshold, add up to max_moves copies; *n_moves gets
+ * the number added and moves (int32 [max_moves][2], may be NULL) the
+ * (expert, rank) pairs in order.  No trigger: *n_moves = 0. */
+moe_status moe_eplb_rebalance(void *state, int32_t *n_moves, int32_t *moves);
+/* (host) One rank's table: rep_off [E+1], rep_slot [E + R * spare_slots],
+ * slot_expert [E/R + spare_slots] (may be NULL: the expert each local slot
+ * must hold), *n_slots (may be NULL). */
+moe_status moe_eplb_slot_map(const void *state, int32_t rank, int32_t *rep_off,
+                             int32_t *rep_slot, int32_t *slot_expert, int32_t *n_slots);
+
 /* (host) Workspace bytes that moe_layer_forward needs for T tokens; also
  * enough for moe_dispatch and moe_expert_ffn with cap_rows <= T*K (or
  * n_shared*T for the shared experts).  Returns 0 for an invalid shape. */

@@ -178,3 +178,12 @@ def test_profiled_entry_requires_profile():
     w = moe.Weights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)
     assert L.moe_layer_forward_profiled(ctypes.byref(s), ctypes.byref(w), ctypes.byref(sm), 16,
                                         FAKE, FAKE, FAKE, 1 << 40, None, None) == 1
+
+
+def test_expert_counts_validates_before_launch():
+    L = moe.lib()
+    s = _shape()
+    assert L.moe_expert_counts(ctypes.byref(s), 16, FAKE, None, None) == 1   # counts missing
+    assert L.moe_expert_counts(ctypes.byref(s), 16, None, FAKE, None) == 1   # indices missing
+    assert L.moe_expert_counts(ctypes.byref(s), 16, FAKE, FAKE + 2, None) == 4
+    assert L.moe_expert_counts(ctypes.byref(_shape(hidden=100)), 16, FAKE, FAKE, None) == 2
