@@ -17,6 +17,8 @@
 // one barrier per K step, XOR-swizzled LDS rows (see swz()).
 //
 // The grid is persistent (all resident workgroup slots): see tiled_gemm_kernel.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -28,6 +30,7 @@ constexpr int WR = 256;    // weight rows per tile: 128 gate + 128 up, or 256 do
 constexpr int BK = 64;     // reduction per pipeline step
 constexpr int PITCH = BK;  // halves per LDS row (128 B, XOR-swizzled chunks)
 constexpr int kThreads = 512;
+constexpr int kMaxDevices = 64;
 
 // LDS offset (halves) of 16-byte chunk c of row r: the chunk index is XORed
 // with r % 8, so the 16 rows one MFMA fragment read touches spread over all
@@ -285,21 +288,27 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
     if (n_groups <= 0 || n_groups > kMaxGroups) return hipErrorInvalidValue;
     const int n_ntiles = (a.N + WR / NM - 1) / (WR / NM);
     const size_t lds = (size_t)2 * (BM + WR) * PITCH * sizeof(f16);
-    static bool attr_set = false;  // idempotent; a race only repeats the call
-    if (!attr_set) {
+    // Per device, once: allow the dynamic LDS size and count the workgroups
+    // that are resident at once (cached; a race only repeats the queries).
+    static std::atomic<int> resident[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int slots = dev < kMaxDevices ? resident[dev].load(std::memory_order_relaxed) : 0;
+    if (slots <= 0) {
         hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<NM, EPI, GATHER>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    int dev = 0, cus = 256, per_cu = 1;
-    if (hipGetDevice(&dev) == hipSuccess)
+        int cus = 256, per_cu = 1;
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tiled_gemm_kernel<NM, EPI, GATHER>,
-                                                     kThreads, lds) != hipSuccess || per_cu < 1)
-        per_cu = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, tiled_gemm_kernel<NM, EPI, GATHER>, kThreads, lds) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        slots = cus * per_cu;
+        if (dev < kMaxDevices) resident[dev].store(slots, std::memory_order_relaxed);
+    }
     // every resident workgroup slot, never more than the items
-    long grid = (long)cus * per_cu;
+    long grid = slots;
     const long items = max_tiles * n_ntiles * (EPI == 2 ? a.ksplit : 1);
     if (items < grid) grid = items > 0 ? items : 1;
     hipLaunchKernelGGL((tiled_gemm_kernel<NM, EPI, GATHER>), dim3((unsigned)grid), dim3(kThreads),
