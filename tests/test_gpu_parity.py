@@ -312,6 +312,51 @@ def test_dense_topk_equals_experts():
     gh.assert_close(st["out"], ref["out"], "dense layer", atol=1e-5, rtol=1e-4)
 
 
+def test_maximum_experts_top_k_slots_and_shared():
+    """The largest shapes the ABI accepts for routing and placement: E = S =
+    1024 (identity map), top_k = 16, 16 shared experts, at tiny dense dims:
+    the 16-wide top-K path, the general dispatch (S > 256) and 16 secondary
+    groups in the expert launches."""
+    cfg = moe_synth.scaled_config(3, T=48, H=128, I=128, E=1024, K=16, n_shared=16,
+                                  long_tail=False, seed=61)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    tie = _check_routing(L, st)
+    _check_dispatch(L, st)
+    assert int(st["counts"].sum()) == cfg.T * cfg.K
+    ref = gh.oracle_forward(L)
+    gh.assert_close(st["out"], ref["out"], "layer output", rows=~tie)
+    out = gh.gpu_forward(L).cpu().numpy()
+    assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8))
+
+
+def test_single_expert_is_a_plain_swiglu_ffn():
+    """E = K = S = 1: every token's gate is softmax over one logit = 1, so
+    the layer is the textbook SwiGLU FFN y = W_d (SiLU(W_g h) * W_u h),
+    checked against torch on the CPU in float64."""
+    cfg = moe_synth.scaled_config(2, T=70, H=256, I=128, E=1, K=1, ep_size=1, seed=62)
+    L = gh.build_layer(cfg)
+    out = gh.gpu_forward(L).cpu().numpy().astype(np.float64)
+    g, u, d = (torch.from_numpy(m.astype(np.float64)) for m in L.expert(0))
+    h = torch.from_numpy(L.h.astype(np.float64))
+    ref = (torch.nn.functional.silu(h @ g.T) * (h @ u.T)) @ d.T
+    gh.assert_close(out, ref.numpy(), "single-expert layer")
+
+
+@pytest.mark.parametrize("groups", [None, (10, 3)])
+def test_expert_count_not_a_multiple_of_the_wave(groups):
+    """E = 100 (lanes past E hold no expert in the top-K kernel), K = 5, full
+    layer resident, with and without a group limit."""
+    kw = dict(n_groups=groups[0], topk_groups=groups[1]) if groups else {}
+    cfg = moe_synth.scaled_config(2, T=96, H=256, I=128, E=100, K=5, ep_size=1, seed=63, **kw)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    tie = _check_routing(L, st)
+    _check_dispatch(L, st)
+    ref = gh.oracle_forward(L)
+    gh.assert_close(st["out"], ref["out"], "layer output", rows=~tie)
+
+
 # ------------------------------------------------------------ full sizes
 
 
