@@ -405,6 +405,25 @@ def test_prefill_tiled_path_small():
     print(f"[tiled] P={st['P']} max|d|={err:.3e} near_ties={int(tie.sum())}")
 
 
+@pytest.mark.parametrize("T,H,I", [(3000, 640, 384), (8192, 1024, 512)])
+def test_tiled_feature_tiles_and_ragged_rows(T, H, I):
+    """Prefill-sized groups on the LDS-tiled kernel over several feature
+    tiles (gate/up: 128 features per tile, I = 384 three tiles; down: 256
+    per tile, H = 640 two and a half), ragged row tails, K = H and K = I
+    both several 64-wide steps, items spread over the XCDs in contiguous
+    eighths; every stage and the layer against the oracle."""
+    cfg = moe_synth.scaled_config(4, T=T, H=H, I=I, seed=34)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    tie = _check_routing(L, st)
+    _check_dispatch(L, st)
+    _check_ffn(L, st)
+    _check_combine(L, st)
+    ref = gh.oracle_forward(L)
+    err = gh.assert_close(st["out"], ref["out"], "layer output", rows=~tie)
+    print(f"[tiled] T={T} H={H} I={I} P={st['P']} max|d|={err:.3e}")
+
+
 def test_tiled_shared_and_ragged_groups():
     """fp16 16-expert layer with a shared expert at T = 1000: routed groups
     (~125 rows) and the shared group (1000 rows, not a multiple of 128) on
