@@ -10,19 +10,21 @@
 //   out[r][n] = epilogue( sum_k W[g][n][k] * x[r][k] )   for rows r of group g
 //
 // Work decomposition
-//   blockIdx.x  a block of features: 4 waves x 16*NSUB features each (KW = 1;
-//               the router), or 16*NSUB = 64 features shared by the 4 waves
-//               (KW = 4; SwiGLU reads a gate and an up tile per 16-feature
-//               subtile)
+//   blockIdx.x  a block of features: 4 waves x 16*NSUB features each (KW = 1),
+//               or 16*NSUB = 64 features shared by the 4 waves (KW = 4: the
+//               expert GEMMs, and the fp16 router when its K slices are
+//               multiples of 512; SwiGLU reads a gate and an up tile per
+//               16-feature subtile)
 //   blockIdx.y  group g (expert slot)
 //   blockIdx.z  (first row block) * ksplit + K slice; row blocks of 64 rows
 //               are strided by gridDim.z / ksplit.  ksplit > 1 (router only)
 //               writes one fp32 partial per K slice; the top-K kernel sums
 //               them in slice order, so the result stays deterministic.
-// KW = 4 (the expert FFN): wave w of a block runs quarter w of K for all 64
-// features, so each activation fragment it loads feeds 4 (down) or 8
-// (gate/up) MFMAs, while a block still covers only 64 features (fine-grained
-// blocks keep the tail of an uneven grid short).  The 4 partial tiles meet
+// KW = 4: wave w of a block runs quarter w of K (of the K slice, for the
+// router) for all 64 features, so each activation fragment it loads feeds 4
+// (down, router) or 8 (gate/up) MFMAs and a block loads its token rows once,
+// while a block still covers only 64 features (fine-grained blocks keep the
+// tail of an uneven grid short).  The 4 partial tiles meet
 // in LDS and are summed in K order (deterministic); wave w then applies the
 // epilogue to subtile w.  The 64 rows of a row block are processed in MT =
 // 1, 2 or 4 tiles of 16, chosen from the rows actually present, so one pass
@@ -142,7 +144,7 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
                                             int r0, int r1, int kz, f32x4 *red) {
     constexpr bool SW = EPI == EPI_SWIGLU;
     constexpr int NM = SW ? 2 * NSUB : NSUB;
-    static_assert(KW == 1 || (KW == 4 && NSUB == 4 && EPI != EPI_LOGITS), "K split shape");
+    static_assert(KW == 1 || (KW == 4 && NSUB == 4), "K split shape");
     typedef typename Frag<TW>::vec V;
     typedef XFrag<TW, XM> XF;
     typedef typename XF::raw XR;
@@ -239,7 +241,16 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
             }
             __syncthreads();
             const int r = rows[t];
-            if (r < r1) {
+            if (EPI == EPI_LOGITS) {  // fp32 partial of K slice kz
+                if (r < r1) {
+                    float *o = reinterpret_cast<float *>(a.out) + (size_t)kz * a.split_stride +
+                               (size_t)r * a.out_ld;
+                    const int fb = f0 + 16 * wk + 4 * lg;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (fb + j < a.N) o[fb + j] = s0[j];
+                }
+            } else if (r < r1) {
                 float sc = 1.0f;
                 if (XM == DT_FP8) sc = a.x_scale[r] * 256.0f;  // undo the 2^-8 of the decode
                 const int fb = f0 + 16 * wk + 4 * lg;
@@ -387,7 +398,10 @@ hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int m
                              : launch_t<f16, DT_F16, 2, EPI_STORE>(a, n_groups, zblocks, s);
             return launch_t<f16, DT_F16, 1, EPI_STORE>(a, n_groups, zblocks, s);
         }
-        return launch_t<f16, DT_F16, 1, EPI_LOGITS>(a, n_groups, zblocks, s);
+        // router: the 4 waves of a block split each K slice and share 64
+        // experts, so a block loads its token rows once (not once per wave)
+        return kw_ok ? launch_t<f16, DT_F16, 4, EPI_LOGITS, 2, 4>(a, n_groups, zblocks, s)
+                     : launch_t<f16, DT_F16, 1, EPI_LOGITS>(a, n_groups, zblocks, s);
     }
     if (mode == STREAM_SWIGLU) return launch_t<float, DT_F32, 1, EPI_SWIGLU>(a, n_groups, zblocks, s);
     if (mode == STREAM_STORE) return launch_t<float, DT_F32, 1, EPI_STORE>(a, n_groups, zblocks, s);

@@ -34,9 +34,9 @@ inline int has_gate(const moe_shape &s) { return (s.flags & MOE_F_SHARED) ? 1 : 
 
 // Router plan.  Large batches (T >= 2048, fp16) use the LDS-tiled kernel
 // and small ones the weight-stream kernel; either way K is split (slices a
-// multiple of the kernel's K granularity) until there are at least 256
-// workgroups, at most MOE_ROUTER_MAX_SPLIT slices.  The top-K kernel sums
-// the slices in order.
+// multiple of the kernel's K granularity, at most MOE_ROUTER_MAX_SPLIT) so
+// that the workgroup count comes closest to 256.  The top-K kernel sums the
+// slices in order.
 struct RouterPlan {
     bool tiled;
     int ksplit;
@@ -48,12 +48,22 @@ RouterPlan router_plan(const moe_shape &s, int T) {
     p.tiled = T >= 2048 && tiled_gemm_supported_shape(s.hidden, s.act, s.act);
     const long base = p.tiled ? (long)((N + 255) / 256) * ((T + 127) / 128)
                               : (long)((N + 63) / 64) * ((T + 63) / 64);
-    const int gran = p.tiled ? 128 : 4 * (s.act == MOE_F32 ? 16 : 32);
+    // fp16 stream path: K slices that are multiples of 512 let the 4 waves of
+    // a block split each slice (see launch_stream_gemm); other sizes fall
+    // back to the 128 granularity of one wave per slice
+    int gran = p.tiled ? 128 : 4 * (s.act == MOE_F32 ? 16 : 32);
+    if (!p.tiled && s.act != MOE_F32 && s.hidden % 512 == 0) gran = 512;
+    // the valid split whose workgroup count is closest to 256 (measured:
+    // 224 blocks beat 112 and 448 at decode sizes)
     p.ksplit = 1;
+    long best = -1;
     for (int d = 1; d <= MOE_ROUTER_MAX_SPLIT; ++d) {
         if (s.hidden % (d * gran)) continue;
-        p.ksplit = d;
-        if (base * d >= 256) break;
+        const long dist = base * d > 256 ? base * d - 256 : 256 - base * d;
+        if (best < 0 || dist < best) {
+            best = dist;
+            p.ksplit = d;
+        }
     }
     return p;
 }

@@ -442,9 +442,10 @@ def test_tiled_shared_and_ragged_groups():
 @pytest.mark.parametrize("H", [1536, 7168])
 def test_tiled_router_k_split_with_shared_gate(H):
     """Router on the tiled kernel with the shared-gate column (N = E + 1, a
-    ragged feature tile) and a ragged token tail (T = 2100): H = 1536 splits
-    K in 12 slices of 2 K steps, H = 7168 in 14 slices of 8; routing is
-    checked token by token."""
+    ragged feature tile) and a ragged token tail (T = 2100): 34 tiles, so
+    H = 1536 splits K in 6 slices of 4 K steps and H = 7168 in 8 slices of
+    14 (the split closest to 256 workgroups); routing is checked token by
+    token."""
     cfg = moe_synth.scaled_config(1, T=2100, H=H, I=128, dtype="f16", seed=33)
     L = gh.build_layer(cfg)
     st = gh.gpu_stages(L)
