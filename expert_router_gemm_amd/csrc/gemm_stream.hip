@@ -75,7 +75,7 @@
 #define MOE_STREAM_STORE_NSUB_WIDE 4
 #endif
 #ifndef MOE_STREAM_STORE_U_WIDE
-#define MOE_STREAM_STORE_U_WIDE 4
+#define MOE_STREAM_STORE_U_WIDE 2
 #endif
 #ifndef MOE_STREAM_SWIGLU_KW
 #define MOE_STREAM_SWIGLU_KW 4
