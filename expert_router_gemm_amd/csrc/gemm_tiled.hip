@@ -12,9 +12,9 @@
 // 256 features otherwise), BK = 64.  512 threads = 8 waves (2 per SIMD) in a
 // 2 x 4 arrangement; each wave owns 64 rows x 64 weight rows as 16 tiles of
 // v_mfma_f32_16x16x32_f16.
-// Global -> register -> LDS staging with a two-step register prefetch (the
-// loads for step k+2 are in flight while step k computes), two LDS buffers,
-// one barrier per K step, XOR-swizzled LDS rows (see swz()).
+// Global -> register -> LDS staging (two register sets), three LDS stages so
+// the next step's first fragments are read before the barrier, one barrier
+// per K step, XOR-swizzled LDS rows (see swz()).
 //
 // The grid is persistent (all resident workgroup slots): see tiled_gemm_kernel.
 #include <atomic>
@@ -35,6 +35,10 @@ constexpr int RSTEP = kThreads / 8;  // rows one staging pass covers
 constexpr int NXL = BM / RSTEP;      // x loads per thread per K step
 constexpr int NWL = WR / RSTEP;      // weight loads per thread per K step
 constexpr int kMaxDevices = 64;
+#ifndef MOE_TILED_3ST
+#define MOE_TILED_3ST 1
+#endif
+constexpr int NSTAGE = MOE_TILED_3ST ? 3 : 2;  // LDS stages
 
 // LDS offset (halves) of 16-byte chunk c of row r: the chunk index is XORed
 // with r % 8, so the 16 rows one MFMA fragment read touches spread over all
@@ -146,6 +150,7 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
 #pragma unroll
             for (int j = 0; j < NJ; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+#if !MOE_TILED_3ST
     auto compute = [&](int buf) {
         const f16 *A = As + buf * BM * PITCH;
         const f16 *B = Bs + buf * WR * PITCH;
@@ -170,6 +175,7 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
                     for (int j = 0; j < NJ; ++j) acc[m][i][j] = mfma16(af[i], bf[m][j], acc[m][i][j]);
         }
     };
+#endif
 
     // This tile's K slice: steps [kz*nk, (kz+1)*nk), nk even (K is a
     // multiple of 2*BK*ksplit).  The loop body is branch-free so the
@@ -177,6 +183,91 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
     // last step and is never used).
     const int nk = EPI == 2 ? K / BK / a.ksplit : K / BK;
     const int k0 = EPI == 2 ? kz * nk * BK : 0;
+#if MOE_TILED_3ST
+    // Three LDS stages: step k computes from stage k%3 while the staged data
+    // of step k+2 goes to stage (k+2)%3 (last read during step k-1), so the
+    // first-half fragments of step k+1 (stage (k+1)%3, complete since the
+    // barrier that ended step k-1) are read during step k and no step starts
+    // by waiting for LDS.  Per step: the 16 MFMAs of the first K half with
+    // the fragment reads of the second, then the 16 of the second half with
+    // the next step's first-half reads, the staging writes and the refill
+    // loads, pinned with scheduling-group barriers; one barrier per step.
+    f16x8 af0[4], bf0[NM][NJ], af1[4], bf1[NM][NJ];
+    auto fread = [&](f16x8 *af, f16x8 (*bf)[NJ], int st, int ks) {
+        const f16 *A = As + st * BM * PITCH;
+        const f16 *B = Bs + st * WR * PITCH;
+        const int ch = ks + lg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            af[i] = *reinterpret_cast<const f16x8 *>(A + swz(wm * 64 + i * 16 + lr, ch));
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                bf[m][j] = *reinterpret_cast<const f16x8 *>(
+                    B + swz(m * FN + wn * (FN / WNW) + j * 16 + lr, ch));
+    };
+    auto mm = [&](const f16x8 *af, f16x8 (*bf)[NJ]) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[m][i][j] = mfma16(af[i], bf[m][j], acc[m][i][j]);
+    };
+    auto order = [&]() {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < NXL + NWL; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8 - NXL - NWL, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto kstep = [&](int k) { return k0 + (k < nk ? k : nk - 1) * BK; };
+    MOE_GLOAD(ra0, rb0, k0);
+    MOE_GLOAD(ra1, rb1, k0 + BK);
+    MOE_LSTORE(ra0, rb0, 0);
+    MOE_LSTORE(ra1, rb1, 1);
+    MOE_GLOAD(ra0, rb0, kstep(2));
+    __syncthreads();
+    fread(af0, bf0, 0, 0);
+    int s0 = 0, s1 = 1, s2 = 2;  // stages of steps kt, kt+1, kt+2
+    for (int kt = 0; kt < nk; kt += 2) {
+        fread(af1, bf1, s0, 4);
+        mm(af0, bf0);
+        fread(af0, bf0, s1, 0);
+        mm(af1, bf1);
+        MOE_LSTORE(ra0, rb0, s2);
+        MOE_GLOAD(ra1, rb1, kstep(kt + 3));
+        order();
+        fread(af1, bf1, s1, 4);
+        mm(af0, bf0);
+        fread(af0, bf0, s2, 0);
+        mm(af1, bf1);
+        MOE_LSTORE(ra1, rb1, s0);
+        MOE_GLOAD(ra0, rb0, kstep(kt + 4));
+        order();
+        // steps kt+2, kt+3, kt+4 sit in stages s2, s0, s1
+        const int t = s0;
+        s0 = s2;
+        s2 = s1;
+        s1 = t;
+    }
+#else
     MOE_GLOAD(ra0, rb0, k0);
     MOE_GLOAD(ra1, rb1, k0 + BK);
     MOE_LSTORE(ra0, rb0, 0);
@@ -193,6 +284,7 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
         MOE_LSTORE(ra0, rb0, 0);
         __syncthreads();
     }
+#endif
 #undef MOE_GLOAD
 #undef MOE_LSTORE
 
@@ -241,8 +333,8 @@ template <int NM, int EPI, bool GATHER>
 __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int n_ntiles,
                                                               int n_groups) {
     extern __shared__ __attribute__((aligned(16))) f16 lds[];
-    f16 *As = lds;                          // [2][BM][PITCH]
-    f16 *Bs = lds + 2 * BM * PITCH;         // [2][WR][PITCH]
+    f16 *As = lds;                          // [NSTAGE][BM][PITCH]
+    f16 *Bs = lds + NSTAGE * BM * PITCH;    // [NSTAGE][WR][PITCH]
     __shared__ int tstart[kMaxGroups + 1];  // first row tile of each group
     __shared__ int scan[2][kThreads];
 
@@ -319,7 +411,7 @@ template <int NM, int EPI, bool GATHER>
 hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream_t s) {
     if (n_groups <= 0 || n_groups > kMaxGroups) return hipErrorInvalidValue;
     const int n_ntiles = (a.N + WR / NM - 1) / (WR / NM);
-    const size_t lds = (size_t)2 * (BM + WR) * PITCH * sizeof(f16);
+    const size_t lds = (size_t)NSTAGE * (BM + WR) * PITCH * sizeof(f16);
     // Per device, once: allow the dynamic LDS size and count the workgroups
     // that are resident at once (cached; a race only repeats the queries).
     static std::atomic<int> resident[kMaxDevices];
