@@ -9,31 +9,33 @@
 // One block per token with one thread per 8 consecutive features (up to
 // 1024 threads: 896 for hidden 7168), so every y row of the token is read
 // once with 16-byte loads; the token's local pairs are compacted in k order
-// into LDS first.
+// into LDS first (one wave, a ballot and popcounts), and each thread loads
+// them 4 at a time.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
+// 16 bytes of a row: 8 fp16 values, or two 16-byte halves of 8 fp32 values
 template <typename T>
-__device__ __forceinline__ void load8(const T *p, float v[8]);
+struct Raw8;
 template <>
-__device__ __forceinline__ void load8<f16>(const f16 *p, float v[8]) {
-    const f16x8 x = *reinterpret_cast<const f16x8 *>(p);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (float)x[j];
-}
+struct Raw8<f16> {
+    f16x8 v;
+    __device__ __forceinline__ void load(const f16 *p) { v = *reinterpret_cast<const f16x8 *>(p); }
+    __device__ __forceinline__ float operator[](int j) const { return (float)v[j]; }
+};
 template <>
-__device__ __forceinline__ void load8<float>(const float *p, float v[8]) {
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[j] = a[j];
-        v[j + 4] = b[j];
+struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const f32x4 *>(p);
+        b = *reinterpret_cast<const f32x4 *>(p + 4);
     }
-}
+    __device__ __forceinline__ float operator[](int j) const { return j < 4 ? a[j] : b[j - 4]; }
+};
+
 template <typename T>
 __device__ __forceinline__ void store8(T *p, const float v[8]);
 template <>
@@ -49,24 +51,33 @@ __device__ __forceinline__ void store8<float>(float *p, const float v[8]) {
     *reinterpret_cast<f32x4 *>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
+// Rows are summed in batches of 4 whose loads are in flight together (one
+// round trip per 4 rows instead of per row, at 4 fp16 vectors of registers).
+constexpr int kMaxPairs = 16;  // top-K limit of the shape check
+
 template <typename T>
 __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
-    __shared__ int rows[16];
-    __shared__ float gates[16];
+    __shared__ int rows[kMaxPairs];
+    __shared__ float gates[kMaxPairs];
     __shared__ int npairs;
     const int t = blockIdx.x;
-    if (threadIdx.x == 0) {
-        // local pairs of this token, compacted in k order
-        int n = 0;
-        for (int k = 0; k < a.K; ++k) {
-            const int r = a.inv_pos[(size_t)t * a.K + k];
-            if (r >= 0) {
-                rows[n] = r;
-                gates[n] = a.topk_w[(size_t)t * a.K + k];
-                ++n;
-            }
+    if (threadIdx.x < 64) {
+        // the token's local pairs, compacted in k order: lane k reads pair k,
+        // its slot among the local pairs is the count of local lanes below it
+        const int k = threadIdx.x;
+        int r = -1;
+        float g = 0.0f;
+        if (k < a.K) {
+            r = a.inv_pos[(size_t)t * a.K + k];
+            g = a.topk_w[(size_t)t * a.K + k];
         }
-        npairs = n;
+        const uint64_t local = __ballot(r >= 0);
+        if (r >= 0) {
+            const int pos = __popcll(local & ((1ull << k) - 1));
+            rows[pos] = r;
+            gates[pos] = g;
+        }
+        if (k == 0) npairs = __popcll(local);
     }
     __syncthreads();
     const int np = npairs;
@@ -77,20 +88,28 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
     T *out = reinterpret_cast<T *>(a.out) + (size_t)t * a.H;
     for (int i = threadIdx.x * 8; i < a.H; i += blockDim.x * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int q = 0; q < np; ++q) {
-            float v[8];
-            load8<T>(y + (size_t)rows[q] * a.H + i, v);
-            const float g = gates[q];
+        // batches of 4 rows: their loads are in flight together
+        for (int q0 = 0; q0 < np; q0 += 4) {
+            Raw8<T> v[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] += g * v[j];
+            for (int q = 0; q < 4; ++q)
+                if (q0 + q < np) v[q].load(y + (size_t)rows[q0 + q] * a.H + i);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q0 + q < np) {
+                    const float g = gates[q0 + q];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[j] += g * v[q][j];
+                }
+            }
         }
         if (sh) {
             float sv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int s = 0; s < a.n_shared; ++s) {
-                float v[8];
-                load8<T>(shy + ((size_t)s * a.T + t) * a.H + i, v);
+                Raw8<T> u;
+                u.load(shy + ((size_t)s * a.T + t) * a.H + i);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) sv[j] += v[j];
+                for (int j = 0; j < 8; ++j) sv[j] += u[j];
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[j] += gs * sv[j];
@@ -104,6 +123,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
     // one thread per 8 features, up to 1024 threads (whole waves)
+    if (a.K < 1 || a.K > kMaxPairs) return hipErrorInvalidValue;
     int threads = ((a.H / 8 + 63) / 64) * 64;
     if (threads > 1024) threads = 1024;
     if (a.dtype == DT_F16)
