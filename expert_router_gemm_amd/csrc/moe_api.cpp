@@ -31,6 +31,10 @@ inline int has_gate(const moe_shape &s) { return (s.flags & MOE_F_SHARED) ? 1 : 
 #ifndef MOE_ROUTER_MAX_SPLIT
 #define MOE_ROUTER_MAX_SPLIT 16
 #endif
+// Smallest batch that takes the LDS-tiled router (compile-time tuning knob).
+#ifndef MOE_ROUTER_TILED_MIN_T
+#define MOE_ROUTER_TILED_MIN_T 2048
+#endif
 
 // Router plan.  Large batches (T >= 2048, fp16) use the LDS-tiled kernel
 // and small ones the weight-stream kernel; either way K is split (slices a
@@ -45,7 +49,7 @@ struct RouterPlan {
 RouterPlan router_plan(const moe_shape &s, int T) {
     const int N = s.n_experts + has_gate(s);
     RouterPlan p;
-    p.tiled = T >= 2048 && tiled_gemm_supported_shape(s.hidden, s.act, s.act);
+    p.tiled = T >= MOE_ROUTER_TILED_MIN_T && tiled_gemm_supported_shape(s.hidden, s.act, s.act);
     const long base = p.tiled ? (long)((N + 255) / 256) * ((T + 127) / 128)
                               : (long)((N + 63) / 64) * ((T + 63) / 64);
     // fp16 stream path: K slices that are multiples of 512 let the 4 waves of
