@@ -35,10 +35,7 @@ constexpr int RSTEP = kThreads / 8;  // rows one staging pass covers
 constexpr int NXL = BM / RSTEP;      // x loads per thread per K step
 constexpr int NWL = WR / RSTEP;      // weight loads per thread per K step
 constexpr int kMaxDevices = 64;
-#ifndef MOE_TILED_3ST
-#define MOE_TILED_3ST 1
-#endif
-constexpr int NSTAGE = MOE_TILED_3ST ? 3 : 2;  // LDS stages
+constexpr int NSTAGE = 3;  // LDS stages
 
 // LDS offset (halves) of 16-byte chunk c of row r: the chunk index is XORed
 // with r % 8, so the 16 rows one MFMA fragment read touches spread over all
@@ -46,15 +43,19 @@ constexpr int NSTAGE = MOE_TILED_3ST ? 3 : 2;  // LDS stages
 // measured with SQ_LDS_BANK_CONFLICT).
 __device__ __forceinline__ int swz(int r, int c) { return r * PITCH + ((c ^ (r & 7)) << 3); }
 
-// One output tile: rows [rs, rs+128) of group g x features [n0, n0 + WR/NM).
-// 8 waves = 2 (rows) x 4 (weight rows); wave (wm, wn) owns x rows
-// wm*64..+64 and, per matrix m, weight rows m*FN + wn*FN/4 .. +FN/4
-// (FN = WR/NM features), as 4 x (4/NM) x NM tiles of 16x16x32 MFMAs.
+// One work item: x rows [rs, rs+128) of group g x features [n0, n0 + WR/NM),
+// K slice kz (router logits only).  Everything a load or the epilogue needs.
+template <int NM>
+struct Item {
+    int rs, r1, n0, kz, k0;                // rows, features, K slice, K offset
+    __amdgpu_buffer_rsrc_t xres, wres[NM];  // this tile's x rows and weight rows
+    const f16 *xgat[NXL];                  // gathered x rows (GATHER)
+};
+
 template <int NM, int EPI, bool GATHER>
-__device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs, int g, int mt,
-                                          int nt, int kz) {
-    constexpr int FN = WR / NM;   // features per tile
-    constexpr int NJ = 4 / NM;    // 16-feature subtiles per wave and matrix
+__device__ __forceinline__ Item<NM> make_item(const StreamArgs &a, int g, int mt, int nt, int kz,
+                                              int nk) {
+    constexpr int FN = WR / NM;  // features per tile
     // wave-uniform by construction; readfirstlane keeps them (and the buffer
     // descriptors built from them) in scalar registers
     g = __builtin_amdgcn_readfirstlane(g);
@@ -71,46 +72,116 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
     }
     r0 = __builtin_amdgcn_readfirstlane(r0);
     r1 = __builtin_amdgcn_readfirstlane(r1);
-    const int rs = r0 + mt * BM;
-    const int n0 = nt * FN;
+    Item<NM> it;
+    it.rs = r0 + mt * BM;
+    it.r1 = r1;
+    it.n0 = nt * FN;
+    it.kz = kz;
+    it.k0 = EPI == 2 ? kz * nk * BK : 0;
     const int K = a.K;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WNW, wn = wave % WNW;
-    const int lr = lane & 15, lg = lane >> 4;
-
-    // ---- global loads: buffer loads against per-tile resource descriptors.
-    // Rows past the tile's valid rows fall outside the descriptor's range and
-    // load zeros, so no clamping is needed; 32-bit lane offsets keep the
-    // address cost at one VGPR per load.  Thread t moves 16-byte chunk t%8 of
-    // rows t/8 + RSTEP*i (i < NXL for x, i < NWL for the weight rows).
-    const int rows_valid = (r1 - rs) < BM ? (r1 - rs) : BM;
-    const int xrow0 = a.x_broadcast ? rs - r0 : rs;
-    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+    const int tid = threadIdx.x;
+    // Buffer loads against per-tile resource descriptors: rows past the
+    // tile's valid rows fall outside the descriptor's range and load zeros,
+    // so no clamping is needed; 32-bit lane offsets keep the address cost at
+    // one VGPR per load.
+    const int rows_valid = (r1 - it.rs) < BM ? (r1 - it.rs) : BM;
+    const int xrow0 = a.x_broadcast ? it.rs - r0 : it.rs;
+    it.xres = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(reinterpret_cast<const f16 *>(a.x) + (size_t)xrow0 * K), (short)0,
         rows_valid * K * 2, 0x00020000);
     // gathered x rows (rows named by a.gather): plain global loads from the
     // row each thread moves; rows past the group repeat its last row (never
     // stored)
-    const f16 *xgat[NXL];
     if (GATHER) {
 #pragma unroll
         for (int i = 0; i < NXL; ++i) {
-            int r = rs + (tid >> 3) + RSTEP * i;
+            int r = it.rs + (tid >> 3) + RSTEP * i;
             if (r > r1 - 1) r = r1 - 1;
-            xgat[i] = reinterpret_cast<const f16 *>(a.x) +
-                      (size_t)(a.gather[r] / a.gather_div) * K + (tid & 7) * 8;
+            it.xgat[i] = reinterpret_cast<const f16 *>(a.x) +
+                         (size_t)(a.gather[r] / a.gather_div) * K + (tid & 7) * 8;
         }
     }
-
-    const int ncols = (a.N - n0) < FN ? (a.N - n0) : FN;
-    __amdgpu_buffer_rsrc_t wres[NM];
+    const int ncols = (a.N - it.n0) < FN ? (a.N - it.n0) : FN;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
-        wres[m] = __builtin_amdgcn_make_buffer_rsrc(
+        it.wres[m] = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(reinterpret_cast<const f16 *>(m == 0 ? a.w0 : a.w1) +
-                     (size_t)g * a.w_group_stride + (size_t)n0 * K),
+                     (size_t)g * a.w_group_stride + (size_t)it.n0 * K),
             (short)0, ncols * K * 2, 0x00020000);
+    return it;
+}
+
+// The items of one workgroup, in order: item j is seq.first + j*seq.step
+// (< seq.end), decoded to (group, row tile, feature tile, K slice).
+struct ItemSeq {
+    int first, step, end;
+    bool chunked;  // (group, feature tile, row tile) order, else (row tile, feature tile, slice)
+};
+
+__device__ __forceinline__ void decode_item(const int *tstart, int n_groups, int n_ntiles, int ks,
+                                            bool chunked, int item, int &g, int &mt, int &nt,
+                                            int &kz) {
+    int lo = 0, hi = n_groups - 1;
+    if (chunked) {
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tstart[mid] * n_ntiles <= item)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int tg = tstart[lo + 1] - tstart[lo];  // row tiles of group lo
+        const int local = item - tstart[lo] * n_ntiles;
+        g = lo;
+        mt = local % tg;
+        nt = local / tg;
+        kz = 0;
+    } else {
+        kz = item % ks;
+        const int tile = item / ks / n_ntiles;
+        nt = (item / ks) % n_ntiles;
+        // group holding this row tile: last g with tstart[g] <= tile
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tstart[mid] <= tile)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        g = lo;
+        mt = tile - tstart[g];
+    }
+}
+
+// The items of one workgroup, one after the other, with one pipeline: the
+// loads of an item's first K steps are issued during the previous item's
+// last steps (its K steps past the end map to the next item's first ones),
+// so only the workgroup's first item starts by waiting for memory.
+// 8 waves = 2 (rows) x 4 (weight rows); wave (wm, wn) owns x rows
+// wm*64..+64 and, per matrix m, weight rows m*FN + wn*FN/4 .. +FN/4
+// (FN = WR/NM features), as 4 x (4/NM) x NM tiles of 16x16x32 MFMAs.
+template <int NM, int EPI, bool GATHER>
+__device__ __forceinline__ void run_items(const StreamArgs &a, f16 *As, f16 *Bs,
+                                          const int *tstart, int n_groups, int n_ntiles, int ks,
+                                          const ItemSeq seq) {
+    constexpr int FN = WR / NM;   // features per tile
+    constexpr int NJ = 4 / NM;    // 16-feature subtiles per wave and matrix
+    const int K = a.K;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WNW, wn = wave % WNW;
+    const int lr = lane & 15, lg = lane >> 4;
+    // K steps per item: [kz*nk, (kz+1)*nk), nk even (K is a multiple of
+    // 2*BK*ksplit).  Items chain only with nk >= 4 (the loads run up to 3
+    // steps ahead), and not when x rows are gathered (the next item's row
+    // indices would be waited for together with the in-flight staging
+    // loads: measured 1% slower); otherwise each item restarts the pipeline.
+    const int nk = EPI == 2 ? K / BK / a.ksplit : K / BK;
+    constexpr bool CHAIN = !GATHER;
+    const bool chain = CHAIN && nk >= 4;
+
+    // Thread t moves 16-byte chunk t%8 of rows t/8 + RSTEP*i (i < NXL for x,
+    // i < NWL for the weight rows).
     const int trow = tid >> 3, tch = tid & 7;
     const int goff = trow * K * 2 + tch * 16;  // byte offset of row trow, chunk tch
     const int rstep = RSTEP * K * 2;           // RSTEP rows further
@@ -118,72 +189,43 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
 
     // two register staging sets: set 0 holds even K steps, set 1 odd ones
     f16x8 ra0[NXL], rb0[NWL], ra1[NXL], rb1[NWL];
-#define MOE_GLOAD(RA, RB, k0)                                                          \
-    {                                                                                  \
-        const int kb_ = (k0) * 2;                                                      \
-        if (GATHER) {                                                                  \
-            _Pragma("unroll") for (int i = 0; i < NXL; ++i) RA[i] = load16(xgat[i] + (k0)); \
-        } else {                                                                       \
-            _Pragma("unroll") for (int i = 0; i < NXL; ++i) RA[i] = __builtin_bit_cast( \
-                f16x8, __builtin_amdgcn_raw_buffer_load_b128(xres, goff + i * rstep + kb_, 0, 0)); \
-        }                                                                              \
-        _Pragma("unroll") for (int i = 0; i < NWL; ++i) RB[i] = __builtin_bit_cast(     \
-            f16x8, __builtin_amdgcn_raw_buffer_load_b128(                              \
-                       wres[(i * RSTEP) / FN],                                         \
-                       goff + ((i * RSTEP) % FN / RSTEP) * rstep + kb_, 0, 0));        \
-    }
-#define MOE_LSTORE(RA, RB, buf)                                                        \
-    {                                                                                  \
-        f16 *A_ = As + (buf) * BM * PITCH + lds0;                                      \
-        f16 *B_ = Bs + (buf) * WR * PITCH + lds0;                                      \
-        _Pragma("unroll") for (int i = 0; i < NXL; ++i)                                \
-            *reinterpret_cast<f16x8 *>(A_ + i * RSTEP * PITCH) = RA[i];                \
-        _Pragma("unroll") for (int i = 0; i < NWL; ++i)                                \
-            *reinterpret_cast<f16x8 *>(B_ + i * RSTEP * PITCH) = RB[i];                \
-    }
-
-    f32x4 acc[NM][4][NJ];
+    // K step s of the chain: steps past the current item's end belong to the
+    // next item (or re-read the last step when there is none; never used).
+    // Branch-free (scalar selects), so the compiler's wait counts stay exact.
+    auto gload = [&](f16x8 *RA, f16x8 *RB, const Item<NM> &cur, const Item<NM> &nxt,
+                     bool has_nxt, int s) {
+        const bool to_nxt = CHAIN && s >= nk && has_nxt;
+        const int sk = s < nk ? s : (to_nxt ? s - nk : nk - 1);
+        const int kb = ((to_nxt ? nxt.k0 : cur.k0) + sk * BK) * 2;
+        if (GATHER) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+            for (int i = 0; i < NXL; ++i)
+                RA[i] = load16((to_nxt ? nxt.xgat[i] : cur.xgat[i]) + kb / 2);
+        } else {
+            const __amdgpu_buffer_rsrc_t xr = to_nxt ? nxt.xres : cur.xres;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < NXL; ++i)
+                RA[i] = __builtin_bit_cast(
+                    f16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, goff + i * rstep + kb, 0, 0));
+        }
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#if !MOE_TILED_3ST
-    auto compute = [&](int buf) {
-        const f16 *A = As + buf * BM * PITCH;
-        const f16 *B = Bs + buf * WR * PITCH;
-#pragma unroll
-        for (int ks = 0; ks < BK / 8; ks += 4) {  // two 32-wide MFMA steps (in chunks)
-            const int ch = ks + lg;                // this lane's logical 16-byte chunk
-            f16x8 af[4], bf[NM][NJ];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const f16x8 *>(A + swz(wm * 64 + i * 16 + lr, ch));
-#pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    bf[m][j] = *reinterpret_cast<const f16x8 *>(
-                        B + swz(m * FN + wn * (FN / WNW) + j * 16 + lr, ch));
-#pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) acc[m][i][j] = mfma16(af[i], bf[m][j], acc[m][i][j]);
+        for (int i = 0; i < NWL; ++i) {
+            const int m = (i * RSTEP) / FN;
+            const __amdgpu_buffer_rsrc_t wr = to_nxt ? nxt.wres[m] : cur.wres[m];
+            RB[i] = __builtin_bit_cast(
+                f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                           wr, goff + ((i * RSTEP) % FN / RSTEP) * rstep + kb, 0, 0));
         }
     };
-#endif
+    auto lstore = [&](const f16x8 *RA, const f16x8 *RB, int st) {
+        f16 *A_ = As + st * BM * PITCH + lds0;
+        f16 *B_ = Bs + st * WR * PITCH + lds0;
+#pragma unroll
+        for (int i = 0; i < NXL; ++i) *reinterpret_cast<f16x8 *>(A_ + i * RSTEP * PITCH) = RA[i];
+#pragma unroll
+        for (int i = 0; i < NWL; ++i) *reinterpret_cast<f16x8 *>(B_ + i * RSTEP * PITCH) = RB[i];
+    };
 
-    // This tile's K slice: steps [kz*nk, (kz+1)*nk), nk even (K is a
-    // multiple of 2*BK*ksplit).  The loop body is branch-free so the
-    // compiler's wait counts stay exact (a prefetch past the end re-reads the
-    // last step and is never used).
-    const int nk = EPI == 2 ? K / BK / a.ksplit : K / BK;
-    const int k0 = EPI == 2 ? kz * nk * BK : 0;
-#if MOE_TILED_3ST
     // Three LDS stages: step k computes from stage k%3 while the staged data
     // of step k+2 goes to stage (k+2)%3 (last read during step k-1), so the
     // first-half fragments of step k+1 (stage (k+1)%3, complete since the
@@ -193,10 +235,10 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
     // the next step's first-half reads, the staging writes and the refill
     // loads, pinned with scheduling-group barriers; one barrier per step.
     f16x8 af0[4], bf0[NM][NJ], af1[4], bf1[NM][NJ];
-    auto fread = [&](f16x8 *af, f16x8 (*bf)[NJ], int st, int ks) {
+    auto fread = [&](f16x8 *af, f16x8 (*bf)[NJ], int st, int kq) {
         const f16 *A = As + st * BM * PITCH;
         const f16 *B = Bs + st * WR * PITCH;
-        const int ch = ks + lg;
+        const int ch = kq + lg;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             af[i] = *reinterpret_cast<const f16x8 *>(A + swz(wm * 64 + i * 16 + lr, ch));
@@ -207,6 +249,7 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
                 bf[m][j] = *reinterpret_cast<const f16x8 *>(
                     B + swz(m * FN + wn * (FN / WNW) + j * 16 + lr, ch));
     };
+    f32x4 acc[NM][4][NJ];
     auto mm = [&](const f16x8 *af, f16x8 (*bf)[NJ]) {
 #pragma unroll
         for (int m = 0; m < NM; ++m)
@@ -237,82 +280,101 @@ __device__ __forceinline__ void tile_body(const StreamArgs &a, f16 *As, f16 *Bs,
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto kstep = [&](int k) { return k0 + (k < nk ? k : nk - 1) * BK; };
-    MOE_GLOAD(ra0, rb0, k0);
-    MOE_GLOAD(ra1, rb1, k0 + BK);
-    MOE_LSTORE(ra0, rb0, 0);
-    MOE_LSTORE(ra1, rb1, 1);
-    MOE_GLOAD(ra0, rb0, kstep(2));
-    __syncthreads();
-    fread(af0, bf0, 0, 0);
-    int s0 = 0, s1 = 1, s2 = 2;  // stages of steps kt, kt+1, kt+2
-    for (int kt = 0; kt < nk; kt += 2) {
-        fread(af1, bf1, s0, 4);
-        mm(af0, bf0);
-        fread(af0, bf0, s1, 0);
-        mm(af1, bf1);
-        MOE_LSTORE(ra0, rb0, s2);
-        MOE_GLOAD(ra1, rb1, kstep(kt + 3));
-        order();
-        fread(af1, bf1, s1, 4);
-        mm(af0, bf0);
-        fread(af0, bf0, s2, 0);
-        mm(af1, bf1);
-        MOE_LSTORE(ra1, rb1, s0);
-        MOE_GLOAD(ra0, rb0, kstep(kt + 4));
-        order();
-        // steps kt+2, kt+3, kt+4 sit in stages s2, s0, s1
-        const int t = s0;
-        s0 = s2;
-        s2 = s1;
-        s1 = t;
-    }
-#else
-    MOE_GLOAD(ra0, rb0, k0);
-    MOE_GLOAD(ra1, rb1, k0 + BK);
-    MOE_LSTORE(ra0, rb0, 0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-        // step kt: LDS buffer 0; refill set 0 with step kt+2; stage set 1 (kt+1)
-        MOE_GLOAD(ra0, rb0, k0 + (kt + 2 < nk ? kt + 2 : nk - 1) * BK);
-        compute(0);
-        MOE_LSTORE(ra1, rb1, 1);
-        __syncthreads();
-        // step kt+1: LDS buffer 1; refill set 1 with step kt+3; stage set 0 (kt+2)
-        MOE_GLOAD(ra1, rb1, k0 + (kt + 3 < nk ? kt + 3 : nk - 1) * BK);
-        compute(1);
-        MOE_LSTORE(ra0, rb0, 0);
-        __syncthreads();
-    }
-#endif
-#undef MOE_GLOAD
-#undef MOE_LSTORE
 
-    // ---- epilogue.  acc[m][i][j]: x row wm*64 + i*16 + 4*lg + q (q = 0..3),
-    // feature n0 + wn*FN/4 + j*16 + lr (A = x rows, B = weight rows).
+    if (seq.first >= seq.end) return;
+    int g, mt, nt, kz;
+    decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, seq.first, g, mt, nt, kz);
+    Item<NM> cur = make_item<NM, EPI, GATHER>(a, g, mt, nt, kz, nk);
+    Item<NM> nxt = cur;
+    int inext = seq.first + seq.step;
+    bool primed = false;  // the pipeline already holds this item's first steps
+    int s0 = 0, s1 = 1, s2 = 2;  // stages of steps kt, kt+1, kt+2
+    for (;;) {
+        const bool has_nxt = chain && inext < seq.end;
+        if (has_nxt) {
+            decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, inext, g, mt, nt, kz);
+            nxt = make_item<NM, EPI, GATHER>(a, g, mt, nt, kz, nk);
+        }
+        if (!primed) {
+            gload(ra0, rb0, cur, nxt, false, 0);
+            gload(ra1, rb1, cur, nxt, false, 1);
+            lstore(ra0, rb0, s0);
+            lstore(ra1, rb1, s1);
+            gload(ra0, rb0, cur, nxt, has_nxt, 2);
+            __syncthreads();
+            fread(af0, bf0, s0, 0);
+        }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = rs + wm * 64 + i * 16 + 4 * lg + q;
-            if (r >= r1) continue;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int f = n0 + wn * (FN / WNW) + j * 16 + lr;
-                if (f >= a.N) continue;
-                if (EPI == 2) {  // logits, fp32 partial of K slice kz
-                    reinterpret_cast<float *>(a.out)[(size_t)kz * a.split_stride +
-                                                     (size_t)r * a.out_ld + f] = acc[0][i][j][q];
-                } else {
-                    float v;
-                    if (EPI == 1)
-                        v = siluf_(acc[0][i][j][q]) * acc[NM - 1][i][j][q];
-                    else
-                        v = acc[0][i][j][q];
-                    reinterpret_cast<f16 *>(a.out)[(size_t)r * a.out_ld + f] = to_f16(v);
+                for (int j = 0; j < NJ; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < nk; kt += 2) {
+            fread(af1, bf1, s0, 4);
+            mm(af0, bf0);
+            fread(af0, bf0, s1, 0);
+            mm(af1, bf1);
+            lstore(ra0, rb0, s2);
+            gload(ra1, rb1, cur, nxt, has_nxt, kt + 3);
+            order();
+            fread(af1, bf1, s1, 4);
+            mm(af0, bf0);
+            fread(af0, bf0, s2, 0);
+            mm(af1, bf1);
+            lstore(ra1, rb1, s0);
+            gload(ra0, rb0, cur, nxt, has_nxt, kt + 4);
+            order();
+            // steps kt+2, kt+3, kt+4 sit in stages s2, s0, s1
+            const int t = s0;
+            s0 = s2;
+            s2 = s1;
+            s1 = t;
+        }
+
+        // ---- epilogue.  acc[m][i][j]: x row wm*64 + i*16 + 4*lg + q
+        // (q = 0..3), feature n0 + wn*FN/4 + j*16 + lr (A = x rows, B =
+        // weight rows).
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = cur.rs + wm * 64 + i * 16 + 4 * lg + q;
+                if (r >= cur.r1) continue;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int f = cur.n0 + wn * (FN / WNW) + j * 16 + lr;
+                    if (f >= a.N) continue;
+                    if (EPI == 2) {  // logits, fp32 partial of K slice kz
+                        reinterpret_cast<float *>(a.out)[(size_t)cur.kz * a.split_stride +
+                                                         (size_t)r * a.out_ld + f] =
+                            acc[0][i][j][q];
+                    } else {
+                        float v;
+                        if (EPI == 1)
+                            v = siluf_(acc[0][i][j][q]) * acc[NM - 1][i][j][q];
+                        else
+                            v = acc[0][i][j][q];
+                        reinterpret_cast<f16 *>(a.out)[(size_t)r * a.out_ld + f] = to_f16(v);
+                    }
                 }
             }
         }
+        if (!has_nxt && inext >= seq.end) break;
+        // the next item: chained (its first steps are already staged, its
+        // first fragments read) or restarted
+        primed = has_nxt;
+        if (!has_nxt) {
+            // restart: every stage is free (the last step's barrier came
+            // after every fragment read)
+            decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, inext, g, mt, nt, kz);
+            nxt = make_item<NM, EPI, GATHER>(a, g, mt, nt, kz, nk);
+            s0 = 0;
+            s1 = 1;
+            s2 = 2;
+        }
+        cur = nxt;
+        inext += seq.step;
     }
 }
 
@@ -320,7 +382,7 @@ constexpr int kMaxGroups = 1024;
 
 // Persistent: a fixed grid walks the real tiles.  Each workgroup first builds
 // the prefix of row tiles per group from the device-side offsets (group
-// sizes are only known on the device), then walks its share of the items.
+// sizes are only known on the device), then runs its share of the items.
 // Expert GEMMs (grid a multiple of the 8 XCDs, workgroups dealt to them
 // round-robin): items ordered (group, feature tile, row tile) and cut into
 // 8 contiguous ranges, one per XCD, so each XCD streams about 1/8 of the
@@ -365,46 +427,20 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
     const int ks = EPI == 2 ? a.ksplit : 1;  // K slices (logits only)
     const int total = carry * n_ntiles * ks;
 
+    ItemSeq seq;
     if (EPI != 2 && gridDim.x % 8 == 0) {
-        // Items ordered (group, feature tile, row tile); XCD x (workgroups
-        // b with b % 8 == x) takes the x-th eighth of that list, so a group's
-        // weight tiles and activation rows are fetched into one XCD's L2, and
-        // the row tiles sharing a weight tile run side by side.
         const int xcd = blockIdx.x & 7, nl = gridDim.x >> 3;
-        const int c0 = (int)((long)total * xcd / 8), c1 = (int)((long)total * (xcd + 1) / 8);
-        for (int item = c0 + (blockIdx.x >> 3); item < c1; item += nl) {
-            int lo = 0, hi = n_groups - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (tstart[mid] * n_ntiles <= item)
-                    lo = mid;
-                else
-                    hi = mid - 1;
-            }
-            const int g = lo;
-            const int tg = tstart[g + 1] - tstart[g];  // row tiles of group g
-            const int local = item - tstart[g] * n_ntiles;
-            tile_body<NM, EPI, GATHER>(a, As, Bs, g, local % tg, local / tg, 0);
-        }
-        return;
+        seq.first = (int)((long)total * xcd / 8) + (int)(blockIdx.x >> 3);
+        seq.step = nl;
+        seq.end = (int)((long)total * (xcd + 1) / 8);
+        seq.chunked = true;
+    } else {
+        seq.first = blockIdx.x;
+        seq.step = gridDim.x;
+        seq.end = total;
+        seq.chunked = false;
     }
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int kz = EPI == 2 ? item % ks : 0;
-        const int tile = item / ks / n_ntiles;
-        const int nt = (item / ks) % n_ntiles;
-        // group holding this row tile: last g with tstart[g] <= tile
-        int lo = 0, hi = n_groups - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (tstart[mid] <= tile)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        const int g = lo;
-        const int mt = tile - tstart[g];
-        tile_body<NM, EPI, GATHER>(a, As, Bs, g, mt, nt, kz);
-    }
+    run_items<NM, EPI, GATHER>(a, As, Bs, tstart, n_groups, n_ntiles, ks, seq);
 }
 
 template <int NM, int EPI, bool GATHER>
