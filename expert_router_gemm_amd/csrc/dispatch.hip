@@ -177,6 +177,11 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
     __shared__ int rslot[kSmallNnz];
     const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
     const int C = (a.T + 63) / 64;
+    const int t = tid;
+    // this token's experts, loaded while the slot table is staged
+    int ex[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) ex[k] = k < K && t < a.T ? a.topk_idx[(size_t)t * K + k] : -1;
     for (int i = tid; i < C * kSmallS; i += 1024) (&masks[0][0])[i] = 0ull;  // chunks in use
     for (int i = tid; i <= a.E; i += 1024) roff[i] = a.rep_off[i];
     const int nnz = a.rep_off[a.E];
@@ -184,16 +189,12 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
     if (table_in_lds)
         for (int i = tid; i < nnz; i += 1024) rslot[i] = a.rep_slot[i];
     __syncthreads();
-    const int t = tid;
     const unsigned long long bit = 1ull << lane;
     int sls[KMAX];  // this thread's slots, kept for the final pass
     if (t < a.T) {
-        int ex[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) ex[k] = k < K ? a.topk_idx[(size_t)t * K + k] : -1;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (k >= K) break;
+            if (k >= K) continue;  // (KT == 0) rounds past top_k
             const int e = ex[k];
             int sl = -1;
             if (e >= 0 && e < a.E) {
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
     if (t < a.T)
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (k >= K) break;
+            if (k >= K) continue;
             const size_t p = (size_t)t * K + k;
             const int sl = sls[k];
             if (sl < 0) {
