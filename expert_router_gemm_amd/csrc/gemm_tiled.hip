@@ -16,7 +16,9 @@
 // the next step's first fragments are read before the barrier, one barrier
 // per K step, XOR-swizzled LDS rows (see swz()).
 //
-// The grid is persistent (all resident workgroup slots): see tiled_gemm_kernel.
+// The grid is persistent (all resident workgroup slots): see tiled_gemm_kernel;
+// a workgroup's items share one pipeline where rows are not gathered (see
+// run_items).
 #include <atomic>
 
 #include "common.h"
@@ -25,17 +27,17 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128;    // x rows per tile
-constexpr int WNW = 4;        // waves along the weight rows (2 x 4 waves)
-constexpr int WR = 64 * WNW;  // weight rows per tile (gate + up halves for SwiGLU)
-constexpr int BK = 64;     // reduction per pipeline step
-constexpr int PITCH = BK;  // halves per LDS row (128 B, XOR-swizzled chunks)
+constexpr int BM = 128;              // x rows per tile
+constexpr int WNW = 4;               // waves along the weight rows (2 x 4 waves)
+constexpr int WR = 64 * WNW;         // weight rows per tile (gate + up halves for SwiGLU)
+constexpr int BK = 64;               // reduction per pipeline step
+constexpr int PITCH = BK;            // halves per LDS row (128 B, XOR-swizzled chunks)
 constexpr int kThreads = 128 * WNW;  // 2 x WNW waves
 constexpr int RSTEP = kThreads / 8;  // rows one staging pass covers
 constexpr int NXL = BM / RSTEP;      // x loads per thread per K step
 constexpr int NWL = WR / RSTEP;      // weight loads per thread per K step
+constexpr int NSTAGE = 3;            // LDS stages
 constexpr int kMaxDevices = 64;
-constexpr int NSTAGE = 3;  // LDS stages
 
 // LDS offset (halves) of 16-byte chunk c of row r: the chunk index is XORed
 // with r % 8, so the 16 rows one MFMA fragment read touches spread over all
