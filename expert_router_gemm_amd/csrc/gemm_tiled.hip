@@ -8,17 +8,19 @@
 //
 //   out[r][n] = epilogue( sum_k W[g][n][k] * x[r][k] )   rows r of group g
 //
-// Tile: 128 rows x 256 weight rows (128 features x gate and up for SwiGLU,
-// 256 features otherwise), BK = 64.  512 threads = 8 waves (2 per SIMD) in a
-// 2 x 4 arrangement; each wave owns 64 rows x 64 weight rows as 16 tiles of
-// v_mfma_f32_16x16x32_f16.
-// Global -> register -> LDS staging (two register sets), three LDS stages so
-// the next step's first fragments are read before the barrier, one barrier
-// per K step, XOR-swizzled LDS rows (see swz()).
+// Tiles: 256 x rows (expert GEMMs) or 128 (router) by 256 weight rows (128
+// features x gate and up for SwiGLU, 256 features otherwise), BK = 64.
+// 512 threads = 8 waves (2 per SIMD) in a 2 x 4 arrangement; each wave owns
+// TBM/2 rows x 64 weight rows as tiles of v_mfma_f32_16x16x32_f16.
+// Operands go from global memory straight into LDS (buffer/global loads with
+// the lds modifier: no register staging), two stages for 256-row tiles and
+// three for 128-row ones, one barrier per K step, XOR-swizzled LDS rows (see
+// swz()).  Building with MOE_TILED_DMA=0 selects the earlier register-staged
+// pipeline (128-row tiles only), kept for comparison.
 //
 // The grid is persistent (all resident workgroup slots): see tiled_gemm_kernel;
 // a workgroup's items share one pipeline where rows are not gathered (see
-// run_items).
+// run_items_dma).
 #include <atomic>
 
 #include "common.h"
@@ -38,6 +40,12 @@ constexpr int NXL = BM / RSTEP;      // x loads per thread per K step
 constexpr int NWL = WR / RSTEP;      // weight loads per thread per K step
 constexpr int NSTAGE = 3;            // LDS stages
 constexpr int kMaxDevices = 64;
+#ifndef MOE_TILED_DMA
+#define MOE_TILED_DMA 1
+#endif
+#ifndef MOE_TILED_EXPERT_ROWS
+#define MOE_TILED_EXPERT_ROWS 256
+#endif
 
 // LDS offset (halves) of 16-byte chunk c of row r: the chunk index is XORed
 // with r % 8, so the 16 rows one MFMA fragment read touches spread over all
@@ -52,9 +60,11 @@ struct Item {
     int rs, r1, n0, kz, k0;                // rows, features, K slice, K offset
     __amdgpu_buffer_rsrc_t xres, wres[NM];  // this tile's x rows and weight rows
     const f16 *xgat[NXL];                  // gathered x rows (GATHER)
+    const f16 *xb, *wb[NM];                // the same ranges as base and bytes
+    int xbytes, wbytes;
 };
 
-template <int NM, int EPI, bool GATHER>
+template <int NM, int EPI, bool GATHER, int TBM = BM>
 __device__ __forceinline__ Item<NM> make_item(const StreamArgs &a, int g, int mt, int nt, int kz,
                                               int nk) {
     constexpr int FN = WR / NM;  // features per tile
@@ -75,7 +85,7 @@ __device__ __forceinline__ Item<NM> make_item(const StreamArgs &a, int g, int mt
     r0 = __builtin_amdgcn_readfirstlane(r0);
     r1 = __builtin_amdgcn_readfirstlane(r1);
     Item<NM> it;
-    it.rs = r0 + mt * BM;
+    it.rs = r0 + mt * TBM;
     it.r1 = r1;
     it.n0 = nt * FN;
     it.kz = kz;
@@ -86,11 +96,11 @@ __device__ __forceinline__ Item<NM> make_item(const StreamArgs &a, int g, int mt
     // tile's valid rows fall outside the descriptor's range and load zeros,
     // so no clamping is needed; 32-bit lane offsets keep the address cost at
     // one VGPR per load.
-    const int rows_valid = (r1 - it.rs) < BM ? (r1 - it.rs) : BM;
+    const int rows_valid = (r1 - it.rs) < TBM ? (r1 - it.rs) : TBM;
     const int xrow0 = a.x_broadcast ? it.rs - r0 : it.rs;
-    it.xres = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(reinterpret_cast<const f16 *>(a.x) + (size_t)xrow0 * K), (short)0,
-        rows_valid * K * 2, 0x00020000);
+    it.xb = reinterpret_cast<const f16 *>(a.x) + (size_t)xrow0 * K;
+    it.xbytes = rows_valid * K * 2;
+    it.xres = __builtin_amdgcn_make_buffer_rsrc((void *)it.xb, (short)0, it.xbytes, 0x00020000);
     // gathered x rows (rows named by a.gather): plain global loads from the
     // row each thread moves; rows past the group repeat its last row (never
     // stored)
@@ -104,12 +114,14 @@ __device__ __forceinline__ Item<NM> make_item(const StreamArgs &a, int g, int mt
         }
     }
     const int ncols = (a.N - it.n0) < FN ? (a.N - it.n0) : FN;
+    it.wbytes = ncols * K * 2;
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-        it.wres[m] = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(reinterpret_cast<const f16 *>(m == 0 ? a.w0 : a.w1) +
-                     (size_t)g * a.w_group_stride + (size_t)it.n0 * K),
-            (short)0, ncols * K * 2, 0x00020000);
+    for (int m = 0; m < NM; ++m) {
+        it.wb[m] = reinterpret_cast<const f16 *>(m == 0 ? a.w0 : a.w1) +
+                   (size_t)g * a.w_group_stride + (size_t)it.n0 * K;
+        it.wres[m] =
+            __builtin_amdgcn_make_buffer_rsrc((void *)it.wb[m], (short)0, it.wbytes, 0x00020000);
+    }
     return it;
 }
 
@@ -380,6 +392,252 @@ __device__ __forceinline__ void run_items(const StreamArgs &a, f16 *As, f16 *Bs,
     }
 }
 
+// ---- direct global -> LDS staging (gfx950 buffer/global loads with the lds
+// modifier).  Lane l of one such load writes its 16 bytes to LDS byte
+// M0 + 16 l, so one wave instruction fills 1 KB = 8 rows of 128 B; the XOR
+// swizzle of swz() is applied on the global side (lane l of a block of 8
+// rows fetches global chunk (l % 8) ^ (l / 8) of row l / 8).  The loads are
+// issued from inline asm so that the compiler does not order every LDS read
+// behind every load in flight (it cannot tell the stages apart); completion
+// is waited for explicitly (vmcnt, in issue order) before the barrier that
+// publishes a stage.  M0 is written here and used by nothing else in these
+// kernels.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+// Raw buffer descriptor (base, byte range; stride 0) held in scalar registers.
+__device__ __forceinline__ u32x4 srd(const void *base, int bytes) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xFFFFu);
+    r[2] = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+__device__ __forceinline__ void dma_buf16(u32x4 r, uint32_t m0, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0),
+                 "v"(voff), "s"(r), "s"(soff)
+                 : "memory");
+}
+__device__ __forceinline__ void dma_glb16(const void *p, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(p)
+                 : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// The items of one workgroup with direct-to-LDS staging.  Tiles of TBM x
+// rows (128 or 256) by 256 weight rows; 8 waves in 2 (rows) x 4 (weight
+// rows), wave (wm, wn) owning TBM/2 rows x 64 weight rows.  128-row tiles use
+// three LDS stages (the loads of step k+2 issued at the start of step k),
+// 256-row tiles two (step k+1's loads issued at the start of step k; a step
+// is twice as long), so a load has about 2048 MFMA cycles to land either way.
+// Wave w stages x rows w*TBM/8..+TBM/8 and weight rows w*32..+32 of every
+// step.  A wave whose rows all lie past the group's end (the last, partly
+// filled row tile of a group) skips its fragment reads and MFMAs.  Items
+// chain (the steps past an item's end load the next item's first ones)
+// unless x rows are gathered.
+template <int TBM, int NM, int EPI, bool GATHER>
+__device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 *Bs,
+                                              const int *tstart, int n_groups, int n_ntiles,
+                                              int ks, const ItemSeq seq) {
+    constexpr int FN = WR / NM;
+    constexpr int NJ = 4 / NM;
+    constexpr int WMR = TBM / 2;           // rows per wave
+    constexpr int MI = WMR / 16;           // 16-row subtiles per wave
+    constexpr int NSTG = TBM == 128 ? 3 : 2;
+    constexpr int LOOK = NSTG - 1;         // steps loaded ahead
+    constexpr int XL = TBM / 8 / 8;        // wave loads of x rows per step (8 rows each)
+    constexpr int WL = WR / 8 / 8;         // of weight rows
+    constexpr int XW = TBM / 8;            // x rows one wave stages
+    static_assert(TBM == 128 || TBM == 256, "tile height");
+    static_assert(WL == 4, "8 waves stage 256 weight rows");
+    const int K = a.K;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WNW, wn = wave % WNW;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int nk = EPI == 2 ? K / BK / a.ksplit : K / BK;
+    const bool chain = !GATHER;
+
+    // this lane's source row within a block of 8 and its (swizzled) chunk
+    const int r8 = lane >> 3, gch = (lane & 7) ^ r8;
+    int xoff[XL], woff[WL];
+#pragma unroll
+    for (int i = 0; i < XL; ++i) xoff[i] = (wave * XW + i * 8 + r8) * K * 2 + gch * 16;
+    const int wmat = (wave * 32) / FN;  // the weight matrix this wave stages
+#pragma unroll
+    for (int i = 0; i < WL; ++i) woff[i] = ((wave * 32 + i * 8 + r8) % FN) * K * 2 + gch * 16;
+    constexpr int ASTAGE = TBM * PITCH * 2, BSTAGE = WR * PITCH * 2;  // bytes
+    const uint32_t a_m0 = lds_addr(As) + wave * XW * 128;
+    const uint32_t b_m0 = lds_addr(Bs) + wave * 32 * 128;
+
+    // gathered rows: this lane's source row of each of its x loads
+    const f16 *xg[XL];
+    auto set_gather = [&](const Item<NM> &it) {
+        if (GATHER) {
+#pragma unroll
+            for (int i = 0; i < XL; ++i) {
+                int r = it.rs + wave * XW + i * 8 + r8;
+                if (r > it.r1 - 1) r = it.r1 - 1;
+                xg[i] = reinterpret_cast<const f16 *>(a.x) +
+                        (size_t)(a.gather[r] / a.gather_div) * K + gch * 8;
+            }
+        }
+    };
+    // stage K step s of the chain into LDS stage st (steps past the current
+    // item's end: the next item's, or a harmless re-load of the last step)
+    auto stage = [&](const Item<NM> &cur, const Item<NM> &nxt, bool has_nxt, int s, int st) {
+        const bool to_nxt = s >= nk && has_nxt;
+        const int sk = s < nk ? s : (to_nxt ? s - nk : nk - 1);
+        const int kb = __builtin_amdgcn_readfirstlane(((to_nxt ? nxt.k0 : cur.k0) + sk * BK) * 2);
+        if (GATHER) {
+#pragma unroll
+            for (int i = 0; i < XL; ++i)
+                dma_glb16(xg[i] + kb / 2, a_m0 + st * ASTAGE + i * 1024);
+        } else {
+            const u32x4 xr = to_nxt ? srd(nxt.xb, nxt.xbytes) : srd(cur.xb, cur.xbytes);
+#pragma unroll
+            for (int i = 0; i < XL; ++i) dma_buf16(xr, a_m0 + st * ASTAGE + i * 1024, xoff[i], kb);
+        }
+        // (a select, not an index: a run-time index would put the items in
+        // scratch memory)
+        const f16 *wb0 = to_nxt ? nxt.wb[0] : cur.wb[0];
+        const f16 *wb1 = to_nxt ? nxt.wb[NM - 1] : cur.wb[NM - 1];
+        const u32x4 wr = srd(wmat == 0 ? wb0 : wb1, to_nxt ? nxt.wbytes : cur.wbytes);
+#pragma unroll
+        for (int i = 0; i < WL; ++i) dma_buf16(wr, b_m0 + st * BSTAGE + i * 1024, woff[i], kb);
+    };
+
+    f16x8 af0[MI], bf0[NM][NJ], af1[MI], bf1[NM][NJ];
+    auto fread = [&](f16x8 *af, f16x8 (*bf)[NJ], int st, int kq) {
+        const f16 *A = As + st * TBM * PITCH;
+        const f16 *B = Bs + st * WR * PITCH;
+        const int ch = kq + lg;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+            af[i] = *reinterpret_cast<const f16x8 *>(A + swz(wm * WMR + i * 16 + lr, ch));
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                bf[m][j] = *reinterpret_cast<const f16x8 *>(
+                    B + swz(m * FN + wn * (FN / WNW) + j * 16 + lr, ch));
+    };
+    f32x4 acc[NM][MI][NJ];
+    auto mm = [&](const f16x8 *af, f16x8 (*bf)[NJ]) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[m][i][j] = mfma16(af[i], bf[m][j], acc[m][i][j]);
+    };
+    auto next_stage = [](int st) { return st + 1 == NSTG ? 0 : st + 1; };
+
+    if (seq.first >= seq.end) return;
+    int g, mt, nt, kz;
+    decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, seq.first, g, mt, nt, kz);
+    Item<NM> cur = make_item<NM, EPI, false, TBM>(a, g, mt, nt, kz, nk);
+    Item<NM> nxt = cur;
+    int inext = seq.first + seq.step;
+    bool primed = false;
+    int sc = 0;  // stage of step kt
+    for (;;) {
+        const bool has_nxt = chain && inext < seq.end;
+        if (has_nxt) {
+            decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, inext, g, mt, nt, kz);
+            nxt = make_item<NM, EPI, false, TBM>(a, g, mt, nt, kz, nk);
+        }
+        if (!primed) {
+            set_gather(cur);
+            int st = sc;
+#pragma unroll
+            for (int j = 0; j < LOOK; ++j) {
+                stage(cur, nxt, false, j, st);
+                st = next_stage(st);
+            }
+        }
+        // wave-uniform: does this wave own any row of the tile?
+        const bool live = cur.rs + wm * WMR < cur.r1;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < nk; ++kt) {
+            // this wave's loads of step kt are in; the barrier publishes every
+            // wave's and retires the reads of step kt-1's stage, which the
+            // loads of step kt+LOOK then refill
+            wait_vm<(LOOK - 1) * (XL + WL)>();
+            __syncthreads();
+            const int sl = LOOK == 1 ? next_stage(sc) : next_stage(next_stage(sc));
+            stage(cur, nxt, has_nxt, kt + LOOK, sl);
+            if (live) {
+                // both halves' fragments, then the MFMAs (the second half's
+                // reads land during the first half's MFMAs)
+                fread(af0, bf0, sc, 0);
+                fread(af1, bf1, sc, 4);
+                mm(af0, bf0);
+                mm(af1, bf1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MI + NM * NJ), 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM * MI * NJ, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            sc = next_stage(sc);
+        }
+
+        // ---- epilogue.  acc[m][i][j]: x row wm*WMR + i*16 + 4*lg + q
+        // (q = 0..3), feature n0 + wn*FN/4 + j*16 + lr.
+        if (live) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = cur.rs + wm * WMR + i * 16 + 4 * lg + q;
+                    if (r >= cur.r1) continue;
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const int f = cur.n0 + wn * (FN / WNW) + j * 16 + lr;
+                        if (f >= a.N) continue;
+                        if (EPI == 2) {
+                            reinterpret_cast<float *>(a.out)[(size_t)cur.kz * a.split_stride +
+                                                             (size_t)r * a.out_ld + f] =
+                                acc[0][i][j][q];
+                        } else {
+                            float v;
+                            if (EPI == 1)
+                                v = siluf_(acc[0][i][j][q]) * acc[NM - 1][i][j][q];
+                            else
+                                v = acc[0][i][j][q];
+                            reinterpret_cast<f16 *>(a.out)[(size_t)r * a.out_ld + f] = to_f16(v);
+                        }
+                    }
+                }
+            }
+        }
+        if (!has_nxt && inext >= seq.end) break;
+        primed = has_nxt;
+        if (!has_nxt) {
+            // restart: let the dummy loads land and every wave finish reading
+            // before the stages are refilled
+            wait_vm<0>();
+            __syncthreads();
+            decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, inext, g, mt, nt, kz);
+            nxt = make_item<NM, EPI, false, TBM>(a, g, mt, nt, kz, nk);
+            sc = 0;
+        }
+        cur = nxt;
+        inext += seq.step;
+    }
+    wait_vm<0>();
+}
+
 constexpr int kMaxGroups = 1024;
 
 // Persistent: a fixed grid walks the real tiles.  Each workgroup first builds
@@ -393,12 +651,21 @@ constexpr int kMaxGroups = 1024;
 // items round-robin, measured on the 16384-token prefill).  Router logits
 // (K slices) and small grids: item w, w + G, ... of (row tile, feature
 // tile[, K slice]).
-template <int NM, int EPI, bool GATHER>
+template <int TBM>
+constexpr int n_stages() {
+    return MOE_TILED_DMA && TBM == 256 ? 2 : NSTAGE;
+}
+template <int TBM>
+constexpr size_t tile_lds_bytes() {
+    return (size_t)n_stages<TBM>() * (TBM + WR) * PITCH * sizeof(f16);
+}
+
+template <int TBM, int NM, int EPI, bool GATHER>
 __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int n_ntiles,
                                                               int n_groups) {
     extern __shared__ __attribute__((aligned(16))) f16 lds[];
-    f16 *As = lds;                          // [NSTAGE][BM][PITCH]
-    f16 *Bs = lds + NSTAGE * BM * PITCH;    // [NSTAGE][WR][PITCH]
+    f16 *As = lds;                                    // [stages][TBM][PITCH]
+    f16 *Bs = lds + n_stages<TBM>() * TBM * PITCH;    // [stages][WR][PITCH]
     __shared__ int tstart[kMaxGroups + 1];  // first row tile of each group
     __shared__ int scan[2][kThreads];
 
@@ -410,7 +677,7 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
         int nt_g = 0;
         if (g < n_groups) {
             int rows = a.offsets ? a.offsets[g + 1] - a.offsets[g] : a.rows_per_group;
-            nt_g = rows > 0 ? (rows + BM - 1) / BM : 0;
+            nt_g = rows > 0 ? (rows + TBM - 1) / TBM : 0;
         }
         int cur = 0;
         scan[0][tid] = nt_g;
@@ -442,14 +709,21 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
         seq.end = total;
         seq.chunked = false;
     }
+#if MOE_TILED_DMA
+    run_items_dma<TBM, NM, EPI, GATHER>(a, As, Bs, tstart, n_groups, n_ntiles, ks, seq);
+#else
+    static_assert(TBM == BM, "register staging uses 128-row tiles");
     run_items<NM, EPI, GATHER>(a, As, Bs, tstart, n_groups, n_ntiles, ks, seq);
+#endif
 }
 
-template <int NM, int EPI, bool GATHER>
+// max_tiles bounds the 128-row tiles (so also the taller ones): it only
+// sizes the grid, surplus workgroups find no item and exit.
+template <int TBM, int NM, int EPI, bool GATHER>
 hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream_t s) {
     if (n_groups <= 0 || n_groups > kMaxGroups) return hipErrorInvalidValue;
     const int n_ntiles = (a.N + WR / NM - 1) / (WR / NM);
-    const size_t lds = (size_t)NSTAGE * (BM + WR) * PITCH * sizeof(f16);
+    const size_t lds = tile_lds_bytes<TBM>();
     // Per device, once: allow the dynamic LDS size and count the workgroups
     // that are resident at once (cached; a race only repeats the queries).
     static std::atomic<int> resident[kMaxDevices];
@@ -457,13 +731,13 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
     int slots = dev < kMaxDevices ? resident[dev].load(std::memory_order_relaxed) : 0;
     if (slots <= 0) {
-        hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<NM, EPI, GATHER>,
+        hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<TBM, NM, EPI, GATHER>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         int cus = 256, per_cu = 1;
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, tiled_gemm_kernel<NM, EPI, GATHER>, kThreads, lds) != hipSuccess ||
+                &per_cu, tiled_gemm_kernel<TBM, NM, EPI, GATHER>, kThreads, lds) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
         slots = cus * per_cu;
@@ -473,7 +747,7 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
     long grid = slots;
     const long items = max_tiles * n_ntiles * (EPI == 2 ? a.ksplit : 1);
     if (items < grid) grid = items > 0 ? items : 1;
-    hipLaunchKernelGGL((tiled_gemm_kernel<NM, EPI, GATHER>), dim3((unsigned)grid), dim3(kThreads),
+    hipLaunchKernelGGL((tiled_gemm_kernel<TBM, NM, EPI, GATHER>), dim3((unsigned)grid), dim3(kThreads),
                        lds, s, a, n_ntiles, n_groups);
     return hipGetLastError();
 }
@@ -491,11 +765,12 @@ bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype) {
 
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,
                              hipStream_t s) {
+    constexpr int XB = MOE_TILED_DMA ? MOE_TILED_EXPERT_ROWS : BM;  // expert GEMM tile rows
     if (mode == STREAM_SWIGLU)
-        return a.gather ? launch_t<2, 1, true>(a, n_groups, max_tiles, s)
-                        : launch_t<2, 1, false>(a, n_groups, max_tiles, s);
-    if (mode == STREAM_STORE) return launch_t<1, 0, false>(a, n_groups, max_tiles, s);
-    return launch_t<1, 2, false>(a, n_groups, max_tiles, s);
+        return a.gather ? launch_t<XB, 2, 1, true>(a, n_groups, max_tiles, s)
+                        : launch_t<XB, 2, 1, false>(a, n_groups, max_tiles, s);
+    if (mode == STREAM_STORE) return launch_t<XB, 1, 0, false>(a, n_groups, max_tiles, s);
+    return launch_t<BM, 1, 2, false>(a, n_groups, max_tiles, s);
 }
 
 }  // namespace moe
