@@ -36,18 +36,34 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
-KERNEL_SOURCES = ["expert_router_gemm_amd/csrc/gemm_stream.hip",
-                  "expert_router_gemm_amd/csrc/common.h",
-                  "expert_router_gemm_amd/csrc/kernels.h"]
-DOMINANT = "stream_gemm_kernel"  # + the SwiGLU epilogue template argument
+# The dominant kernel of a workload: the gate/up weight stream at decode
+# sizes, the LDS-tiled gate/up GEMM (256-row tiles, rows gathered) at prefill.
+# Its HBM traffic record is keyed by a hash of the sources it is built from.
+KERNEL_SOURCES = {
+    "stream": ["expert_router_gemm_amd/csrc/gemm_stream.hip",
+               "expert_router_gemm_amd/csrc/common.h",
+               "expert_router_gemm_amd/csrc/kernels.h"],
+    "tiled": ["expert_router_gemm_amd/csrc/gemm_tiled.hip",
+              "expert_router_gemm_amd/csrc/common.h",
+              "expert_router_gemm_amd/csrc/kernels.h"],
+}
+DOMINANT = {"stream": "stream_gemm_kernel", "tiled": "tiled_gemm_kernel"}
 
 
-def kernel_source_hash() -> str:
+def dominant_kind(workload: int) -> str:
+    return "tiled" if workload == 4 else "stream"
+
+
+def kernel_source_hash(kind: str = "stream") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def traffic_path(kind: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{kind}_gemm_swiglu_{workload}.json")
 
 
 def log(msg):
@@ -206,15 +222,15 @@ def algorithmic_work(ctx):
                 layer_flops=up["flops"] + down["flops"] + route["flops"] + shared["flops"])
 
 
-def load_traffic(workload: str):
+def load_traffic(kind: str, workload: str):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 PMC record, if it was taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", f"traffic_stream_gemm_swiglu_{workload}.json")
+    p = traffic_path(kind, workload)
     if not os.path.exists(p):
         return None
     with open(p) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -302,12 +318,17 @@ def cpu_baseline(ctx, budget_s: float = 20.0):
 # ------------------------------------------------------------------ PMC summary
 
 
-def is_swiglu_stream(kernel_name: str) -> bool:
-    """The gate/up launch of the stream GEMM: template arguments
-    <TW, XM, NSUB, EPI, KW, U> with EPI = SwiGLU (1), demangled or mangled."""
+def is_dominant(kernel_name: str, kind: str) -> bool:
+    """The gate/up launch of the dominant kernel, demangled or mangled.
+    Stream GEMM: template arguments <TW, XM, NSUB, EPI, KW, U> with EPI =
+    SwiGLU (1).  Tiled GEMM: <TBM, NM, EPI, GATHER> = <256, 2, 1, true>."""
     import re
-    if DOMINANT not in kernel_name:
+    if DOMINANT[kind] not in kernel_name:
         return False
+    if kind == "tiled":
+        n = kernel_name.replace(" ", "")
+        return ("tiled_gemm_kernel<256,2,1,true>" in n
+                or "tiled_gemm_kernelILi256ELi2ELi1ELb1E" in n)
     n = kernel_name.replace(" ", "")
     m = re.search(r"stream_gemm_kernel<[^,]+,(\d+),(\d+),(\d+),", n)
     if m:
@@ -316,7 +337,7 @@ def is_swiglu_stream(kernel_name: str) -> bool:
     return bool(m) and m.group(3) == "1"
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int):
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, kind: str):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant
     kernel, each scaled by what the counter reads for the calibration copy
     kernel of known size; writes profiles/traffic_...json."""
@@ -333,7 +354,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int
                 continue
             name = r.get("Kernel_Name", "")
             v = float(r["Counter_Value"])
-            if is_swiglu_stream(name):
+            if is_dominant(name, kind):
                 dom.append(v)
             elif "AUnaryFunctor" in name and "MulFunctor" in name:  # the calibration copy
                 cp.append(v)
@@ -349,15 +370,16 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int
         out[counter] = dict(kib_per_launch=statistics.median(dom), copy_kib=statistics.median(cp),
                             copy_factor=factor,
                             bytes_per_launch=statistics.median(dom) * 1024.0 * factor)
-    rec = dict(kernel=f"{DOMINANT} (SwiGLU gate/up weight stream)", workload=workload,
-               kernel_source_hash=kernel_source_hash(), counters=out,
+    what = "SwiGLU gate/up weight stream" if kind == "stream" else "SwiGLU gate/up, gathered rows"
+    rec = dict(kernel=f"{DOMINANT[kind]} ({what})", workload=workload,
+               kernel_source_hash=kernel_source_hash(kind), counters=out,
                traffic_bytes_per_launch=out["FETCH_SIZE"]["bytes_per_launch"]
                + out["WRITE_SIZE"]["bytes_per_launch"])
     rec["command"] = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv "
                       "-d DIR -o run -- python3 bench.py --workload N --steps 3 --warmup 1 "
                       "--no-cpu-baseline --copy-calibration; python3 bench.py --summarize-pmc "
                       "FETCH_DIR WRITE_DIR --workload N")
-    p = os.path.join(ROOT, "profiles", f"traffic_stream_gemm_swiglu_{workload}.json")
+    p = traffic_path(kind, workload)
     with open(p, "w") as f:
         json.dump(rec, f, indent=2)
     print(json.dumps(rec, indent=2))
@@ -386,7 +408,8 @@ def main():
 
     if args.summarize_pmc:
         import moe_synth
-        summarize_pmc(*args.summarize_pmc, moe_synth.config(args.workload).name, 1 << 30)
+        summarize_pmc(*args.summarize_pmc, moe_synth.config(args.workload).name, 1 << 30,
+                      dominant_kind(args.workload))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
@@ -460,12 +483,13 @@ def main():
     if decode:
         achieved = work["up"]["bytes"] / (up_ms / 1e3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=load_traffic(cfg.name))
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=load_traffic("stream", cfg.name))
     else:
         achieved = work["up"]["flops"] / (up_ms / 1e3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_F16_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                    traffic=load_traffic(cfg.name))
+                    traffic=load_traffic("tiled", cfg.name))
     roof.update(kernel=("stream_gemm_kernel" if decode else "tiled_gemm_kernel") +
                 " (SwiGLU gate/up, in moe_layer_forward)", launch_ms=round(up_ms, 4),
                 algorithmic_bytes=work["up"]["bytes"], algorithmic_flops=work["up"]["flops"])

@@ -392,6 +392,13 @@ __device__ __forceinline__ void run_items(const StreamArgs &a, f16 *As, f16 *Bs,
     }
 }
 
+// Tile geometry of the direct-to-LDS pipeline: K steps of BK, two LDS
+// stages of 64 KB for 256-row tiles, three of 48 KB for 128-row ones.
+template <int TBM>
+constexpr int n_stages() {
+    return MOE_TILED_DMA && TBM == 256 ? 2 : NSTAGE;
+}
+
 // ---- direct global -> LDS staging (gfx950 buffer/global loads with the lds
 // modifier).  Lane l of one such load writes its 16 bytes to LDS byte
 // M0 + 16 l, so one wave instruction fills 1 KB = 8 rows of 128 B; the XOR
@@ -449,13 +456,14 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
     constexpr int NJ = 4 / NM;
     constexpr int WMR = TBM / 2;           // rows per wave
     constexpr int MI = WMR / 16;           // 16-row subtiles per wave
-    constexpr int NSTG = TBM == 128 ? 3 : 2;
+    constexpr int NSTG = n_stages<TBM>();
     constexpr int LOOK = NSTG - 1;         // steps loaded ahead
-    constexpr int XL = TBM / 8 / 8;        // wave loads of x rows per step (8 rows each)
-    constexpr int WL = WR / 8 / 8;         // of weight rows
+    constexpr int CPR = BK / 8;            // 16-byte chunks per LDS row
+    constexpr int RPI = 64 / CPR;          // rows one wave load fills (1 KB)
     constexpr int XW = TBM / 8;            // x rows one wave stages
+    constexpr int XL = XW / RPI;           // wave loads of x rows per step
+    constexpr int WL = 32 / RPI;           // of weight rows (32 per wave)
     static_assert(TBM == 128 || TBM == 256, "tile height");
-    static_assert(WL == 4, "8 waves stage 256 weight rows");
     const int K = a.K;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -464,17 +472,20 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
     const int nk = EPI == 2 ? K / BK / a.ksplit : K / BK;
     const bool chain = !GATHER;
 
-    // this lane's source row within a block of 8 and its (swizzled) chunk
-    const int r8 = lane >> 3, gch = (lane & 7) ^ r8;
+    // this lane's source row within the block one wave load fills and its
+    // (swizzled) chunk: the row's swizzle key depends only on its offset in
+    // the block
+    const int rsub = lane / CPR, gch = (lane % CPR) ^ (rsub & 7);
     int xoff[XL], woff[WL];
 #pragma unroll
-    for (int i = 0; i < XL; ++i) xoff[i] = (wave * XW + i * 8 + r8) * K * 2 + gch * 16;
+    for (int i = 0; i < XL; ++i) xoff[i] = (wave * XW + i * RPI + rsub) * K * 2 + gch * 16;
     const int wmat = (wave * 32) / FN;  // the weight matrix this wave stages
 #pragma unroll
-    for (int i = 0; i < WL; ++i) woff[i] = ((wave * 32 + i * 8 + r8) % FN) * K * 2 + gch * 16;
-    constexpr int ASTAGE = TBM * PITCH * 2, BSTAGE = WR * PITCH * 2;  // bytes
-    const uint32_t a_m0 = lds_addr(As) + wave * XW * 128;
-    const uint32_t b_m0 = lds_addr(Bs) + wave * 32 * 128;
+    for (int i = 0; i < WL; ++i)
+        woff[i] = ((wave * 32 + i * RPI + rsub) % FN) * K * 2 + gch * 16;
+    constexpr int ASTAGE = TBM * BK * 2, BSTAGE = WR * BK * 2;  // bytes
+    const uint32_t a_m0 = lds_addr(As) + wave * XW * BK * 2;
+    const uint32_t b_m0 = lds_addr(Bs) + wave * 32 * BK * 2;
 
     // gathered rows: this lane's source row of each of its x loads
     const f16 *xg[XL];
@@ -482,7 +493,7 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
         if (GATHER) {
 #pragma unroll
             for (int i = 0; i < XL; ++i) {
-                int r = it.rs + wave * XW + i * 8 + r8;
+                int r = it.rs + wave * XW + i * RPI + rsub;
                 if (r > it.r1 - 1) r = it.r1 - 1;
                 xg[i] = reinterpret_cast<const f16 *>(a.x) +
                         (size_t)(a.gather[r] / a.gather_div) * K + gch * 8;
@@ -513,35 +524,81 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
         for (int i = 0; i < WL; ++i) dma_buf16(wr, b_m0 + st * BSTAGE + i * 1024, woff[i], kb);
     };
 
+    // Fragment reads: the weight fragments first, then the row fragments in
+    // the order the MFMAs consume them (row subtile outer), so a wave's first
+    // MFMA waits for NM*NJ + 1 reads and each later row fragment feeds NM*NJ
+    // MFMAs.
     f16x8 af0[MI], bf0[NM][NJ], af1[MI], bf1[NM][NJ];
+    // (scheduling barriers keep the compiler from moving the row reads ahead)
     auto fread = [&](f16x8 *af, f16x8 (*bf)[NJ], int st, int kq) {
-        const f16 *A = As + st * TBM * PITCH;
-        const f16 *B = Bs + st * WR * PITCH;
+        const f16 *A = As + st * TBM * BK;
+        const f16 *B = Bs + st * WR * BK;
         const int ch = kq + lg;
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-            af[i] = *reinterpret_cast<const f16x8 *>(A + swz(wm * WMR + i * 16 + lr, ch));
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
                 bf[m][j] = *reinterpret_cast<const f16x8 *>(
                     B + swz(m * FN + wn * (FN / WNW) + j * 16 + lr, ch));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+            af[i] = *reinterpret_cast<const f16x8 *>(A + swz(wm * WMR + i * 16 + lr, ch));
+        __builtin_amdgcn_sched_barrier(0);
     };
     f32x4 acc[NM][MI][NJ];
-    auto mm = [&](const f16x8 *af, f16x8 (*bf)[NJ]) {
+    // MFMAs of row subtiles [i0, i1)
+    auto mm = [&](const f16x8 *af, f16x8 (*bf)[NJ], int i0, int i1) {
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[m][i][j] = mfma16(af[i], bf[m][j], acc[m][i][j]);
+    };
+    auto next_stage = [](int st) { return st + 1 == NSTG ? 0 : st + 1; };
+    auto zero_acc = [&]() {
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[m][i][j] = mfma16(af[i], bf[m][j], acc[m][i][j]);
+                for (int j = 0; j < NJ; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    auto next_stage = [](int st) { return st + 1 == NSTG ? 0 : st + 1; };
+    // acc[m][i][j]: x row wm*WMR + i*16 + 4*lg + q (q = 0..3), feature
+    // n0 + wn*FN/4 + j*16 + lr.
+    auto epilogue = [&](const Item<NM> &it) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = it.rs + wm * WMR + i * 16 + 4 * lg + q;
+                if (r >= it.r1) continue;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int f = it.n0 + wn * (FN / WNW) + j * 16 + lr;
+                    if (f >= a.N) continue;
+                    if (EPI == 2) {
+                        reinterpret_cast<float *>(a.out)[(size_t)it.kz * a.split_stride +
+                                                         (size_t)r * a.out_ld + f] =
+                            acc[0][i][j][q];
+                    } else {
+                        float v;
+                        if (EPI == 1)
+                            v = siluf_(acc[0][i][j][q]) * acc[NM - 1][i][j][q];
+                        else
+                            v = acc[0][i][j][q];
+                        reinterpret_cast<f16 *>(a.out)[(size_t)r * a.out_ld + f] = to_f16(v);
+                    }
+                }
+            }
+        }
+    };
 
     if (seq.first >= seq.end) return;
     int g, mt, nt, kz;
     decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, seq.first, g, mt, nt, kz);
+
     Item<NM> cur = make_item<NM, EPI, false, TBM>(a, g, mt, nt, kz, nk);
     Item<NM> nxt = cur;
     int inext = seq.first + seq.step;
@@ -564,63 +621,32 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
         }
         // wave-uniform: does this wave own any row of the tile?
         const bool live = cur.rs + wm * WMR < cur.r1;
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        zero_acc();
         for (int kt = 0; kt < nk; ++kt) {
             // this wave's loads of step kt are in; the barrier publishes every
             // wave's and retires the reads of step kt-1's stage, which the
             // loads of step kt+LOOK then refill
             wait_vm<(LOOK - 1) * (XL + WL)>();
             __syncthreads();
-            const int sl = LOOK == 1 ? next_stage(sc) : next_stage(next_stage(sc));
+            const int sl = sc + LOOK < NSTG ? sc + LOOK : sc + LOOK - NSTG;
             stage(cur, nxt, has_nxt, kt + LOOK, sl);
             if (live) {
-                // both halves' fragments, then the MFMAs (the second half's
-                // reads land during the first half's MFMAs)
+                // the first K half's fragments, half of its MFMAs, the second
+                // half's fragments (landing during the rest), the remaining
+                // MFMAs: at most 2*(MI + NM*NJ) reads in flight and no MFMA
+                // waits for more than the first NM*NJ + 1 of them (the LDS
+                // counter holds 15)
                 fread(af0, bf0, sc, 0);
+                mm(af0, bf0, 0, MI / 2);
                 fread(af1, bf1, sc, 4);
-                mm(af0, bf0);
-                mm(af1, bf1);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MI + NM * NJ), 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM * MI * NJ, 0);
+                mm(af0, bf0, MI / 2, MI);
+                mm(af1, bf1, 0, MI);
                 __builtin_amdgcn_sched_barrier(0);
             }
             sc = next_stage(sc);
         }
 
-        // ---- epilogue.  acc[m][i][j]: x row wm*WMR + i*16 + 4*lg + q
-        // (q = 0..3), feature n0 + wn*FN/4 + j*16 + lr.
-        if (live) {
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = cur.rs + wm * WMR + i * 16 + 4 * lg + q;
-                    if (r >= cur.r1) continue;
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const int f = cur.n0 + wn * (FN / WNW) + j * 16 + lr;
-                        if (f >= a.N) continue;
-                        if (EPI == 2) {
-                            reinterpret_cast<float *>(a.out)[(size_t)cur.kz * a.split_stride +
-                                                             (size_t)r * a.out_ld + f] =
-                                acc[0][i][j][q];
-                        } else {
-                            float v;
-                            if (EPI == 1)
-                                v = siluf_(acc[0][i][j][q]) * acc[NM - 1][i][j][q];
-                            else
-                                v = acc[0][i][j][q];
-                            reinterpret_cast<f16 *>(a.out)[(size_t)r * a.out_ld + f] = to_f16(v);
-                        }
-                    }
-                }
-            }
-        }
+        if (live) epilogue(cur);
         if (!has_nxt && inext >= seq.end) break;
         primed = has_nxt;
         if (!has_nxt) {
@@ -652,20 +678,16 @@ constexpr int kMaxGroups = 1024;
 // (K slices) and small grids: item w, w + G, ... of (row tile, feature
 // tile[, K slice]).
 template <int TBM>
-constexpr int n_stages() {
-    return MOE_TILED_DMA && TBM == 256 ? 2 : NSTAGE;
-}
-template <int TBM>
 constexpr size_t tile_lds_bytes() {
-    return (size_t)n_stages<TBM>() * (TBM + WR) * PITCH * sizeof(f16);
+    return (size_t)n_stages<TBM>() * (TBM + WR) * BK * sizeof(f16);
 }
 
 template <int TBM, int NM, int EPI, bool GATHER>
 __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int n_ntiles,
                                                               int n_groups) {
     extern __shared__ __attribute__((aligned(16))) f16 lds[];
-    f16 *As = lds;                                    // [stages][TBM][PITCH]
-    f16 *Bs = lds + n_stages<TBM>() * TBM * PITCH;    // [stages][WR][PITCH]
+    f16 *As = lds;                                           // [stages][TBM][BK]
+    f16 *Bs = lds + n_stages<TBM>() * TBM * BK;              // [stages][WR][BK]
     __shared__ int tstart[kMaxGroups + 1];  // first row tile of each group
     __shared__ int scan[2][kThreads];
 
@@ -770,7 +792,8 @@ hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long m
         return a.gather ? launch_t<XB, 2, 1, true>(a, n_groups, max_tiles, s)
                         : launch_t<XB, 2, 1, false>(a, n_groups, max_tiles, s);
     if (mode == STREAM_STORE) return launch_t<XB, 1, 0, false>(a, n_groups, max_tiles, s);
-    return launch_t<BM, 1, 2, false>(a, n_groups, max_tiles, s);
+    constexpr int RB = MOE_TILED_DMA ? MOE_TILED_ROUTER_ROWS : BM;  // router tile rows
+    return launch_t<RB, 1, 2, false>(a, n_groups, max_tiles, s);
 }
 
 }  // namespace moe

@@ -44,8 +44,12 @@ struct StreamArgs {
 hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int mode,
                               int n_groups, int zblocks, long est_rows, hipStream_t s);
 
-// LDS-tiled persistent variant for groups of many rows (fp16 only, no K
-// split).  max_tiles bounds the total 128-row tiles (sizes the grid).
+// LDS-tiled persistent variant for groups of many rows (fp16 only; K split
+// for router logits).  max_tiles bounds the total 128-row tiles (sizes the
+// grid).  Router logits use tiles of MOE_TILED_ROUTER_ROWS rows.
+#ifndef MOE_TILED_ROUTER_ROWS
+#define MOE_TILED_ROUTER_ROWS 128
+#endif
 bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype);
 bool tiled_gemm_supported_shape(int K, int dtype, int x_dtype);
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,

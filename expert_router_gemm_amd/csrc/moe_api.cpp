@@ -50,7 +50,8 @@ RouterPlan router_plan(const moe_shape &s, int T) {
     const int N = s.n_experts + has_gate(s);
     RouterPlan p;
     p.tiled = T >= MOE_ROUTER_TILED_MIN_T && tiled_gemm_supported_shape(s.hidden, s.act, s.act);
-    const long base = p.tiled ? (long)((N + 255) / 256) * ((T + 127) / 128)
+    const int tr = MOE_TILED_ROUTER_ROWS;
+    const long base = p.tiled ? (long)((N + 255) / 256) * ((T + tr - 1) / tr)
                               : (long)((N + 63) / 64) * ((T + 63) / 64);
     // fp16 stream path: K slices that are multiples of 512 let the 4 waves of
     // a block split each slice (see launch_stream_gemm); other sizes fall
