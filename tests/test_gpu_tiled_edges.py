@@ -1,0 +1,89 @@
+"""Expert GEMMs on the LDS-tiled kernel at group sizes on the tile edges,
+called through libmoe's C ABI (moe_expert_ffn_up, moe_expert_ffn_down) and
+compared with the oracle's SwiGLU expert (EP blog section 2.2, Step 3).
+
+Groups of 0, 1, 127, 128, 129, 255, 256, 257, 300 and 513 rows: empty
+groups, 256-row tiles whose second row half is empty (those waves skip
+their fragment reads and MFMAs), exact tile multiples and one-row tails.
+The x rows are read three ways: already permuted, gathered through a row
+index (as the gate/up GEMM gathers h through perm_src; direct-to-LDS loads
+from per-lane addresses) and shared (every group reads the same rows, as
+the shared experts do).  H = 512 (the down projection's output spans two
+256-feature tiles), I = 384 (gate/up: three tiles of 128 features).
+
+Bar: |gpu - ref| <= 2e-3 + 2e-2 |ref| on hm and y (fp16 outputs, fp32
+accumulation); rows past the last group are never written.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+gh = pytest.importorskip("gpu_harness")
+moe = pytest.importorskip("expert_router_gemm_amd")
+
+SIZES = [0, 1, 127, 128, 129, 255, 256, 257, 300, 513]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+@pytest.mark.parametrize("x_rows", ["permuted", "gather", "shared"])
+def test_tiled_expert_gemms_at_tile_edges(x_rows):
+    cfg = moe_synth.scaled_config(4, T=sum(SIZES), H=512, I=384, seed=41)
+    G = len(SIZES)
+    offsets = np.concatenate([[0], np.cumsum(SIZES)]).astype(np.int32)
+    P = int(offsets[-1])
+    experts = [moe_synth.gen_expert(cfg, e) for e in range(G)]
+    wg = np.stack([e[0] for e in experts])
+    wu = np.stack([e[1] for e in experts])
+    wd = np.stack([e[2] for e in experts])
+    if x_rows == "shared":
+        x = moe_synth.gen_hidden(cfg, T=max(SIZES))
+        src = np.concatenate([np.arange(n) for n in SIZES]).astype(np.int64)
+        gather = None
+        mode = moe.MOE_X_SHARED
+    elif x_rows == "gather":
+        x = moe_synth.gen_hidden(cfg, T=P + 7)
+        src = np.random.default_rng(41).permutation(P + 7)[:P].astype(np.int64)
+        gather = src.astype(np.int32)  # top_k = 1: x row = gather[r]
+        mode = moe.MOE_X_GATHER
+    else:
+        x = moe_synth.gen_hidden(cfg, T=P)
+        src = np.arange(P, dtype=np.int64)
+        gather = None
+        mode = moe.MOE_X_PERMUTED
+
+    # est. rows per group (cap_rows / n_experts) >= 64 selects the tiled kernel
+    shape = moe.make_shape(hidden=cfg.H, inter=cfg.I, n_experts=G, top_k=1, n_slots=G)
+    cap = P + 64  # rows past the last group stay untouched
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    xd, wgd, wud, wdd, offd = d(x), d(wg), d(wu), d(wd), d(offsets)
+    gd = d(gather) if gather is not None else None
+    sentinel = torch.tensor(12345.0, dtype=torch.float16)
+    hm = torch.full((cap, cfg.I), sentinel.item(), dtype=torch.float16, device="cuda")
+    y = torch.full((cap, cfg.H), sentinel.item(), dtype=torch.float16, device="cuda")
+    print(f"[tiled edges] x_rows={x_rows} groups={SIZES} P={P}", flush=True)
+    moe.moe_expert_ffn_up(shape, G, cap, xd, moe.MOE_F16, None, mode, gd, offd, wgd, wud, hm)
+    moe.moe_expert_ffn_down(shape, G, cap, hm, offd, wdd, y)
+    torch.cuda.synchronize()
+    hm_g, y_g = hm.cpu().numpy(), y.cpu().numpy()
+
+    for g in range(G):
+        a, b = offsets[g], offsets[g + 1]
+        if a == b:
+            continue
+        rows = x[src[a:b]].astype(np.float64)
+        y_ref, hm_ref = oracle.expert_rows(rows, wg[g], wu[g], wd[g], want_hm=True)
+        gh.assert_close(hm_g[a:b], hm_ref, f"hm group {g} ({b - a} rows)")
+        gh.assert_close(y_g[a:b], y_ref, f"y group {g} ({b - a} rows)")
+    assert np.all(hm_g[P:] == sentinel.numpy()), "hm rows past the groups were written"
+    assert np.all(y_g[P:] == sentinel.numpy()), "y rows past the groups were written"
