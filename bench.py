@@ -412,8 +412,9 @@ def main():
                       dominant_kind(args.workload))
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
-              f"--gpus {args.gpus}); see the sharding note in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU: expert parallelism across GPUs (the all-to-all "
+              f"dispatch and combine) is not implemented (asked for --gpus {args.gpus})",
+              file=sys.stderr)
         return 2
 
     import torch

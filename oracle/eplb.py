@@ -13,7 +13,7 @@ stopping) and 6.3 (redundant experts), read for one EP group:
                 stays where it is
   4. cleanup:   optional on the page; not modelled
 
-Readings taken where the page leaves a step open (also listed in the design doc):
+Readings taken where the page leaves a step open:
   * the window counts forwards, not milliseconds: the last W observed
     per-forward histograms are summed;
   * a token routed to an expert with n copies goes to each copy with
