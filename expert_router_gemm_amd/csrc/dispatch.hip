@@ -157,6 +157,65 @@ __global__ __launch_bounds__(256) void dispatch_index_kernel(DispatchArgs a) {
     a.perm_src[row] = (int32_t)p;
 }
 
+// Large batches with a small (chunk, slot) table (S <= 256, C*S <= 64K):
+// the scan and the index outputs in one launch, one block per chunk of 64
+// tokens.  Each block re-derives, from the per-chunk counts, every slot's
+// total and the rows its slot holds in earlier chunks (integer sums, so
+// the order of the LDS atomics does not matter), scans the totals into
+// slot offsets, and places its own pairs; block 0 writes counts and
+// offsets.  Replaces dispatch_scan_kernel's single block and a launch.
+constexpr int kPlaceMaxS = 256, kPlaceMaxTable = 65536;
+
+__global__ __launch_bounds__(256) void dispatch_place_kernel(DispatchArgs a) {
+    __shared__ int tot[kPlaceMaxS], before[kPlaceMaxS], scan[2][kPlaceMaxS];
+    const int tid = threadIdx.x, c = blockIdx.x, S = a.S;
+    const int C = (a.T + 63) / 64;
+    if (tid < S) {
+        tot[tid] = 0;
+        before[tid] = 0;
+    }
+    __syncthreads();
+    const int n = C * S;
+    for (int i = tid; i < n; i += 256) {
+        const int v = a.chunk_counts[i];
+        const int sl = i % S;
+        atomicAdd(&tot[sl], v);
+        if (i / S < c) atomicAdd(&before[sl], v);
+    }
+    __syncthreads();
+    // inclusive scan of the slot totals (entries past S are 0)
+    int cur = 0;
+    scan[0][tid] = tid < S ? tot[tid] : 0;
+    __syncthreads();
+    for (int o = 1; o < kPlaceMaxS; o <<= 1) {
+        scan[cur ^ 1][tid] = scan[cur][tid] + (tid >= o ? scan[cur][tid - o] : 0);
+        cur ^= 1;
+        __syncthreads();
+    }
+    if (tid < S) {
+        const int off = scan[cur][tid] - tot[tid];
+        before[tid] += off;  // absolute first row of this chunk's pairs in slot tid
+        if (c == 0) {
+            a.counts[tid] = tot[tid];
+            a.offsets[tid] = off;
+            if (tid == S - 1) a.offsets[S] = scan[cur][tid];
+        }
+    }
+    __syncthreads();
+    const size_t p0 = (size_t)c * 64 * a.K;
+    const size_t p1 = (size_t)min(a.T, (c + 1) * 64) * a.K;
+    for (size_t p = p0 + tid; p < p1; p += 256) {
+        const int code = a.pair_code[p];
+        if (code < 0) {
+            a.inv_pos[p] = -1;
+            continue;
+        }
+        const int row = before[code >> 6] + (code & 63);
+        a.inv_pos[p] = row;
+        a.perm_src[row] = (int32_t)p;
+    }
+}
+
 // Decode-sized batches (T <= 1024, S <= 256): rank, scan and the index
 // outputs in one block of 1024 threads; wave w owns tokens [64w, 64w + 64).
 constexpr int kSmallT = 1024, kSmallS = 256;
@@ -454,6 +513,12 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
                            (size_t)4 * a.S * sizeof(unsigned long long), s, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    if (C > 0 && a.S <= kPlaceMaxS && (long)C * a.S <= kPlaceMaxTable) {
+        hipLaunchKernelGGL(dispatch_place_kernel, dim3(C), dim3(256), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess || !a.x_perm) return e;
+        return launch_rows(a, s);
     }
     // with T = 0 the scan alone writes all-zero counts and offsets
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, a);
