@@ -60,15 +60,19 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchArgs a) {
     __syncthreads();
     const int t = chunk * 64 + lane;
     const unsigned long long bit = 1ull << lane;
-    if (t < a.T)
-        for (int k = 0; k < a.K; ++k) {
-            const int s = slot_of(a, t, k);
-            if (s >= 0) atomicOr(&m[s], bit);
-        }
+    // the token's slots, kept in registers for the ranking pass (top_k <= 16)
+    int sk[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        sk[k] = (t < a.T && k < a.K) ? slot_of(a, t, k) : -1;
+        if (sk[k] >= 0) atomicOr(&m[sk[k]], bit);
+    }
     __syncthreads();
     if (t < a.T)
-        for (int k = 0; k < a.K; ++k) {
-            const int s = slot_of(a, t, k);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (k >= a.K) break;
+            const int s = sk[k];
             int code = -1;
             if (s >= 0) code = s * 64 + __popcll(m[s] & (bit - 1ull));
             a.pair_code[(size_t)t * a.K + k] = code;
