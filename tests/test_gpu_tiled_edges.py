@@ -87,3 +87,16 @@ def test_tiled_expert_gemms_at_tile_edges(x_rows):
         gh.assert_close(y_g[a:b], y_ref, f"y group {g} ({b - a} rows)")
     assert np.all(hm_g[P:] == sentinel.numpy()), "hm rows past the groups were written"
     assert np.all(y_g[P:] == sentinel.numpy()), "y rows past the groups were written"
+
+
+def test_prefill_layer_repeats_bit_for_bit():
+    """The direct-to-LDS pipeline has no run-to-run freedom (fixed K order
+    per output, explicit load waits): a prefill-sized layer (T = 8192, the
+    tiled router, the fused dispatch placement and the 256-row expert tiles
+    with ragged groups) gives identical bits on five launches."""
+    cfg = moe_synth.scaled_config(4, T=8192, H=1024, I=512, seed=43)
+    L = gh.build_layer(cfg)
+    first = gh.gpu_forward(L).cpu().numpy()
+    for _ in range(4):
+        again = gh.gpu_forward(L).cpu().numpy()
+        assert np.array_equal(first.view(np.uint8), again.view(np.uint8))
