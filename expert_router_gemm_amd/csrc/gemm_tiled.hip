@@ -568,27 +568,58 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
     // acc[m][i][j]: x row wm*WMR + i*16 + 4*lg + q (q = 0..3), feature
     // n0 + wn*FN/4 + j*16 + lr.
     auto epilogue = [&](const Item<NM> &it) {
+        if constexpr (EPI == 2) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
+            for (int i = 0; i < MI; ++i) {
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = it.rs + wm * WMR + i * 16 + 4 * lg + q;
-                if (r >= it.r1) continue;
+                for (int q = 0; q < 4; ++q) {
+                    const int r = it.rs + wm * WMR + i * 16 + 4 * lg + q;
+                    if (r >= it.r1) continue;
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const int f = it.n0 + wn * (FN / WNW) + j * 16 + lr;
-                    if (f >= a.N) continue;
-                    if (EPI == 2) {
+                    for (int j = 0; j < NJ; ++j) {
+                        const int f = it.n0 + wn * (FN / WNW) + j * 16 + lr;
+                        if (f >= a.N) continue;
                         reinterpret_cast<float *>(a.out)[(size_t)it.kz * a.split_stride +
                                                          (size_t)r * a.out_ld + f] =
                             acc[0][i][j][q];
-                    } else {
-                        float v;
-                        if (EPI == 1)
-                            v = siluf_(acc[0][i][j][q]) * acc[NM - 1][i][j][q];
-                        else
-                            v = acc[0][i][j][q];
-                        reinterpret_cast<f16 *>(a.out)[(size_t)r * a.out_ld + f] = to_f16(v);
+                    }
+                }
+            }
+        } else {
+            // fp16 results two features per store: lanes l and l^1 hold the
+            // same 4 rows at adjacent features; they swap two values (DPP
+            // quad_perm [1,0,3,2]) so the even lane writes rows q = 0, 1 and
+            // the odd lane rows 2, 3, each as one 4-byte store
+            const bool odd = lr & 1;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    uint32_t h[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float v = EPI == 1
+                                            ? siluf_(acc[0][i][j][q]) * acc[NM - 1][i][j][q]
+                                            : acc[0][i][j][q];
+                        h[q] = (uint32_t)__builtin_bit_cast(uint16_t, to_f16(v));
+                    }
+                    const uint32_t s0 = odd ? h[0] : h[2], s1 = odd ? h[1] : h[3];
+                    const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0xB1, 0xf, 0xf, false);
+                    const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xf, 0xf, false);
+                    // even lane: rows q0, q1 = (own, partner); odd: rows q2, q3 = (partner, own)
+                    const uint32_t w0 = odd ? (r0 | (h[2] << 16)) : (h[0] | (r0 << 16));
+                    const uint32_t w1 = odd ? (r1 | (h[3] << 16)) : (h[1] | (r1 << 16));
+                    const int f = it.n0 + wn * (FN / WNW) + j * 16 + (lr & ~1);
+                    const int rb = it.rs + wm * WMR + i * 16 + 4 * lg + (odd ? 2 : 0);
+                    if (f < a.N) {
+                        uint32_t *o0 = reinterpret_cast<uint32_t *>(reinterpret_cast<f16 *>(a.out) +
+                                                                    (size_t)rb * a.out_ld + f);
+                        uint32_t *o1 = reinterpret_cast<uint32_t *>(reinterpret_cast<f16 *>(a.out) +
+                                                                    (size_t)(rb + 1) * a.out_ld + f);
+                        if (rb < it.r1) *o0 = w0;
+                        if (rb + 1 < it.r1) *o1 = w1;
                     }
                 }
             }
