@@ -6,10 +6,11 @@ The tiled kernels load operands straight into LDS with gfx950's
 inline asm that writes M0 (the LDS destination) without declaring it
 clobbered (the compiler reserves M0).  That is sound only while nothing
 else in these kernels keeps a value in M0, so: every M0 write must be one
-of those asm blocks' `s_mov_b32 m0, sN`, directly followed by an LDS-DMA
-load, and M0 must appear nowhere else.  The kernels must also keep every
-value in registers (no scratch memory: a scratch access in the K loop would
-be a vector-memory access the explicit load-count waits do not expect).
+of those asm blocks' `s_mov_b32 m0, <scalar register>`, directly followed
+by an LDS-DMA load, and M0 must appear nowhere else.  The kernels must also
+keep every value in registers (no scratch memory: a scratch access in the
+K loop would be a vector-memory access the explicit load-count waits do not
+expect).
 """
 import os
 import re
@@ -48,7 +49,8 @@ def test_m0_written_only_for_lds_dma(asm):
     for i, s in enumerate(lines):
         if not re.search(r"\bm0\b", s):
             continue
-        assert re.fullmatch(r"s_mov_b32 m0, s\d+", s), f"unexpected use of m0: {s!r}"
+        # (the asm operand is any scalar register, vcc's halves included)
+        assert re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)", s), f"unexpected use of m0: {s!r}"
         nxt = lines[i + 1] if i + 1 < len(lines) else ""
         assert re.match(r"(buffer_load_dwordx4 .* lds|global_load_lds_dwordx4 )", nxt), (
             f"m0 write not followed by an LDS-DMA load: {s!r} then {nxt!r}")
