@@ -57,6 +57,9 @@ def test_workspace_bytes():
     assert moe.moe_workspace_bytes(s, 0) > 0
     assert moe.moe_workspace_bytes(_shape(hidden=100), 16) == 0
     assert moe.moe_workspace_bytes(s, -1) == 0
+    # the token limit, 2^20 (include/moe.h), and one past it
+    assert moe.moe_workspace_bytes(s, 1 << 20) > 0
+    assert moe.moe_workspace_bytes(s, (1 << 20) + 1) == 0
     sh = _shape(n_shared=2, shared=True, n_slots=256)
     assert moe.moe_workspace_bytes(sh, 128) > moe.moe_workspace_bytes(_shape(n_slots=256), 128)
     f8 = _shape(dispatch=moe.MOE_FP8_E4M3)  # adds the quantised row copies: 1 B/element
