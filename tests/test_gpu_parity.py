@@ -388,6 +388,28 @@ def test_full_size_sampled(n, groups):
     print(f"[full] workload {n} P={st['P']} sample={len(tok)} max|d|={err:.3e}")
 
 
+@pytest.mark.slow
+def test_layer_at_maximum_tokens():
+    """T = 2^20 tokens (the C ABI's limit) with the rank-share routing of the
+    decode workload (32 local slots of 256 experts, top-8) and H = I = 128:
+    the tiled router, top-K over a million tokens, dispatch through the
+    single-block scan, groups of ~32 K rows in the tiled expert GEMMs and a
+    million-block combine.  Routing of a sample and the whole dispatch
+    exact, layer outputs on the sample within the output bar."""
+    cfg = moe_synth.scaled_config(2, T=1 << 20, H=128, I=128, seed=64)
+    print(f"[case] maximum tokens T={cfg.T} H={cfg.H} I={cfg.I}", flush=True)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    out = gh.gpu_forward(L).cpu().numpy()
+    assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8))
+    tok = np.sort(np.random.default_rng(64).choice(cfg.T, 64, replace=False))
+    tie = _check_routing(L, st, tokens=tok)
+    _check_dispatch(L, st)
+    ref = gh.oracle_forward(L, tokens=tok)
+    err = gh.assert_close(out[tok], ref["out"], "layer output (sample)", rows=~tie)
+    print(f"[max tokens] P={st['P']} sample={len(tok)} max|d|={err:.3e}")
+
+
 def test_prefill_tiled_path_small():
     """T = 4096 rank share: the router (T >= 2048, K split in 2 slices) and
     the routed FFN (>= 64 expected rows per group) take the LDS-tiled kernel."""
