@@ -778,11 +778,13 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
     const int n_ntiles = (a.N + WR / NM - 1) / (WR / NM);
     const size_t lds = tile_lds_bytes<TBM>();
     // Per device, once: allow the dynamic LDS size and count the workgroups
-    // that are resident at once (cached; a race only repeats the queries).
+    // that are resident at once (cached; a race only repeats the queries; the
+    // release store orders the attribute call before any thread that reads
+    // the cached count launches).
     static std::atomic<int> resident[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-    int slots = dev < kMaxDevices ? resident[dev].load(std::memory_order_relaxed) : 0;
+    int slots = dev < kMaxDevices ? resident[dev].load(std::memory_order_acquire) : 0;
     if (slots <= 0) {
         hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<TBM, NM, EPI, GATHER>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -794,7 +796,7 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
             per_cu < 1)
             per_cu = 1;
         slots = cus * per_cu;
-        if (dev < kMaxDevices) resident[dev].store(slots, std::memory_order_relaxed);
+        if (dev < kMaxDevices) resident[dev].store(slots, std::memory_order_release);
     }
     // every resident workgroup slot, never more than the items
     long grid = slots;
