@@ -29,7 +29,7 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128;              // x rows per tile
+constexpr int BM = 128;              // x rows per tile (register-staged kernel, router)
 constexpr int WNW = 4;               // waves along the weight rows (2 x 4 waves)
 constexpr int WR = 64 * WNW;         // weight rows per tile (gate + up halves for SwiGLU)
 constexpr int BK = 64;               // reduction per pipeline step
@@ -53,8 +53,9 @@ constexpr int kMaxDevices = 64;
 // measured with SQ_LDS_BANK_CONFLICT).
 __device__ __forceinline__ int swz(int r, int c) { return r * PITCH + ((c ^ (r & 7)) << 3); }
 
-// One work item: x rows [rs, rs+128) of group g x features [n0, n0 + WR/NM),
-// K slice kz (router logits only).  Everything a load or the epilogue needs.
+// One work item: x rows [rs, rs + tile rows) of group g x features
+// [n0, n0 + WR/NM), K slice kz (router logits only).  Everything a load or
+// the epilogue needs.
 template <int NM>
 struct Item {
     int rs, r1, n0, kz, k0;                // rows, features, K slice, K offset
@@ -167,6 +168,7 @@ __device__ __forceinline__ void decode_item(const int *tstart, int n_groups, int
     }
 }
 
+// Register-staged pipeline (MOE_TILED_DMA=0, 128-row tiles).
 // The items of one workgroup, one after the other, with one pipeline: the
 // loads of an item's first K steps are issued during the previous item's
 // last steps (its K steps past the end map to the next item's first ones),
