@@ -1,0 +1,102 @@
+"""Host logic of bench.py, on the CPU: which kernel the roofline and traffic
+figures describe, the traffic record's key on the kernel sources, the PMC
+summary's calibration arithmetic, and the decode workload's algorithmic
+bytes against the EP blog's per-expert figure (section 6.3: 88 MB per
+expert = 3 matrices of 7168 x 2048 fp16)."""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+import moe_synth
+
+# kernel names as rocprofv3 prints them (PMC runs: mangled; kernel traces:
+# demangled); template arguments <weight, x, subtiles, epilogue, K waves,
+# chunks> and <tile rows, matrices, epilogue, gathered>, epilogue 1 = SwiGLU
+STREAM = "_ZN3moe12_GLOBAL__N_118stream_gemm_kernelIDF16_Li1ELi4ELi{}ELi4ELi2EEEvNS_10StreamArgsE"
+STREAM_F32 = "void moe::(anonymous namespace)::stream_gemm_kernel<float, 1, 4, {}, 4, 2>(moe::StreamArgs)"
+TILED = "void moe::(anonymous namespace)::tiled_gemm_kernel<{}>(moe::StreamArgs, int, int)"
+TILED_MANGLED = "_ZN3moe12_GLOBAL__N_117tiled_gemm_kernelILi256ELi2ELi1ELb{}EEEvNS_10StreamArgsEii"
+COPY = ("void at::native::vectorized_elementwise_kernel<8, at::native::AUnaryFunctor<c10::Half, "
+        "c10::Half, c10::Half, at::native::binary_internal::MulFunctor<float> >>(int)")
+
+
+def test_dominant_kernel_is_the_swiglu_gate_up_launch():
+    assert bench.is_dominant(STREAM.format(1), "stream")
+    assert bench.is_dominant(STREAM_F32.format(1), "stream")
+    for epi in (0, 2):  # down projection, router logits
+        assert not bench.is_dominant(STREAM.format(epi), "stream")
+        assert not bench.is_dominant(STREAM_F32.format(epi), "stream")
+    assert bench.is_dominant(TILED.format("256, 2, 1, true"), "tiled")
+    assert bench.is_dominant(TILED_MANGLED.format(1), "tiled")
+    for args in ("256, 1, 0, false", "128, 1, 2, false", "256, 2, 1, false"):
+        assert not bench.is_dominant(TILED.format(args), "tiled")
+    assert not bench.is_dominant(TILED_MANGLED.format(0), "tiled")
+    # one kind never matches the other's kernels
+    assert not bench.is_dominant(STREAM.format(1), "tiled")
+    assert not bench.is_dominant(TILED.format("256, 2, 1, true"), "stream")
+    assert bench.dominant_kind(4) == "tiled"
+    assert all(bench.dominant_kind(n) == "stream" for n in (1, 2, 3, 5))
+
+
+def test_traffic_record_is_used_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    rec = tmp_path / "rec.json"
+    monkeypatch.setattr(bench, "traffic_path", lambda kind, workload: str(rec))
+    assert bench.load_traffic("tiled", "w") is None  # no record
+    rec.write_text(json.dumps({"kernel_source_hash": bench.kernel_source_hash("tiled"),
+                               "traffic_bytes_per_launch": 1234.5}))
+    assert bench.load_traffic("tiled", "w") == 1234.5
+    # the same record against the other kernel's sources: dropped
+    assert bench.kernel_source_hash("stream") != bench.kernel_source_hash("tiled")
+    assert bench.load_traffic("stream", "w") is None
+
+
+def _counter_csv(path, rows):
+    path.mkdir(parents=True)
+    with open(path / "run_counter_collection.csv", "w") as f:
+        f.write('"Kernel_Name","Counter_Name","Counter_Value"\n')
+        for name, counter, value in rows:
+            f.write(f'"{name}","{counter}",{value}\n')
+
+
+def test_pmc_summary_scales_each_counter_by_the_calibration_copy(tmp_path, monkeypatch):
+    """A 1 GiB copy reads 1 GiB and writes 1 GiB; whatever a counter reads
+    for it fixes that counter's scale (here FETCH reads half, WRITE all)."""
+    gib = 1 << 30
+    dom = TILED.format("256, 2, 1, true")
+    other = TILED.format("256, 1, 0, false")
+    _counter_csv(tmp_path / "fetch", [
+        (dom, "FETCH_SIZE", 1000.0), (dom, "FETCH_SIZE", 1004.0), (dom, "FETCH_SIZE", 990.0),
+        (other, "FETCH_SIZE", 9.0e6), (COPY, "FETCH_SIZE", gib / 1024 / 2)])
+    _counter_csv(tmp_path / "write", [
+        (dom, "WRITE_SIZE", 10.0), (dom, "WRITE_SIZE", 12.0), (dom, "WRITE_SIZE", 11.0),
+        (other, "WRITE_SIZE", 7.0e6), (COPY, "WRITE_SIZE", gib / 1024)])
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "traffic_path", lambda kind, workload: str(out))
+    bench.summarize_pmc(str(tmp_path / "fetch"), str(tmp_path / "write"), "w", gib, "tiled")
+    rec = json.loads(out.read_text())
+    assert rec["kernel_source_hash"] == bench.kernel_source_hash("tiled")
+    assert rec["counters"]["FETCH_SIZE"]["copy_factor"] == pytest.approx(2.0)
+    assert rec["counters"]["WRITE_SIZE"]["copy_factor"] == pytest.approx(1.0)
+    # medians of the dominant launches, in bytes
+    assert rec["traffic_bytes_per_launch"] == pytest.approx(1000.0 * 1024 * 2 + 11.0 * 1024)
+
+
+def test_decode_bytes_follow_the_pages_per_expert_figure():
+    cfg = moe_synth.config(2)  # EP = 8 rank share, T = 256, 32 local slots
+    per_expert = 3 * 7168 * 2048 * 2  # EP blog section 6.3: 88 MB per expert
+    assert per_expert == 88_080_384
+    counts = np.full(32, 8, np.int32)  # every slot touched, P = 256
+    work = bench.algorithmic_work({"cfg": cfg, "b": {"counts": torch.from_numpy(counts)}})
+    T, K, H, P = cfg.T, cfg.K, cfg.H, 256
+    assert (work["P"], work["touched"]) == (P, 32)
+    vec = T * H * 2  # one [256, 7168] fp16 array: router weights, h, output
+    # the layer: every touched expert once, router weights, h and the output,
+    # plus the expert-output round trip and the routing outputs
+    assert work["layer_bytes"] - 2 * P * H * 2 - T * K * 8 == 32 * per_expert + 3 * vec
+    # gate/up launch: two of the three matrices per touched expert, the
+    # gathered rows and the SwiGLU output
+    assert work["up"]["bytes"] == 32 * per_expert * 2 // 3 + P * H * 2 + P * cfg.I * 2
+    assert work["up"]["flops"] == 2 * 2 * P * H * cfg.I
