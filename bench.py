@@ -1,20 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE-layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
 
 One step = one pass of the whole path over one batch resident in HBM: one
 call of moe_layer_forward_profiled (router + top-K, dispatch, gate/up and
 down grouped GEMMs with the shared experts, combine) through libmoe's C ABI
 on torch's current stream; the call records HIP events around the gate/up
 GEMM, which give the roofline record.  The same pass without events, a
-per-stage breakdown and the staged entry points are reported beside it.  The default workload is the EP=8
-rank-share decode batch: 256 tokens, hidden 7168, top-8 of 256 experts, the
-32 local experts' SwiGLU 7168x2048 weights in fp16.
+per-stage breakdown and the staged entry points are reported beside it.
+
+The default workload is the whole DeepSeek-V3 MoE layer at decode: 128
+tokens, hidden 7168, top-8 of 256 routed experts with the long-tail routing
+of the EP blog's section 6.1, 2 shared experts, all 256 + 2 experts' SwiGLU
+7168x2048 weights resident in fp16 (22.5 GB, section 2.1).  After it, the
+same run times the prefill workload (one EP=8 rank's 32 experts, 16384
+tokens: the compute-bound regime) and reports it under the "prefill" key
+with the MFMA fraction of its gate/up GEMM.
 
 Printed: one JSON line with tokens/s, a roofline record for the dominant
 kernel (the gate/up weight stream, timed with HIP events on the stream it
-runs on) and the CPU oracle timed on the host for the same workload.
+runs on), the layer's HBM fraction counting only the bytes the layer must
+move (touched expert weights, shared experts, router, h, out), and the CPU
+oracle timed on the host for the same workload (all host threads the run
+may use, and one thread).
 
 --summarize-pmc FETCH_DIR WRITE_DIR: turn two `rocprofv3 --pmc FETCH_SIZE`
 / `--pmc WRITE_SIZE` runs of this script (with --copy-calibration) into the
@@ -23,6 +32,7 @@ HBM traffic record under profiles/ that later runs report.
 from __future__ import annotations
 
 import argparse
+import gc
 import glob
 import hashlib
 import json
@@ -36,6 +46,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+DEFAULT_WORKLOAD = 3           # whole layer, decode, T = 128
+PREFILL_WORKLOAD = 4           # EP=8 rank share, prefill, T = 16384
 # The dominant kernel of a workload: the gate/up weight stream at decode
 # sizes, the LDS-tiled gate/up GEMM (256-row tiles, rows gathered) at prefill.
 # Its HBM traffic record is keyed by a hash of the sources it is built from.
@@ -51,7 +63,7 @@ DOMINANT = {"stream": "stream_gemm_kernel", "tiled": "tiled_gemm_kernel"}
 
 
 def dominant_kind(workload: int) -> str:
-    return "tiled" if workload == 4 else "stream"
+    return "tiled" if workload == PREFILL_WORKLOAD else "stream"
 
 
 def kernel_source_hash(kind: str = "stream") -> str:
@@ -195,31 +207,43 @@ def profiled_step(ctx, prof):
 # ------------------------------------------------------------------ accounting
 
 
-def algorithmic_work(ctx):
-    """Per-step algorithmic bytes (and FLOPs) of each stage, from the routing
-    the step actually produced (same input every step)."""
-    cfg = ctx["cfg"]
-    counts = ctx["b"]["counts"].cpu().numpy()
+def shared_in_routed_launch(cfg) -> bool:
+    """Whether the layer entry runs the shared experts as extra groups of
+    the routed gate/up launch: both sides stream weights (fewer than 64
+    expected rows per group) and rows are gathered (not fp8 copies)."""
+    if not cfg.n_shared or cfg.dispatch == "fp8":
+        return False
+    return cfg.T * cfg.K // cfg.E < 64 and cfg.n_shared * cfg.T // cfg.E < 64
+
+
+def algorithmic_work(cfg, counts):
+    """Algorithmic bytes and FLOPs of one step, from the routing the step
+    produced (per-slot counts; the same input every step).
+
+    layer_bytes: what the layer must move at least -- the weights of every
+    touched expert and of the shared experts, the router, h in and out back
+    (T*H each).  Intermediates (hm, y) and the softmax/top-K, dispatch and
+    combine count as time, not as work.
+    up: the gate/up launch of the layer entry -- gate and up weights of the
+    touched experts (and of the shared experts when they ride in the same
+    launch), each of its input rows read once and its hm rows written once."""
+    import numpy as np
+    counts = np.asarray(counts)
     P = int(counts.sum())
     touched = int((counts > 0).sum())
     isz = 4 if cfg.dtype == "f32" else 2
     xsz = 1 if cfg.dispatch == "fp8" else isz
     H, I, E, T, K = cfg.H, cfg.I, cfg.E, cfg.T, cfg.K
-    expert_bytes = 3 * H * I * isz
-    up = dict(bytes=touched * 2 * I * H * isz + P * H * xsz + P * 4 * (xsz == 1) + P * I * isz,
-              flops=2 * 2 * P * H * I)
-    down = dict(bytes=touched * H * I * isz + P * I * isz + P * H * isz, flops=2 * P * H * I)
-    route = dict(bytes=(E + (cfg.n_shared > 0)) * H * isz + T * H * isz + T * K * 8,
-                 flops=2 * T * H * (E + (cfg.n_shared > 0)))
-    shared = dict(bytes=cfg.n_shared * expert_bytes + cfg.n_shared * T * (H * isz * 2 + I * isz),
-                  flops=cfg.n_shared * 6 * T * H * I)
-    copy = 2 * P * H * xsz if cfg.dispatch == "fp8" else 0  # fp8 rows: quantised copy
-    layer_bytes = (touched * expert_bytes + shared["bytes"] + route["bytes"]
-                   + T * H * isz  # output
-                   + copy + 2 * P * H * isz)  # dispatch copy, y round trip
-    return dict(P=P, touched=touched, up=up, down=down, route=route, shared=shared,
-                layer_bytes=layer_bytes,
-                layer_flops=up["flops"] + down["flops"] + route["flops"] + shared["flops"])
+    n_sh = cfg.n_shared
+    merged = shared_in_routed_launch(cfg)
+    sh_rows = n_sh * T if merged else 0
+    up_groups = touched + (n_sh if merged else 0)
+    up = dict(bytes=up_groups * 2 * I * H * isz + (P + sh_rows) * (H * xsz + I * isz)
+              + (P * 4 if xsz == 1 else 0),
+              flops=2 * 2 * (P + sh_rows) * H * I)
+    layer_bytes = ((touched + n_sh) * 3 * H * I * isz + E * H * isz + 2 * T * H * isz)
+    layer_flops = (2 * T * H * (E + (n_sh > 0)) + 6 * P * H * I + 6 * n_sh * T * H * I)
+    return dict(P=P, touched=touched, up=up, layer_bytes=layer_bytes, layer_flops=layer_flops)
 
 
 def load_traffic(kind: str, workload: str):
@@ -233,6 +257,99 @@ def load_traffic(kind: str, workload: str):
     if rec.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ timing
+
+
+def time_workload(ctx, K: int, warmup: int, references: bool = True):
+    """Warm up, then time K passes of moe_layer_forward_profiled between two
+    synchronisations (wall clock).  Every EVERY-th pass records HIP events
+    on the launch stream around the gate/up GEMM (events[2], [3]); the
+    others pass no events (an event record costs the stream a few µs).
+    references: also time the entry point without events, a per-stage
+    breakdown and the staged entry points (same kernels)."""
+    import torch
+
+    import expert_router_gemm_amd as moe
+    for _ in range(warmup):
+        fused_step(ctx)
+        if references:
+            staged_step(ctx)
+    torch.cuda.synchronize()
+    EVERY = 5
+    ev_up = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for i in range(0, K, EVERY)}
+    no_ev = moe.make_profile([])
+    profs = [moe.make_profile([None, None, *ev_up[i]]) if i in ev_up else no_ev
+             for i in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        profiled_step(ctx, profs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    r = dict(ms_per_step=wall * 1e3 / K,
+             up_ms=statistics.mean(a.elapsed_time(b) for a, b in ev_up.values()))
+    if not references:
+        return r
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        fused_step(ctx)
+    e1.record()
+    torch.cuda.synchronize()
+    r["plain_ms"] = e0.elapsed_time(e1) / K
+    ev_all = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    for i in range(K):
+        profiled_step(ctx, moe.make_profile(ev_all[i]))
+    torch.cuda.synchronize()
+    names = ["route", "dispatch", "ffn_up", "ffn_down+shared", "combine"]
+    r["stage_ms"] = {n: statistics.median(ev[j].elapsed_time(ev[j + 1]) for ev in ev_all)
+                     for j, n in enumerate(names)}
+    e0.record()
+    for _ in range(K):
+        staged_step(ctx)
+    e1.record()
+    torch.cuda.synchronize()
+    r["staged_ms"] = e0.elapsed_time(e1) / K
+    r["same"] = bool(torch.equal(ctx["b"]["out"], ctx["b"]["out2"]))
+    return r
+
+
+def kernel_roofline(cfg, work, up_ms, workload_kind):
+    """Roofline record of the gate/up launch: algorithmic bytes (decode,
+    HBM-bound) or FLOPs (prefill, MFMA-bound) over its live duration."""
+    if workload_kind == "stream":
+        achieved = work["up"]["bytes"] / (up_ms / 1e3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=load_traffic("stream", cfg.name))
+    else:
+        achieved = work["up"]["flops"] / (up_ms / 1e3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_F16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                    traffic=load_traffic("tiled", cfg.name))
+    roof.update(kernel=f"{DOMINANT[workload_kind]} (SwiGLU gate/up, in moe_layer_forward)",
+                launch_ms=round(up_ms, 4), algorithmic_bytes=work["up"]["bytes"],
+                algorithmic_flops=work["up"]["flops"])
+    return roof
+
+
+def layer_record(work, t):
+    ms = t["ms_per_step"]
+    gbs = work["layer_bytes"] / (ms / 1e3) / 1e9
+    tfs = work["layer_flops"] / (ms / 1e3) / 1e12
+    rec = {"entry": "moe_layer_forward_profiled", "hbm_gbs": round(gbs, 1),
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_tflops": round(tfs, 1),
+           "mfma_frac": round(tfs / MFMA_F16_PEAK_TFLOPS, 4),
+           "algorithmic_bytes": work["layer_bytes"], "algorithmic_flops": work["layer_flops"],
+           "rows": work["P"], "touched_slots": work["touched"]}
+    if "plain_ms" in t:
+        rec.update(no_events_ms=round(t["plain_ms"], 4), staged_calls_ms=round(t["staged_ms"], 4),
+                   staged_equals_fused=t["same"],
+                   stage_ms={k: round(v, 4) for k, v in t["stage_ms"].items()})
+    return rec
 
 
 # ------------------------------------------------------------------ EPLB-lite
@@ -288,31 +405,86 @@ def eplb_report(ctx, steps: int = 12):
 # ------------------------------------------------------------------ CPU baseline
 
 
+def host_threads() -> int:
+    """Host threads the run may use: OMP_NUM_THREADS when set (the share
+    of the machine this process gets), else the CPU count, at most 16."""
+    v = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(v) if v.isdigit() and int(v) > 0 else (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_ram_gb():
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    return round(int(line.split()[1]) / 2 ** 20, 1)
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(ctx, budget_s: float = 20.0):
-    """The oracle (plain C, single thread) on the same workload's tokens, on
-    the host; tokens are taken in order until ~budget_s of CPU work."""
+    """The oracle (plain C, fp64 accumulation) on the same workload's tokens
+    on the host, timed around its layer forward only.  First one thread on
+    the first tokens (doubling until about a third of the budget is used),
+    then every host thread the run may use, each on its own contiguous
+    block of the batch's first tokens (the oracle call releases the
+    interpreter lock), sized from the single-thread rate to fill the rest
+    of the budget; tokens/s of each."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
     cfg = ctx["cfg"]
     ro, rs, se = oracle.placement(cfg.E, cfg.ep_size, cfg.ep_rank, replica_of=ctx["rep"])
     sw = [ctx["host_experts"][int(e)] for e in se]
-    done, t_used, n = 0, 0.0, 16
-    while done < cfg.T and t_used < budget_s:
-        n = min(n, cfg.T - done)
-        tok = np.arange(done, done + n, dtype=np.int32)
-        t0 = time.perf_counter()
+
+    def run(tok):
         oracle.layer_forward(h=np.ascontiguousarray(ctx["h"][tok]), w_router=ctx["wr"][: cfg.E],
                              bias=ctx["bias"], w_sg=ctx["wr"][cfg.E] if cfg.n_shared else None,
                              slot_weights=sw, shared=ctx["shared"], rep_off=ro, rep_slot=rs,
                              seed=cfg.seed, K=cfg.K, fp8_dispatch=cfg.dispatch == "fp8",
                              tok_ids=tok, groups=cfg.groups)
-        t_used += time.perf_counter() - t0
+
+    done, t1, n = 0, 0.0, 1
+    while done < cfg.T and t1 < budget_s / 3:
+        n = min(n, cfg.T - done)
+        tok = np.arange(done, done + n, dtype=np.int32)
+        t0 = time.perf_counter()
+        run(tok)
+        t1 += time.perf_counter() - t0
         done += n
         n *= 2
-    return dict(value=done / t_used, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"first {done} of {cfg.T} tokens of {cfg.name} "
-                       f"({t_used:.1f} s, single-threaded plain C, fp64 accumulation)")
+    single = dict(value=done / t1, cores=1,
+                  sample=f"tokens 0..{done - 1} of {cfg.T} ({t1:.1f} s)")
+    nt = host_threads()
+    rate1 = done / t1
+    per = max(1, int(rate1 * budget_s * 2 / 3))   # tokens one thread does in the rest
+    N = min(cfg.T, nt * per)
+    nt = max(1, min(nt, N))
+    blocks = [np.arange(N * i // nt, N * (i + 1) // nt, dtype=np.int32) for i in range(nt)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(nt) as ex:
+        list(ex.map(run, blocks))
+    tm = time.perf_counter() - t0
+    return dict(value=N / tm, unit="tokens/s", cores=nt, kind="oracle",
+                sample=f"tokens 0..{N - 1} of {cfg.T} of {cfg.name} in {nt} "
+                       f"contiguous blocks, one host thread each ({tm:.1f} s wall; plain C, "
+                       f"fp64 accumulation, forward only)",
+                single_thread=single, cpu_model=cpu_model(), host_ram_gb=host_ram_gb())
 
 
 # ------------------------------------------------------------------ PMC summary
@@ -377,8 +549,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int
                + out["WRITE_SIZE"]["bytes_per_launch"])
     rec["command"] = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv "
                       "-d DIR -o run -- python3 bench.py --workload N --steps 3 --warmup 1 "
-                      "--no-cpu-baseline --copy-calibration; python3 bench.py --summarize-pmc "
-                      "FETCH_DIR WRITE_DIR --workload N")
+                      "--no-cpu-baseline --no-prefill --copy-calibration; python3 bench.py "
+                      "--summarize-pmc FETCH_DIR WRITE_DIR --workload N")
     p = traffic_path(kind, workload)
     with open(p, "w") as f:
         json.dump(rec, f, indent=2)
@@ -388,13 +560,65 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int
 # ------------------------------------------------------------------ main
 
 
+def free_gpu(ctx):
+    import torch
+    ctx.clear()
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def prefill_record(K: int, warmup: int):
+    """The prefill workload timed like the main one; tokens/s, the MFMA
+    fraction of its gate/up launch and of the whole layer."""
+    import torch
+
+    import expert_router_gemm_amd as moe
+    ctx = setup(PREFILL_WORKLOAD, keep_host=False)
+    cfg = ctx["cfg"]
+    t = time_workload(ctx, K, warmup, references=False)
+    prof_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    profiled_step(ctx, moe.make_profile(prof_ev))
+    torch.cuda.synchronize()
+    names = ["route", "dispatch", "ffn_up", "ffn_down+shared", "combine"]
+    t["stage_ms"] = {n: prof_ev[j].elapsed_time(prof_ev[j + 1]) for j, n in enumerate(names)}
+    work = algorithmic_work(cfg, _counts_of(ctx))
+    rec = {"workload": cfg.name, "tokens": cfg.T, "local_slots": ctx["S"],
+           "value": round(cfg.T / (t["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
+           "steps": K, "warmup": warmup, "ms_per_step": round(t["ms_per_step"], 4),
+           "roofline": kernel_roofline(cfg, work, t["up_ms"], "tiled"),
+           "layer": layer_record(work, t)}
+    rec["layer"]["stage_ms_one_pass"] = {k: round(v, 4) for k, v in t["stage_ms"].items()}
+    free_gpu(ctx)
+    return rec
+
+
+def _counts_of(ctx):
+    """Per-slot counts of the routing the timed steps produced (the staged
+    route + dispatch on the same input)."""
+    import torch
+
+    import expert_router_gemm_amd as moe
+    cfg, shape, d, b = ctx["cfg"], ctx["shape"], ctx["d"], ctx["b"]
+    fp8 = cfg.dispatch == "fp8"
+    moe.moe_route(shape, cfg.T, d["h"], d["wr"], d["bias"], b["idx"], b["tw"],
+                  b["sg"] if cfg.n_shared else None, None, b["ws"])
+    moe.moe_dispatch(shape, cfg.T, d["h"], b["idx"], ctx["smap"], b["xp"] if fp8 else None,
+                     b["xs"] if fp8 else None, b["counts"], b["offsets"], b["perm"], b["inv"],
+                     b["ws"])
+    torch.cuda.synchronize()
+    return b["counts"].cpu().numpy()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill workload's extra record")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (PMC scale)")
@@ -423,77 +647,17 @@ def main():
         return 1
     import expert_router_gemm_amd as moe
     moe.lib()
-    ctx = setup(args.workload, groups=groups)
+    want_cpu = not args.no_cpu_baseline
+    ctx = setup(args.workload, keep_host=want_cpu, groups=groups)
     cfg = ctx["cfg"]
+    kind = dominant_kind(args.workload)
 
-    for _ in range(args.warmup):
-        fused_step(ctx)
-        staged_step(ctx)
-    torch.cuda.synchronize()
-
-    # Timed region: K passes of moe_layer_forward_profiled.  Every EVERY-th
-    # pass records HIP events on the launch stream around the gate/up GEMM
-    # (events[2], [3]); the others pass no events (an event record costs the
-    # stream a few microseconds).
-    K = args.steps
-    EVERY = 5
-    ev_up = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for i in range(0, K, EVERY)}
-    no_ev = moe.make_profile([])
-    profs = [moe.make_profile([None, None, *ev_up[i]]) if i in ev_up else no_ev
-             for i in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        profiled_step(ctx, profs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / K
-    up_ms = statistics.mean(a.elapsed_time(b) for a, b in ev_up.values())
-    log(f"[bench] timed {K} steps of moe_layer_forward_profiled: {ms_per_step:.4f} ms/step, "
-        f"gate/up {up_ms * 1e3:.1f} us")
-
-    # References, not the reported value: the entry point without events, a
-    # per-stage breakdown, and the staged entry points (same kernels).
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(K):
-        fused_step(ctx)
-    e1.record()
-    torch.cuda.synchronize()
-    plain_ms = e0.elapsed_time(e1) / K
-    ev_all = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
-    for i in range(K):
-        profiled_step(ctx, moe.make_profile(ev_all[i]))
-    torch.cuda.synchronize()
-    names = ["route", "dispatch", "ffn_up", "ffn_down+shared", "combine"]
-    stage_ms = {n: statistics.median(ev[j].elapsed_time(ev[j + 1]) for ev in ev_all)
-                for j, n in enumerate(names)}
-    e0.record()
-    for _ in range(K):
-        staged_step(ctx)
-    e1.record()
-    torch.cuda.synchronize()
-    staged_ms = e0.elapsed_time(e1) / K
-    same = bool(torch.equal(ctx["b"]["out"], ctx["b"]["out2"]))
-
-    work = algorithmic_work(ctx)
-    value = cfg.T / (ms_per_step / 1e3)
-
-    decode = args.workload != 4
-    if decode:
-        achieved = work["up"]["bytes"] / (up_ms / 1e3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=load_traffic("stream", cfg.name))
-    else:
-        achieved = work["up"]["flops"] / (up_ms / 1e3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_F16_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                    traffic=load_traffic("tiled", cfg.name))
-    roof.update(kernel=("stream_gemm_kernel" if decode else "tiled_gemm_kernel") +
-                " (SwiGLU gate/up, in moe_layer_forward)", launch_ms=round(up_ms, 4),
-                algorithmic_bytes=work["up"]["bytes"], algorithmic_flops=work["up"]["flops"])
+    t = time_workload(ctx, args.steps, args.warmup)
+    log(f"[bench] timed {args.steps} steps of moe_layer_forward_profiled on {cfg.name}: "
+        f"{t['ms_per_step']:.4f} ms/step, gate/up {t['up_ms'] * 1e3:.1f} us")
+    work = algorithmic_work(cfg, ctx["b"]["counts"].cpu().numpy())
+    value = cfg.T / (t["ms_per_step"] / 1e3)
+    roof = kernel_roofline(cfg, work, t["up_ms"], kind)
 
     if args.copy_calibration:
         # a plain elementwise kernel that reads 1 GiB and writes 1 GiB
@@ -502,22 +666,24 @@ def main():
         torch.cuda.synchronize()
         torch.mul(a, 1.0, out=bb)
         torch.cuda.synchronize()
+        del a, bb
 
     eplb = eplb_report(ctx) if args.eplb else None
-
     cpu = None
-    if not args.no_cpu_baseline:
+    if want_cpu:
+        t0 = time.time()
         cpu = cpu_baseline(ctx, args.cpu_budget)
-
-    layer_gbs = work["layer_bytes"] / (ms_per_step / 1e3) / 1e9
+        log(f"[bench] cpu baseline: {cpu['value']:.2f} tokens/s on {cpu['cores']} threads, "
+            f"{cpu['single_thread']['value']:.2f} on one ({time.time() - t0:.1f} s)")
+    layer = layer_record(work, t)
     rec = {
         "metric": "MoE-layer tokens/s at 1 GPU + % HBM BW (decode) / % MFMA peak (prefill)",
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(t["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -527,21 +693,19 @@ def main():
                    "experts": cfg.E, "top_k": cfg.K, "local_slots": ctx["S"],
                    "shared_experts": cfg.n_shared, "dispatch": cfg.dispatch,
                    "ep_size": cfg.ep_size, "ep_rank": cfg.ep_rank,
+                   "long_tail": cfg.long_tail,
                    "group_limit": list(groups) if groups else None},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "layer": {"entry": "moe_layer_forward_profiled", "hbm_gbs": round(layer_gbs, 1),
-                  "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
-                  "mfma_tflops": round(work["layer_flops"] / (ms_per_step / 1e3) / 1e12, 1),
-                  "mfma_frac": round(work["layer_flops"] / (ms_per_step / 1e3) / 1e12
-                                     / MFMA_F16_PEAK_TFLOPS, 4),
-                  "algorithmic_bytes": work["layer_bytes"], "rows": work["P"],
-                  "touched_slots": work["touched"], "no_events_ms": round(plain_ms, 4),
-                  "staged_calls_ms": round(staged_ms, 4), "staged_equals_fused": same,
-                  "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}},
+        "layer": layer,
     }
     if eplb:
         rec["eplb"] = eplb
+    free_gpu(ctx)
+    if not args.no_prefill and args.workload != PREFILL_WORKLOAD:
+        rec["prefill"] = prefill_record(args.steps, args.warmup)
+        log(f"[bench] prefill {rec['prefill']['workload']}: {rec['prefill']['value']:.0f} "
+            f"tokens/s, gate/up {rec['prefill']['roofline']['achieved']} TFLOP/s")
     print(json.dumps(rec))
     return 0
 

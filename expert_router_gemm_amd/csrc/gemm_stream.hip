@@ -40,67 +40,27 @@
 #include "common.h"
 #include "kernels.h"
 
-// Compile-time tuning knobs (defaults are the measured best on MI355X):
-//   MOE_STREAM_U          K chunks per register buffer (double-buffered)
-//   MOE_STREAM_MAX_WAVES  cap on waves per SIMD (0 = compiler's choice)
-//   MOE_STREAM_COND_PREFETCH  1: skip the prefetch past the end (the
-//       compiler then waits for every load before the second compute)
-//   MOE_STREAM_NT         1: weights loaded with the non-temporal hint
-#ifndef MOE_STREAM_U
-#define MOE_STREAM_U 8
-#endif
-#ifndef MOE_STREAM_MAX_WAVES
-#define MOE_STREAM_MAX_WAVES 0
-#endif
-#ifndef MOE_STREAM_COND_PREFETCH
-#define MOE_STREAM_COND_PREFETCH 1
-#endif
-#ifndef MOE_STREAM_NT
-#define MOE_STREAM_NT 0
-#endif
-//   MOE_STREAM_STORE_WIDE_ROWS  expected rows per group from which the plain
-//       (down projection) GEMM takes the wide shape below (measured faster
-//       from ~8 rows per group; one subtile per wave for fewer rows)
-//   MOE_STREAM_STORE_NSUB_WIDE, MOE_STREAM_STORE_U_WIDE  subtiles per wave
-//       and K chunks per buffer of that wide shape
-//   MOE_STREAM_SWIGLU_NSUB  16-feature subtiles per wave of the SwiGLU GEMM
-//   MOE_STREAM_SWIGLU_U     its K chunks per register buffer
-//   MOE_STREAM_U_MT2        K chunks per buffer for 17-32 rows per pass
-//   MOE_STREAM_SWIGLU_KW, MOE_STREAM_STORE_KW  4: the waves of a block split
-//       K and share 4 subtiles (NSUB must be 4); 1: each wave its own
-#ifndef MOE_STREAM_STORE_WIDE_ROWS
-#define MOE_STREAM_STORE_WIDE_ROWS 6
-#endif
-#ifndef MOE_STREAM_STORE_NSUB_WIDE
-#define MOE_STREAM_STORE_NSUB_WIDE 4
-#endif
-#ifndef MOE_STREAM_STORE_U_WIDE
-#define MOE_STREAM_STORE_U_WIDE 2
-#endif
-#ifndef MOE_STREAM_SWIGLU_KW
-#define MOE_STREAM_SWIGLU_KW 4
-#endif
-#ifndef MOE_STREAM_STORE_KW
-#define MOE_STREAM_STORE_KW 4
-#endif
-#ifndef MOE_STREAM_SWIGLU_NSUB
-#define MOE_STREAM_SWIGLU_NSUB 4
-#endif
-#ifndef MOE_STREAM_SWIGLU_U
-#define MOE_STREAM_SWIGLU_U 2
-#endif
-#ifndef MOE_STREAM_U_MT2
-#define MOE_STREAM_U_MT2 MOE_STREAM_U
-#endif
-#if MOE_STREAM_MAX_WAVES > 0
-#define MOE_STREAM_OCC __attribute__((amdgpu_waves_per_eu(1, MOE_STREAM_MAX_WAVES)))
-#else
-#define MOE_STREAM_OCC
-#endif
-
 namespace moe {
 
 namespace {
+
+// Kernel shapes (measured best on MI355X):
+//   kU              K chunks per register buffer (double-buffered) of the
+//                   one-wave-per-slice shapes
+//   kStoreWideRows  expected rows per group from which the plain (down
+//                   projection) GEMM takes the wide shape (measured faster
+//                   from ~8 rows per group; one subtile per wave for fewer)
+//   kStoreNsubWide, kStoreUWide  subtiles per wave and K chunks per buffer
+//                   of that wide shape
+//   kSwigluNsub, kSwigluU  the SwiGLU GEMM's subtiles and chunks per buffer
+// The wide store shape, the SwiGLU GEMM and the fp16 router split K over
+// the 4 waves of a block (KW = 4) when K allows it.
+constexpr int kU = 8;
+constexpr int kStoreWideRows = 6;
+constexpr int kStoreNsubWide = 4;
+constexpr int kStoreUWide = 2;
+constexpr int kSwigluNsub = 4;
+constexpr int kSwigluU = 2;
 
 // Epilogues
 enum : int { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_LOGITS = 2 };
@@ -125,11 +85,7 @@ struct XFrag<f16, DT_FP8> {  // 8 fp8 codes, decoded to fp16 * 2^-8
 // Weight loads: every weight byte is read exactly once per launch.
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::vec wload16(const T *p) {
-#if MOE_STREAM_NT
-    return __builtin_nontemporal_load(reinterpret_cast<const typename Frag<T>::vec *>(p));
-#else
     return load16(p);
-#endif
 }
 
 // NSUB 16-feature subtiles per wave; NM = weight tiles per K chunk (SwiGLU:
@@ -207,19 +163,16 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
         }                                                                        \
     }
 
-    // Branch-free double buffering (NC is a multiple of 2U): a conditional
-    // prefetch would make the compiler wait for every outstanding load before
-    // the second compute; the last prefetch instead re-reads the chunk group
-    // just loaded (cache hits, never used).
+    // Double buffering (NC is a multiple of 2U): buffer b's loads are in
+    // flight while buffer a is computed, and the next group of a's while b
+    // is.  The last iteration skips the prefetch past the end; the compiler
+    // then waits for every outstanding load before that iteration's second
+    // compute.
     MOE_LOAD(wa, xa, 0);
     for (int c = 0; c < NC; c += 2 * U) {
         MOE_LOAD(wb, xb, c + U);
         MOE_COMPUTE(wa, xa);
-#if MOE_STREAM_COND_PREFETCH
         if (c + 2 * U < NC) MOE_LOAD(wa, xa, c + 2 * U);
-#else
-        MOE_LOAD(wa, xa, (c + 2 * U < NC) ? c + 2 * U : c + U);
-#endif
         MOE_COMPUTE(wb, xb);
     }
 #undef MOE_LOAD
@@ -314,7 +267,7 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
 }
 
 template <typename TW, int XM, int NSUB, int EPI, int KW, int U>
-__global__ __launch_bounds__(256) MOE_STREAM_OCC void stream_gemm_kernel(StreamArgs a) {
+__global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
     constexpr int FPW = 16 * NSUB;  // features per wave
     constexpr int NM = EPI == EPI_SWIGLU ? 2 * NSUB : NSUB;
     __shared__ f32x4 red[KW > 1 ? KW * NM * 64 : 1];
@@ -347,7 +300,7 @@ __global__ __launch_bounds__(256) MOE_STREAM_OCC void stream_gemm_kernel(StreamA
     for (int rb = zr; r0 + rb * 64 < r1; rb += zn) {
         const int rs = r0 + rb * 64;
         const int n = r1 - rs;
-        constexpr int U2 = U > MOE_STREAM_U_MT2 ? MOE_STREAM_U_MT2 : U;
+        constexpr int U2 = U;
         constexpr int U4 = KW > 1 ? 1 : (U > 2 ? 2 : U);
         if (n <= 16)
             stream_pass<TW, XM, NSUB, EPI, KW, 1, U>(b, g, f0, rs, r0, r1, kz, red);
@@ -358,7 +311,7 @@ __global__ __launch_bounds__(256) MOE_STREAM_OCC void stream_gemm_kernel(StreamA
     }
 }
 
-template <typename TW, int XM, int NSUB, int EPI, int U = MOE_STREAM_U, int KW = 1>
+template <typename TW, int XM, int NSUB, int EPI, int U = kU, int KW = 1>
 hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t s) {
     constexpr int FPB = (KW > 1 ? 1 : 4) * 16 * NSUB;  // features per block
     dim3 grid((a.N + FPB - 1) / FPB, n_groups + a.n_sec, zblocks * a.ksplit);
@@ -382,8 +335,7 @@ hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int m
         // the K-split shapes need K to hold 4 quarters of 4 chunks of 32
         const bool kw_ok = a.K % (a.ksplit * 4 * 4 * 32) == 0;
         if (mode == STREAM_SWIGLU) {
-            constexpr int NS = MOE_STREAM_SWIGLU_NSUB, U = MOE_STREAM_SWIGLU_U;
-            constexpr int KW = MOE_STREAM_SWIGLU_KW;
+            constexpr int NS = kSwigluNsub, U = kSwigluU, KW = 4;
             if (x_dtype == DT_FP8)
                 return kw_ok ? launch_t<f16, DT_FP8, NS, EPI_SWIGLU, U, KW>(a, n_groups, zblocks, s)
                              : launch_t<f16, DT_FP8, 1, EPI_SWIGLU>(a, n_groups, zblocks, s);
@@ -391,9 +343,8 @@ hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int m
                          : launch_t<f16, DT_F16, 1, EPI_SWIGLU>(a, n_groups, zblocks, s);
         }
         if (mode == STREAM_STORE) {
-            if (est_rows >= MOE_STREAM_STORE_WIDE_ROWS)
-                return kw_ok ? launch_t<f16, DT_F16, MOE_STREAM_STORE_NSUB_WIDE, EPI_STORE,
-                                        MOE_STREAM_STORE_U_WIDE, MOE_STREAM_STORE_KW>(
+            if (est_rows >= kStoreWideRows)
+                return kw_ok ? launch_t<f16, DT_F16, kStoreNsubWide, EPI_STORE, kStoreUWide, 4>(
                                    a, n_groups, zblocks, s)
                              : launch_t<f16, DT_F16, 2, EPI_STORE>(a, n_groups, zblocks, s);
             return launch_t<f16, DT_F16, 1, EPI_STORE>(a, n_groups, zblocks, s);

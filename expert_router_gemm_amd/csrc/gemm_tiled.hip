@@ -15,8 +15,7 @@
 // Operands go from global memory straight into LDS (buffer/global loads with
 // the lds modifier: no register staging), two stages for 256-row tiles and
 // three for 128-row ones, one barrier per K step, XOR-swizzled LDS rows (see
-// swz()).  Building with MOE_TILED_DMA=0 selects the earlier register-staged
-// pipeline (128-row tiles only), kept for comparison.
+// swz()).
 //
 // The grid is persistent (all resident workgroup slots): see tiled_gemm_kernel;
 // a workgroup's items share one pipeline where rows are not gathered (see
@@ -29,23 +28,13 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128;              // x rows per tile (register-staged kernel, router)
 constexpr int WNW = 4;               // waves along the weight rows (2 x 4 waves)
 constexpr int WR = 64 * WNW;         // weight rows per tile (gate + up halves for SwiGLU)
 constexpr int BK = 64;               // reduction per pipeline step
 constexpr int PITCH = BK;            // halves per LDS row (128 B, XOR-swizzled chunks)
 constexpr int kThreads = 128 * WNW;  // 2 x WNW waves
-constexpr int RSTEP = kThreads / 8;  // rows one staging pass covers
-constexpr int NXL = BM / RSTEP;      // x loads per thread per K step
-constexpr int NWL = WR / RSTEP;      // weight loads per thread per K step
-constexpr int NSTAGE = 3;            // LDS stages
+constexpr int kExpertRows = 256;     // x rows per tile of the expert GEMMs
 constexpr int kMaxDevices = 64;
-#ifndef MOE_TILED_DMA
-#define MOE_TILED_DMA 1
-#endif
-#ifndef MOE_TILED_EXPERT_ROWS
-#define MOE_TILED_EXPERT_ROWS 256
-#endif
 
 // LDS offset (halves) of 16-byte chunk c of row r: the chunk index is XORed
 // with r % 8, so the 16 rows one MFMA fragment read touches spread over all
@@ -59,18 +48,16 @@ __device__ __forceinline__ int swz(int r, int c) { return r * PITCH + ((c ^ (r &
 template <int NM>
 struct Item {
     int rs, r1, n0, kz, k0;                // rows, features, K slice, K offset
-    __amdgpu_buffer_rsrc_t xres, wres[NM];  // this tile's x rows and weight rows
-    const f16 *xgat[NXL];                  // gathered x rows (GATHER)
-    const f16 *xb, *wb[NM];                // the same ranges as base and bytes
-    int xbytes, wbytes;
+    const f16 *xb, *wb[NM];                // this tile's x rows and weight rows
+    int xbytes, wbytes;                    // their byte ranges
 };
 
-template <int NM, int EPI, bool GATHER, int TBM = BM>
+template <int NM, int EPI, int TBM>
 __device__ __forceinline__ Item<NM> make_item(const StreamArgs &a, int g, int mt, int nt, int kz,
                                               int nk) {
     constexpr int FN = WR / NM;  // features per tile
-    // wave-uniform by construction; readfirstlane keeps them (and the buffer
-    // descriptors built from them) in scalar registers
+    // wave-uniform by construction; readfirstlane keeps them (and the
+    // ranges formed from them) in scalar registers
     g = __builtin_amdgcn_readfirstlane(g);
     mt = __builtin_amdgcn_readfirstlane(mt);
     nt = __builtin_amdgcn_readfirstlane(nt);
@@ -92,37 +79,19 @@ __device__ __forceinline__ Item<NM> make_item(const StreamArgs &a, int g, int mt
     it.kz = kz;
     it.k0 = EPI == 2 ? kz * nk * BK : 0;
     const int K = a.K;
-    const int tid = threadIdx.x;
-    // Buffer loads against per-tile resource descriptors: rows past the
-    // tile's valid rows fall outside the descriptor's range and load zeros,
-    // so no clamping is needed; 32-bit lane offsets keep the address cost at
-    // one VGPR per load.
+    // Loads go through buffer descriptors over [xb, xb + xbytes) and
+    // [wb, wb + wbytes): rows past the tile's valid rows fall outside the
+    // range and load zeros, so no clamping is needed.
     const int rows_valid = (r1 - it.rs) < TBM ? (r1 - it.rs) : TBM;
     const int xrow0 = a.x_broadcast ? it.rs - r0 : it.rs;
     it.xb = reinterpret_cast<const f16 *>(a.x) + (size_t)xrow0 * K;
     it.xbytes = rows_valid * K * 2;
-    it.xres = __builtin_amdgcn_make_buffer_rsrc((void *)it.xb, (short)0, it.xbytes, 0x00020000);
-    // gathered x rows (rows named by a.gather): plain global loads from the
-    // row each thread moves; rows past the group repeat its last row (never
-    // stored)
-    if (GATHER) {
-#pragma unroll
-        for (int i = 0; i < NXL; ++i) {
-            int r = it.rs + (tid >> 3) + RSTEP * i;
-            if (r > r1 - 1) r = r1 - 1;
-            it.xgat[i] = reinterpret_cast<const f16 *>(a.x) +
-                         (size_t)(a.gather[r] / a.gather_div) * K + (tid & 7) * 8;
-        }
-    }
     const int ncols = (a.N - it.n0) < FN ? (a.N - it.n0) : FN;
     it.wbytes = ncols * K * 2;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
+    for (int m = 0; m < NM; ++m)
         it.wb[m] = reinterpret_cast<const f16 *>(m == 0 ? a.w0 : a.w1) +
                    (size_t)g * a.w_group_stride + (size_t)it.n0 * K;
-        it.wres[m] =
-            __builtin_amdgcn_make_buffer_rsrc((void *)it.wb[m], (short)0, it.wbytes, 0x00020000);
-    }
     return it;
 }
 
@@ -168,237 +137,11 @@ __device__ __forceinline__ void decode_item(const int *tstart, int n_groups, int
     }
 }
 
-// Register-staged pipeline (MOE_TILED_DMA=0, 128-row tiles).
-// The items of one workgroup, one after the other, with one pipeline: the
-// loads of an item's first K steps are issued during the previous item's
-// last steps (its K steps past the end map to the next item's first ones),
-// so only the workgroup's first item starts by waiting for memory.
-// 8 waves = 2 (rows) x 4 (weight rows); wave (wm, wn) owns x rows
-// wm*64..+64 and, per matrix m, weight rows m*FN + wn*FN/4 .. +FN/4
-// (FN = WR/NM features), as 4 x (4/NM) x NM tiles of 16x16x32 MFMAs.
-template <int NM, int EPI, bool GATHER>
-__device__ __forceinline__ void run_items(const StreamArgs &a, f16 *As, f16 *Bs,
-                                          const int *tstart, int n_groups, int n_ntiles, int ks,
-                                          const ItemSeq seq) {
-    constexpr int FN = WR / NM;   // features per tile
-    constexpr int NJ = 4 / NM;    // 16-feature subtiles per wave and matrix
-    const int K = a.K;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WNW, wn = wave % WNW;
-    const int lr = lane & 15, lg = lane >> 4;
-    // K steps per item: [kz*nk, (kz+1)*nk), nk even (K is a multiple of
-    // 2*BK*ksplit).  Items chain only with nk >= 4 (the loads run up to 3
-    // steps ahead), and not when x rows are gathered (the next item's row
-    // indices would be waited for together with the in-flight staging
-    // loads: measured 1% slower); otherwise each item restarts the pipeline.
-    const int nk = EPI == 2 ? K / BK / a.ksplit : K / BK;
-    constexpr bool CHAIN = !GATHER;
-    const bool chain = CHAIN && nk >= 4;
-
-    // Thread t moves 16-byte chunk t%8 of rows t/8 + RSTEP*i (i < NXL for x,
-    // i < NWL for the weight rows).
-    const int trow = tid >> 3, tch = tid & 7;
-    const int goff = trow * K * 2 + tch * 16;  // byte offset of row trow, chunk tch
-    const int rstep = RSTEP * K * 2;           // RSTEP rows further
-    const int lds0 = swz(trow, tch);           // (trow + RSTEP i) % 8 == trow % 8
-
-    // two register staging sets: set 0 holds even K steps, set 1 odd ones
-    f16x8 ra0[NXL], rb0[NWL], ra1[NXL], rb1[NWL];
-    // K step s of the chain: steps past the current item's end belong to the
-    // next item (or re-read the last step when there is none; never used).
-    // Branch-free (scalar selects), so the compiler's wait counts stay exact.
-    auto gload = [&](f16x8 *RA, f16x8 *RB, const Item<NM> &cur, const Item<NM> &nxt,
-                     bool has_nxt, int s) {
-        const bool to_nxt = CHAIN && s >= nk && has_nxt;
-        const int sk = s < nk ? s : (to_nxt ? s - nk : nk - 1);
-        const int kb = ((to_nxt ? nxt.k0 : cur.k0) + sk * BK) * 2;
-        if (GATHER) {
-#pragma unroll
-            for (int i = 0; i < NXL; ++i)
-                RA[i] = load16((to_nxt ? nxt.xgat[i] : cur.xgat[i]) + kb / 2);
-        } else {
-            const __amdgpu_buffer_rsrc_t xr = to_nxt ? nxt.xres : cur.xres;
-#pragma unroll
-            for (int i = 0; i < NXL; ++i)
-                RA[i] = __builtin_bit_cast(
-                    f16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, goff + i * rstep + kb, 0, 0));
-        }
-#pragma unroll
-        for (int i = 0; i < NWL; ++i) {
-            const int m = (i * RSTEP) / FN;
-            const __amdgpu_buffer_rsrc_t wr = to_nxt ? nxt.wres[m] : cur.wres[m];
-            RB[i] = __builtin_bit_cast(
-                f16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                           wr, goff + ((i * RSTEP) % FN / RSTEP) * rstep + kb, 0, 0));
-        }
-    };
-    auto lstore = [&](const f16x8 *RA, const f16x8 *RB, int st) {
-        f16 *A_ = As + st * BM * PITCH + lds0;
-        f16 *B_ = Bs + st * WR * PITCH + lds0;
-#pragma unroll
-        for (int i = 0; i < NXL; ++i) *reinterpret_cast<f16x8 *>(A_ + i * RSTEP * PITCH) = RA[i];
-#pragma unroll
-        for (int i = 0; i < NWL; ++i) *reinterpret_cast<f16x8 *>(B_ + i * RSTEP * PITCH) = RB[i];
-    };
-
-    // Three LDS stages: step k computes from stage k%3 while the staged data
-    // of step k+2 goes to stage (k+2)%3 (last read during step k-1), so the
-    // first-half fragments of step k+1 (stage (k+1)%3, complete since the
-    // barrier that ended step k-1) are read during step k and no step starts
-    // by waiting for LDS.  Per step: the 16 MFMAs of the first K half with
-    // the fragment reads of the second, then the 16 of the second half with
-    // the next step's first-half reads, the staging writes and the refill
-    // loads, pinned with scheduling-group barriers; one barrier per step.
-    f16x8 af0[4], bf0[NM][NJ], af1[4], bf1[NM][NJ];
-    auto fread = [&](f16x8 *af, f16x8 (*bf)[NJ], int st, int kq) {
-        const f16 *A = As + st * BM * PITCH;
-        const f16 *B = Bs + st * WR * PITCH;
-        const int ch = kq + lg;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            af[i] = *reinterpret_cast<const f16x8 *>(A + swz(wm * 64 + i * 16 + lr, ch));
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                bf[m][j] = *reinterpret_cast<const f16x8 *>(
-                    B + swz(m * FN + wn * (FN / WNW) + j * 16 + lr, ch));
-    };
-    f32x4 acc[NM][4][NJ];
-    auto mm = [&](const f16x8 *af, f16x8 (*bf)[NJ]) {
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[m][i][j] = mfma16(af[i], bf[m][j], acc[m][i][j]);
-    };
-    auto order = [&]() {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < NXL + NWL; ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8 - NXL - NWL, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    if (seq.first >= seq.end) return;
-    int g, mt, nt, kz;
-    decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, seq.first, g, mt, nt, kz);
-    Item<NM> cur = make_item<NM, EPI, GATHER>(a, g, mt, nt, kz, nk);
-    Item<NM> nxt = cur;
-    int inext = seq.first + seq.step;
-    bool primed = false;  // the pipeline already holds this item's first steps
-    int s0 = 0, s1 = 1, s2 = 2;  // stages of steps kt, kt+1, kt+2
-    for (;;) {
-        const bool has_nxt = chain && inext < seq.end;
-        if (has_nxt) {
-            decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, inext, g, mt, nt, kz);
-            nxt = make_item<NM, EPI, GATHER>(a, g, mt, nt, kz, nk);
-        }
-        if (!primed) {
-            gload(ra0, rb0, cur, nxt, false, 0);
-            gload(ra1, rb1, cur, nxt, false, 1);
-            lstore(ra0, rb0, s0);
-            lstore(ra1, rb1, s1);
-            gload(ra0, rb0, cur, nxt, has_nxt, 2);
-            __syncthreads();
-            fread(af0, bf0, s0, 0);
-        }
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kt = 0; kt < nk; kt += 2) {
-            fread(af1, bf1, s0, 4);
-            mm(af0, bf0);
-            fread(af0, bf0, s1, 0);
-            mm(af1, bf1);
-            lstore(ra0, rb0, s2);
-            gload(ra1, rb1, cur, nxt, has_nxt, kt + 3);
-            order();
-            fread(af1, bf1, s1, 4);
-            mm(af0, bf0);
-            fread(af0, bf0, s2, 0);
-            mm(af1, bf1);
-            lstore(ra1, rb1, s0);
-            gload(ra0, rb0, cur, nxt, has_nxt, kt + 4);
-            order();
-            // steps kt+2, kt+3, kt+4 sit in stages s2, s0, s1
-            const int t = s0;
-            s0 = s2;
-            s2 = s1;
-            s1 = t;
-        }
-
-        // ---- epilogue.  acc[m][i][j]: x row wm*64 + i*16 + 4*lg + q
-        // (q = 0..3), feature n0 + wn*FN/4 + j*16 + lr (A = x rows, B =
-        // weight rows).
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = cur.rs + wm * 64 + i * 16 + 4 * lg + q;
-                if (r >= cur.r1) continue;
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const int f = cur.n0 + wn * (FN / WNW) + j * 16 + lr;
-                    if (f >= a.N) continue;
-                    if (EPI == 2) {  // logits, fp32 partial of K slice kz
-                        reinterpret_cast<float *>(a.out)[(size_t)cur.kz * a.split_stride +
-                                                         (size_t)r * a.out_ld + f] =
-                            acc[0][i][j][q];
-                    } else {
-                        float v;
-                        if (EPI == 1)
-                            v = siluf_(acc[0][i][j][q]) * acc[NM - 1][i][j][q];
-                        else
-                            v = acc[0][i][j][q];
-                        reinterpret_cast<f16 *>(a.out)[(size_t)r * a.out_ld + f] = to_f16(v);
-                    }
-                }
-            }
-        }
-        if (!has_nxt && inext >= seq.end) break;
-        // the next item: chained (its first steps are already staged, its
-        // first fragments read) or restarted
-        primed = has_nxt;
-        if (!has_nxt) {
-            // restart: every stage is free (the last step's barrier came
-            // after every fragment read)
-            decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, inext, g, mt, nt, kz);
-            nxt = make_item<NM, EPI, GATHER>(a, g, mt, nt, kz, nk);
-            s0 = 0;
-            s1 = 1;
-            s2 = 2;
-        }
-        cur = nxt;
-        inext += seq.step;
-    }
-}
-
 // Tile geometry of the direct-to-LDS pipeline: K steps of BK, two LDS
 // stages of 64 KB for 256-row tiles, three of 48 KB for 128-row ones.
 template <int TBM>
 constexpr int n_stages() {
-    return MOE_TILED_DMA && TBM == 256 ? 2 : NSTAGE;
+    return TBM == 256 ? 2 : 3;
 }
 
 // ---- direct global -> LDS staging (gfx950 buffer/global loads with the lds
@@ -632,7 +375,7 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
     int g, mt, nt, kz;
     decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, seq.first, g, mt, nt, kz);
 
-    Item<NM> cur = make_item<NM, EPI, false, TBM>(a, g, mt, nt, kz, nk);
+    Item<NM> cur = make_item<NM, EPI, TBM>(a, g, mt, nt, kz, nk);
     Item<NM> nxt = cur;
     int inext = seq.first + seq.step;
     bool primed = false;
@@ -641,7 +384,7 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
         const bool has_nxt = chain && inext < seq.end;
         if (has_nxt) {
             decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, inext, g, mt, nt, kz);
-            nxt = make_item<NM, EPI, false, TBM>(a, g, mt, nt, kz, nk);
+            nxt = make_item<NM, EPI, TBM>(a, g, mt, nt, kz, nk);
         }
         if (!primed) {
             set_gather(cur);
@@ -688,7 +431,7 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
             wait_vm<0>();
             __syncthreads();
             decode_item(tstart, n_groups, n_ntiles, ks, seq.chunked, inext, g, mt, nt, kz);
-            nxt = make_item<NM, EPI, false, TBM>(a, g, mt, nt, kz, nk);
+            nxt = make_item<NM, EPI, TBM>(a, g, mt, nt, kz, nk);
             sc = 0;
         }
         cur = nxt;
@@ -764,12 +507,7 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
         seq.end = total;
         seq.chunked = false;
     }
-#if MOE_TILED_DMA
     run_items_dma<TBM, NM, EPI, GATHER>(a, As, Bs, tstart, n_groups, n_ntiles, ks, seq);
-#else
-    static_assert(TBM == BM, "register staging uses 128-row tiles");
-    run_items<NM, EPI, GATHER>(a, As, Bs, tstart, n_groups, n_ntiles, ks, seq);
-#endif
 }
 
 // max_tiles bounds the 128-row tiles (so also the taller ones): it only
@@ -822,13 +560,12 @@ bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype) {
 
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,
                              hipStream_t s) {
-    constexpr int XB = MOE_TILED_DMA ? MOE_TILED_EXPERT_ROWS : BM;  // expert GEMM tile rows
+    constexpr int XB = kExpertRows;
     if (mode == STREAM_SWIGLU)
         return a.gather ? launch_t<XB, 2, 1, true>(a, n_groups, max_tiles, s)
                         : launch_t<XB, 2, 1, false>(a, n_groups, max_tiles, s);
     if (mode == STREAM_STORE) return launch_t<XB, 1, 0, false>(a, n_groups, max_tiles, s);
-    constexpr int RB = MOE_TILED_DMA ? MOE_TILED_ROUTER_ROWS : BM;  // router tile rows
-    return launch_t<RB, 1, 2, false>(a, n_groups, max_tiles, s);
+    return launch_t<kTiledRouterRows, 1, 2, false>(a, n_groups, max_tiles, s);
 }
 
 }  // namespace moe

@@ -46,10 +46,8 @@ hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int m
 
 // LDS-tiled persistent variant for groups of many rows (fp16 only; K split
 // for router logits).  max_tiles bounds the total 128-row tiles (sizes the
-// grid).  Router logits use tiles of MOE_TILED_ROUTER_ROWS rows.
-#ifndef MOE_TILED_ROUTER_ROWS
-#define MOE_TILED_ROUTER_ROWS 128
-#endif
+// grid).  Router logits use tiles of kTiledRouterRows rows.
+constexpr int kTiledRouterRows = 128;
 bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype);
 bool tiled_gemm_supported_shape(int K, int dtype, int x_dtype);
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,

@@ -27,18 +27,12 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline int act_bytes(const moe_shape &s) { return s.act == MOE_F32 ? 4 : 2; }
 inline int has_gate(const moe_shape &s) { return (s.flags & MOE_F_SHARED) ? 1 : 0; }
 
-// Largest router K split (compile-time tuning knob).
-#ifndef MOE_ROUTER_MAX_SPLIT
-#define MOE_ROUTER_MAX_SPLIT 16
-#endif
-// Smallest batch that takes the LDS-tiled router (compile-time tuning knob).
-#ifndef MOE_ROUTER_TILED_MIN_T
-#define MOE_ROUTER_TILED_MIN_T 2048
-#endif
+constexpr int kRouterMaxSplit = 16;      // largest router K split
+constexpr int kRouterTiledMinT = 2048;   // smallest batch on the LDS-tiled router
 
 // Router plan.  Large batches (T >= 2048, fp16) use the LDS-tiled kernel
 // and small ones the weight-stream kernel; either way K is split (slices a
-// multiple of the kernel's K granularity, at most MOE_ROUTER_MAX_SPLIT) so
+// multiple of the kernel's K granularity, at most kRouterMaxSplit) so
 // that the workgroup count comes closest to 256.  The top-K kernel sums the
 // slices in order.
 struct RouterPlan {
@@ -49,8 +43,8 @@ struct RouterPlan {
 RouterPlan router_plan(const moe_shape &s, int T) {
     const int N = s.n_experts + has_gate(s);
     RouterPlan p;
-    p.tiled = T >= MOE_ROUTER_TILED_MIN_T && tiled_gemm_supported_shape(s.hidden, s.act, s.act);
-    const int tr = MOE_TILED_ROUTER_ROWS;
+    p.tiled = T >= kRouterTiledMinT && tiled_gemm_supported_shape(s.hidden, s.act, s.act);
+    const int tr = kTiledRouterRows;
     const long base = p.tiled ? (long)((N + 255) / 256) * ((T + tr - 1) / tr)
                               : (long)((N + 63) / 64) * ((T + 63) / 64);
     // fp16 stream path: K slices that are multiples of 512 let the 4 waves of
@@ -62,7 +56,7 @@ RouterPlan router_plan(const moe_shape &s, int T) {
     // 224 blocks beat 112 and 448 at decode sizes)
     p.ksplit = 1;
     long best = -1;
-    for (int d = 1; d <= MOE_ROUTER_MAX_SPLIT; ++d) {
+    for (int d = 1; d <= kRouterMaxSplit; ++d) {
         if (s.hidden % (d * gran)) continue;
         const long dist = base * d > 256 ? base * d - 256 : 256 - base * d;
         if (best < 0 || dist < best) {

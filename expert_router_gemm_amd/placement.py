@@ -13,7 +13,7 @@ expert's list is [home copy, extra slot].
 """
 from __future__ import annotations
 
-from typing import Iterable, Optional, Sequence
+from typing import Optional, Sequence
 
 import numpy as np
 
@@ -58,7 +58,3 @@ def drop_replica(rep_off: np.ndarray, rep_slot: np.ndarray, expert: int, which: 
     off = rep_off.copy()
     off[expert + 1:] -= 1
     return off, slot
-
-
-def local_experts(slot_experts: Iterable[int]) -> list:
-    return [int(e) for e in slot_experts]

@@ -89,14 +89,60 @@ def test_decode_bytes_follow_the_pages_per_expert_figure():
     per_expert = 3 * 7168 * 2048 * 2  # EP blog section 6.3: 88 MB per expert
     assert per_expert == 88_080_384
     counts = np.full(32, 8, np.int32)  # every slot touched, P = 256
-    work = bench.algorithmic_work({"cfg": cfg, "b": {"counts": torch.from_numpy(counts)}})
-    T, K, H, P = cfg.T, cfg.K, cfg.H, 256
+    work = bench.algorithmic_work(cfg, counts)
+    T, H, P = cfg.T, cfg.H, 256
     assert (work["P"], work["touched"]) == (P, 32)
     vec = T * H * 2  # one [256, 7168] fp16 array: router weights, h, output
-    # the layer: every touched expert once, router weights, h and the output,
-    # plus the expert-output round trip and the routing outputs
-    assert work["layer_bytes"] - 2 * P * H * 2 - T * K * 8 == 32 * per_expert + 3 * vec
+    # the layer: every touched expert once, router weights, h and the
+    # output; the expert-output round trip and the routing outputs are time
+    assert work["layer_bytes"] == 32 * per_expert + 3 * vec == 2_829_582_336
     # gate/up launch: two of the three matrices per touched expert, the
     # gathered rows and the SwiGLU output
     assert work["up"]["bytes"] == 32 * per_expert * 2 // 3 + P * H * 2 + P * cfg.I * 2
     assert work["up"]["flops"] == 2 * 2 * P * H * cfg.I
+
+
+def test_full_layer_bytes_count_the_touched_and_shared_experts():
+    """Whole layer at decode (T = 128, 256 experts, 2 shared): touched
+    experts + the shared experts (section 2.1: 176 MB for two) + router +
+    h + out.  The shared experts ride in the routed gate/up launch."""
+    cfg = moe_synth.config(3)
+    counts = np.zeros(256, np.int32)
+    counts[:238] = 4
+    counts[0] += 1024 - 4 * 238  # P = T * K = 1024 over 238 touched experts
+    work = bench.algorithmic_work(cfg, counts)
+    assert work["touched"] == 238 and work["P"] == 1024
+    assert work["layer_bytes"] == 238 * 88_080_384 + 176_160_768 + 3_670_016 + 2 * 1_835_008
+    assert bench.shared_in_routed_launch(cfg)
+    H, I, T = cfg.H, cfg.I, cfg.T
+    assert work["up"]["bytes"] == ((238 + 2) * 2 * I * H * 2 + (1024 + 2 * T) * (H + I) * 2)
+
+
+def test_replica_fp8_bytes_follow_the_survey_figure():
+    """Imbalanced decode with one replica slot and fp8 rows: 33 touched
+    slots; the layer figure is 33 experts + router + h + out, and the
+    gate/up launch reads one byte per element of each fp8 row plus its
+    fp32 scale."""
+    cfg = moe_synth.config(5)
+    counts = np.full(33, 16, np.int32)
+    work = bench.algorithmic_work(cfg, counts)
+    assert work["layer_bytes"] == 2_925_002_752
+    P, H, I = 33 * 16, cfg.H, cfg.I
+    assert not bench.shared_in_routed_launch(cfg)
+    assert work["up"]["bytes"] == 33 * 2 * I * H * 2 + P * (H + 4) + P * I * 2
+
+
+def test_cpu_baseline_runs_single_and_multi_threaded():
+    """The oracle baseline leg on the tiny workload's host inputs: one
+    thread first, then several threads on disjoint token blocks."""
+    import oracle
+    cfg = moe_synth.config(1)
+    rep_off, rep_slot, slot_experts = oracle.placement(cfg.E, 1, 0)
+    ctx = dict(cfg=cfg, rep=None, h=moe_synth.gen_hidden(cfg), wr=moe_synth.gen_router(cfg),
+               bias=moe_synth.gen_router_bias(cfg), shared=moe_synth.gen_shared_weights(cfg),
+               host_experts={int(e): moe_synth.gen_expert(cfg, int(e)) for e in slot_experts})
+    rec = bench.cpu_baseline(ctx, budget_s=0.3)
+    assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s"
+    assert rec["value"] > 0 and rec["single_thread"]["value"] > 0
+    assert 1 <= rec["cores"] <= 16 and rec["single_thread"]["cores"] == 1
+    assert rec["cpu_model"]
