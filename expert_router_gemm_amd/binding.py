@@ -21,6 +21,7 @@ MOE_X_PERMUTED, MOE_X_SHARED, MOE_X_GATHER = 0, 1, 2
 EXPORTED = (
     "moe_route", "moe_dispatch", "moe_expert_ffn_up", "moe_expert_ffn_down",
     "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_profiled",
+    "moe_layer_forward_noalloc",
     "moe_workspace_bytes", "moe_status_str", "moe_version", "moe_expert_counts",
     "moe_eplb_state_bytes", "moe_eplb_init", "moe_eplb_observe", "moe_eplb_loads",
     "moe_eplb_rebalance", "moe_eplb_slot_map",
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward_profiled.argtypes = [SP, ctypes.POINTER(Weights),
                                                  ctypes.POINTER(SlotMap), I32, P, P, P, SZ,
                                                  ctypes.POINTER(Profile), P]
+        L.moe_layer_forward_noalloc.argtypes = [SP, ctypes.POINTER(Weights),
+                                                ctypes.POINTER(SlotMap), I32, P, P, P]
         L.moe_workspace_bytes.argtypes = [SP, I32]
         L.moe_workspace_bytes.restype = SZ
         L.moe_expert_counts.argtypes = [SP, I32, P, P, P]
@@ -208,6 +211,18 @@ def moe_layer_forward(shape, weights: Weights, slot_map: SlotMap, T, h, out, ws,
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(shape), ctypes.byref(weights), ctypes.byref(slot_map), T, _p(h), _p(out),
         _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_layer_forward_noalloc(shape, weights: Weights, slot_map: SlotMap, T, h, out,
+                              stream=None):
+    """moe_layer_forward with the library's own static device workspace
+    (for callers that cannot allocate; see include/moe.h)."""
+    _check("moe_layer_forward_noalloc", lib().moe_layer_forward_noalloc(
+        ctypes.byref(shape), ctypes.byref(weights), ctypes.byref(slot_map), T, _p(h), _p(out),
+        _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def make_profile(events) -> Profile:

@@ -19,8 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["moe_api.cpp", "eplb.cpp", "gemm_stream.hip", "gemm_tiled.hip", "route_topk.hip",
-           "dispatch.hip", "combine.hip", "expert_counts.hip"]
+SOURCES = ["moe_api.cpp", "noalloc.hip", "eplb.cpp", "gemm_stream.hip", "gemm_tiled.hip",
+           "route_topk.hip", "dispatch.hip", "combine.hip", "expert_counts.hip"]
 
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "../../include/moe.h"
+#include "api_internal.h"
 #include "kernels.h"
 
 #define MOE_EXPORT extern "C" __attribute__((visibility("default")))
@@ -527,16 +528,10 @@ MOE_EXPORT moe_status moe_expert_counts(const moe_shape *shape, int32_t T,
     return MOE_OK;
 }
 
-namespace {
-moe_status layer_forward_impl(const moe_shape *shape, const moe_weights *w,
-                              const moe_slot_map *map, int32_t T, const void *h, void *out,
-                              void *ws, size_t ws_bytes, const moe_profile *prof, void *stream);
-}
-
 MOE_EXPORT moe_status moe_layer_forward(const moe_shape *shape, const moe_weights *w,
                                         const moe_slot_map *map, int32_t T, const void *h,
                                         void *out, void *ws, size_t ws_bytes, void *stream) {
-    return layer_forward_impl(shape, w, map, T, h, out, ws, ws_bytes, nullptr, stream);
+    return moe::layer_forward_run(shape, w, map, T, h, out, ws, ws_bytes, nullptr, stream);
 }
 
 MOE_EXPORT moe_status moe_layer_forward_profiled(const moe_shape *shape, const moe_weights *w,
@@ -545,18 +540,17 @@ MOE_EXPORT moe_status moe_layer_forward_profiled(const moe_shape *shape, const m
                                                  size_t ws_bytes, const moe_profile *prof,
                                                  void *stream) {
     if (!prof) return MOE_ERR_INVALID_ARG;
-    return layer_forward_impl(shape, w, map, T, h, out, ws, ws_bytes, prof, stream);
+    return moe::layer_forward_run(shape, w, map, T, h, out, ws, ws_bytes, prof, stream);
 }
 
-namespace {
-moe_status layer_forward_impl(const moe_shape *shape, const moe_weights *w,
-                              const moe_slot_map *map, int32_t T, const void *h, void *out,
-                              void *ws, size_t ws_bytes, const moe_profile *prof, void *stream) {
+namespace moe {
+
+moe_status layer_forward_validate(const moe_shape *shape, const moe_weights *w,
+                                  const moe_slot_map *map, int32_t T, const void *h, void *out) {
     TRY(check_shape(shape));
     TRY(check_T(T));
     if (!w || !map) return MOE_ERR_INVALID_ARG;
-    if (T == 0) return MOE_OK;  // no token: empty output
-    const moe_shape &s = *shape;
+    if (T == 0) return MOE_OK;  // no token: nothing else is read
     TRY(need(h));
     TRY(need(out));
     TRY(need(w->w_router));
@@ -566,12 +560,21 @@ moe_status layer_forward_impl(const moe_shape *shape, const moe_weights *w,
     TRY(need(w->w_down));
     TRY(need4(map->rep_off));
     TRY(need4(map->rep_slot));
-    const int gate = has_gate(s);
-    if (gate) {
+    if (has_gate(*shape)) {
         TRY(need(w->sh_gate));
         TRY(need(w->sh_up));
         TRY(need(w->sh_down));
     }
+    return MOE_OK;
+}
+
+moe_status layer_forward_run(const moe_shape *shape, const moe_weights *w,
+                             const moe_slot_map *map, int32_t T, const void *h, void *out,
+                             void *ws, size_t ws_bytes, const moe_profile *prof, void *stream) {
+    TRY(layer_forward_validate(shape, w, map, T, h, out));
+    if (T == 0) return MOE_OK;  // no token: empty output
+    const moe_shape &s = *shape;
+    const int gate = has_gate(s);
     const Layout L = layout(s, T);
     if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
@@ -655,4 +658,4 @@ moe_status layer_forward_impl(const moe_shape *shape, const moe_weights *w,
 #undef MARK
     return MOE_OK;
 }
-}  // namespace
+}  // namespace moe

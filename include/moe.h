@@ -16,7 +16,13 @@
  * Conventions for every call
  *   - Pointers are DEVICE memory unless marked (host).  The caller allocates
  *     and owns every buffer; the library never allocates, frees or
- *     synchronises, and keeps no state between calls (thread-safe).
+ *     synchronises.  State it keeps across calls, per device: the number of
+ *     resident workgroups of each LDS-tiled GEMM kernel (counted, after
+ *     raising the kernel's dynamic LDS limit with hipFuncSetAttribute, on
+ *     the first launch of that kernel on the device; later calls read it),
+ *     and the device address of moe_layer_forward_noalloc's static
+ *     workspace array.  Both are set up race-free; every entry point may be
+ *     called from several host threads.
  *   - Matrices are row-major and "out-major": a weight that maps an input of
  *     length n to m outputs is stored [m][n], i.e. the transpose of the
  *     page's [in, out] math shapes (router [7168, 256], gate/up
@@ -221,6 +227,24 @@ moe_status moe_layer_forward_profiled(const moe_shape *shape, const moe_weights 
                                       const moe_slot_map *map, int32_t T, const void *h,
                                       void *out, void *ws, size_t ws_bytes,
                                       const moe_profile *prof, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as moe_layer_forward -- same kernels and order, so the output is
+ * bitwise equal -- with the workspace held by the library: one static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES per device, kept until the
+ * process ends and looked up on the first call on each device.  Nothing is
+ * allocated or freed.  Shapes whose moe_workspace_bytes(shape, T) exceeds
+ * the array return MOE_ERR_WORKSPACE with nothing enqueued (64 MiB holds
+ * DeepSeek-V3 decode batches up to 256 tokens: 39.5 MiB for one EP=8
+ * rank's 32 experts, 48.6 MiB for the whole layer with 2 shared experts).
+ * Every call on one device uses the same array: calls that overlap on a
+ * GPU (other streams, other threads) race and must be ordered by the
+ * caller.  Other arguments and errors as moe_layer_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_forward_noalloc(const moe_shape *shape, const moe_weights *weights,
+                                     const moe_slot_map *map, int32_t T, const void *h,
+                                     void *out, void *stream);
 
 /* ------------------------------------------------------------------
  * EPLB-lite: the load balancer of section 6.2 with the redundant copies of

@@ -190,3 +190,25 @@ def test_expert_counts_validates_before_launch():
     assert L.moe_expert_counts(ctypes.byref(s), 16, None, FAKE, None) == 1   # indices missing
     assert L.moe_expert_counts(ctypes.byref(s), 16, FAKE, FAKE + 2, None) == 4
     assert L.moe_expert_counts(ctypes.byref(_shape(hidden=100)), 16, FAKE, FAKE, None) == 2
+
+
+def test_noalloc_entry_validates_before_touching_a_device():
+    """moe_layer_forward_noalloc: the argument checks of moe_layer_forward
+    first (nothing looked up on a device), then the workspace limit of its
+    static array (64 MiB: DeepSeek-V3 decode up to 256 tokens)."""
+    L = moe.lib()
+    s = _shape()
+    sm = moe.SlotMap(FAKE, FAKE, 0)
+    w = moe.Weights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)
+    fwd = lambda shape, T, h=FAKE, out=FAKE, wts=w: L.moe_layer_forward_noalloc(  # noqa: E731
+        ctypes.byref(shape), ctypes.byref(wts), ctypes.byref(sm), T, h, out, None)
+    assert fwd(_shape(hidden=100), 16) == 2                    # shape
+    assert fwd(s, -1) == 2                                     # T
+    assert fwd(s, 16, h=None) == 1                             # input missing
+    assert fwd(s, 16, out=FAKE + 8) == 4                       # output misaligned
+    assert fwd(_shape(n_shared=2, shared=True), 16) == 1       # shared weights missing
+    assert fwd(s, 0) == 0                                      # no token: nothing to do
+    assert moe.MOE_NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert moe.moe_workspace_bytes(s, 256) <= moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert moe.moe_workspace_bytes(s, 1024) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert fwd(s, 1024) == 5                                   # beyond the array
