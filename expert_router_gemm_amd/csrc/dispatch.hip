@@ -50,6 +50,22 @@ __device__ __forceinline__ int slot_of(const DispatchArgs &a, int t, int k) {
     return (s >= 0 && s < a.S) ? s : -1;
 }
 
+// A token's pairs must land in distinct slots (its K experts are distinct,
+// and a slot holds one expert).  Should two of them meet in one slot anyway
+// (repeated ids in a caller's topk_idx, or a table listing a slot under two
+// experts), the later pair is not dispatched: its slot becomes -1, so every
+// row still belongs to exactly one pair and the result stays deterministic.
+template <int KMAX>
+__device__ __forceinline__ void drop_repeated_slots(int (&sl)[KMAX], int K = KMAX) {
+#pragma unroll
+    for (int k = 1; k < KMAX; ++k) {
+        if (k >= K) continue;
+#pragma unroll
+        for (int j = 0; j < k; ++j)
+            if (sl[k] >= 0 && sl[k] == sl[j]) sl[k] = -1;
+    }
+}
+
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchArgs a) {
     extern __shared__ unsigned long long masks[];  // [4][S]
     const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -63,10 +79,11 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchArgs a) {
     // the token's slots, kept in registers for the ranking pass (top_k <= 16)
     int sk[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        sk[k] = (t < a.T && k < a.K) ? slot_of(a, t, k) : -1;
+    for (int k = 0; k < 16; ++k) sk[k] = (t < a.T && k < a.K) ? slot_of(a, t, k) : -1;
+    drop_repeated_slots<16>(sk);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
         if (sk[k] >= 0) atomicOr(&m[sk[k]], bit);
-    }
     __syncthreads();
     if (t < a.T)
 #pragma unroll
@@ -272,8 +289,11 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
                 }
             }
             sls[k] = sl;
-            if (sl >= 0) atomicOr(&masks[wave][sl], bit);
         }
+        drop_repeated_slots<KMAX>(sls, K);
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (k < K && sls[k] >= 0) atomicOr(&masks[wave][sls[k]], bit);
     }
     __syncthreads();
     // per slot: exclusive scan over chunks, total

@@ -22,6 +22,9 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxShared = 16;
 constexpr int kMaxGroupsRoute = 64;  // expert groups of group-limited routing
 constexpr int64_t kMaxTokens = 1 << 20;
+// hidden and inter: the LDS-tiled GEMM forms a tile's byte ranges and row
+// offsets (up to 256 rows of K fp16 values) in 32 bits
+constexpr int kMaxDim = 65536;
 
 inline size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -78,6 +81,7 @@ moe_status check_shape(const moe_shape *s) {
     if (!s) return MOE_ERR_INVALID_ARG;
     if (s->flags & ~MOE_F_SHARED) return MOE_ERR_INVALID_ARG;
     if (s->hidden <= 0 || s->inter <= 0 || s->hidden % 128 || s->inter % 128) return MOE_ERR_SHAPE;
+    if (s->hidden > kMaxDim || s->inter > kMaxDim) return MOE_ERR_SHAPE;
     if (s->n_experts < 1 || s->n_experts > kMaxExperts) return MOE_ERR_SHAPE;
     if (s->top_k < 1 || s->top_k > kMaxTopK || s->top_k > s->n_experts) return MOE_ERR_SHAPE;
     if (s->n_slots < 1 || s->n_slots > kMaxSlots) return MOE_ERR_SHAPE;

@@ -38,9 +38,15 @@
  *     MOE_ERR_LAUNCH if a kernel launch was rejected.  Nothing is enqueued
  *     when validation fails.  Faults inside kernels surface at the caller's
  *     next synchronisation of the stream.  No C++ exception crosses the ABI.
- *   - Limits: hidden and inter positive multiples of 128;
+ *   - Limits: hidden and inter positive multiples of 128, at most 65536;
  *     1 <= top_k <= min(E, 16); E <= 1024; 1 <= S <= 1024; n_shared <= 16;
  *     0 <= T <= 2^20 (T = 0 is valid: no token, nothing routed).
+ *   - Routing preconditions: a token's top_k experts are distinct (the
+ *     router never repeats one) and each local slot is listed under one
+ *     expert (a slot holds one expert's weights).  Dispatch keeps its
+ *     output well defined when they are broken: of two pairs of one token
+ *     that would meet in one slot, only the earlier k is dispatched (the
+ *     later gets inv_pos = -1 and contributes nothing).
  */
 #ifndef MOE_H
 #define MOE_H

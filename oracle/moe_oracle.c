@@ -472,12 +472,23 @@ int oref_layer_forward(const oref_dims *d, const void *h, const int32_t *tok_ids
     oref_softmax_topk_grouped(T, E, K, d->n_groups, d->topk_groups, logits, idx, w);
     oref_slot_map(T, K, idx, tok_ids, rep_off, rep_slot, seed, slot);
 
+    /* A token's K experts are distinct (Step 1 picks K different experts)
+     * and a slot holds one expert's weights, so no slot receives a token
+     * twice and a slot holds at most T rows.  Inputs that break this (a
+     * slot table listing one slot under two experts) are refused. */
+    for (int t = 0; t < T && rc == 0; ++t)
+        for (int k = 1; k < K && rc == 0; ++k)
+            for (int j = 0; j < k; ++j)
+                if (slot[(size_t)t * K + k] >= 0 &&
+                    slot[(size_t)t * K + k] == slot[(size_t)t * K + j])
+                    rc = -2;
+
     for (size_t j = 0; j < (size_t)T * H; ++j)
         out[j] = 0.0f;
     double *acc = (double *)calloc((size_t)T * H + 1, sizeof(double));
 
     /* routed experts, slot-outer so each slot's weights are walked once */
-    /* a slot receives each token at most once, so R <= T rows */
+    /* a slot receives each token at most once (checked above), so R <= T */
     double *x = (double *)malloc(sizeof(double) * (size_t)T * H + 1);
     float *y = (float *)malloc(sizeof(float) * (size_t)T * H + 1);
     int32_t *pair = (int32_t *)malloc(sizeof(int32_t) * (size_t)T * K + 1);

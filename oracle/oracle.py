@@ -345,6 +345,9 @@ def layer_forward(*, h: np.ndarray, w_router: np.ndarray, bias, w_sg,
         _ptr(sh[0]), _ptr(sh[1]), _ptr(sh[2]), _ptr(_c(rep_off, np.int32)),
         _ptr(_c(rep_slot, np.int32)), seed, _ptr(out), _ptr(idx), _ptr(w),
         _ptr(slot), _ptr(logits), _ptr(gs))
+    if rc == -2:
+        raise ValueError("oracle: two pairs of one token land in one slot (a token's experts "
+                         "are distinct and a slot holds one expert)")
     if rc != 0:
         raise RuntimeError("oracle: a pair was routed to a slot without weights")
     return dict(out=out, topk_idx=idx, topk_w=w, slot=slot, logits=logits,

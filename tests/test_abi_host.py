@@ -79,6 +79,7 @@ def _route(shape, T=16, **ptr):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(hidden=7000), 2), (dict(inter=100), 2), (dict(top_k=0), 2), (dict(top_k=17), 2),
+    (dict(hidden=65536 + 128), 2), (dict(inter=65536 + 128), 2), (dict(hidden=1 << 22), 2),
     (dict(n_experts=4, top_k=8), 2), (dict(n_experts=2048), 2), (dict(n_slots=0), 2),
     (dict(n_slots=2000), 2), (dict(act=7), 3), (dict(act=0, dispatch=2), 3),
     (dict(shared=True, n_shared=0), 2),
@@ -88,6 +89,14 @@ def _route(shape, T=16, **ptr):
 ])
 def test_route_rejects_bad_shapes(kw, status):
     assert _route(_shape(**kw)) == status
+
+
+def test_largest_hidden_and_inter_are_accepted():
+    """65536 is the largest hidden / inter size (32-bit tile offsets)."""
+    big = _shape(hidden=65536, inter=65536)
+    assert moe.moe_workspace_bytes(big, 16) > 0
+    assert moe.moe_workspace_bytes(_shape(hidden=65536 + 128), 16) == 0
+    assert _route(big, T=0, ws=None) == 0
 
 
 def test_route_accepts_group_limits():

@@ -535,3 +535,26 @@ def test_combine_consistent_with_layer():
     # no local pair and no shared term: exact zeros
     z = oracle.combine(y, np.full_like(inv, -1), res["topk_w"])
     assert np.all(z == 0)
+
+
+def test_layer_refuses_a_token_meeting_one_slot_twice():
+    """A token's experts are distinct (Step 1) and a slot holds one expert,
+    so a slot sees a token at most once; a table listing slot 0 under
+    experts 0 and 1 breaks that for every token routed to both, and the
+    oracle refuses it rather than summing the slot twice (or overrunning
+    its per-slot row buffers)."""
+    T, H, I, E, K = 6, 16, 8, 4, 2
+    rng = np.random.default_rng(3)
+    h = rng.standard_normal((T, H)).astype(np.float32)
+    wr = rng.standard_normal((E, H)).astype(np.float32)
+    bias = np.array([50.0, 40.0, 0.0, 0.0], np.float32)  # experts 0 and 1 win every token
+    ex = [tuple(rng.standard_normal(s).astype(np.float32) for s in ((I, H), (I, H), (H, I)))
+          for _ in range(2)]
+    kw = dict(h=h, w_router=wr, bias=bias, w_sg=None, slot_weights=ex, shared=None, seed=0,
+              K=K, fp8_dispatch=False)
+    ok = oracle.layer_forward(rep_off=np.arange(E + 1, dtype=np.int32),
+                              rep_slot=np.array([0, 1, -1, -1], np.int32), **kw)
+    assert np.all(np.sort(ok["topk_idx"], 1) == [0, 1])
+    with pytest.raises(ValueError, match="one slot"):
+        oracle.layer_forward(rep_off=np.arange(E + 1, dtype=np.int32),
+                             rep_slot=np.array([0, 0, -1, -1], np.int32), **kw)
