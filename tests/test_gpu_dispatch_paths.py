@@ -99,14 +99,15 @@ def test_dispatch_drops_the_later_pair_of_a_repeated_slot(T):
     shape = moe.make_shape(hidden=H, inter=128, n_experts=E, top_k=K, n_slots=S)
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     h = torch.zeros((T, H), dtype=torch.float16, device="cuda")
-    sm = moe.make_slot_map(d(rep_off), d(rep_slot), seed)
+    ro, rs, tk = d(rep_off), d(rep_slot), d(topk)  # kept alive: the map holds raw pointers
+    sm = moe.make_slot_map(ro, rs, seed)
     counts = torch.full((S,), -7, dtype=torch.int32, device="cuda")
     offsets = torch.full((S + 1,), -7, dtype=torch.int32, device="cuda")
     perm = torch.full((T * K,), -7, dtype=torch.int32, device="cuda")
     inv = torch.full((T, K), -7, dtype=torch.int32, device="cuda")
     ws = torch.empty(moe.moe_workspace_bytes(shape, T), dtype=torch.uint8, device="cuda")
     print(f"[dispatch repeated slots] T={T} dropped={(keep != slot).sum()}", flush=True)
-    moe.moe_dispatch(shape, T, h, d(topk), sm, None, None, counts, offsets, perm, inv, ws)
+    moe.moe_dispatch(shape, T, h, tk, sm, None, None, counts, offsets, perm, inv, ws)
     torch.cuda.synchronize()
     P = int(offsets_r[S])
     assert np.array_equal(counts.cpu().numpy(), counts_r)

@@ -361,15 +361,54 @@ def test_expert_count_not_a_multiple_of_the_wave(groups):
 
 
 FULL_SAMPLE = {2: 32, 3: 12, 4: 24, 5: 32}
+TILE_ROWS = 256  # row tile of the LDS-tiled expert GEMMs
+
+
+def _strata_rows(offsets, rng, tile=TILE_ROWS):
+    """Rows that cover every (slot, row tile): the first and last row of
+    each tile of each non-empty slot, plus one drawn at random."""
+    rows = []
+    for s in range(len(offsets) - 1):
+        a, b = int(offsets[s]), int(offsets[s + 1])
+        for t0 in range(a, b, tile):
+            t1 = min(b, t0 + tile)
+            rows += [t0, t1 - 1, int(rng.integers(t0, t1))]
+    return np.unique(np.asarray(rows, np.int64))
+
+
+def _check_ffn_rows(L, st, rows):
+    """hm and y of the given dispatched rows against the oracle's SwiGLU on
+    the GPU's own dispatched inputs (fp8: its codes and scales), expert by
+    expert (regenerated one at a time, not kept).  Returns max |d| of y."""
+    cfg = L.cfg
+    off = st["offsets"]
+    slot_of_row = np.searchsorted(off, rows, side="right") - 1
+    dec = oracle.e4m3_decode_table() if cfg.dispatch == "fp8" else None
+    need = sorted(set(int(s) for s in slot_of_row))
+    worst = 0.0
+    for e, w in moe_synth.iter_experts(cfg, [int(L.slot_experts[s]) for s in need]):
+        for s in [s for s in need if int(L.slot_experts[s]) == e]:
+            r = rows[slot_of_row == s]
+            if cfg.dispatch == "fp8":
+                x = dec[st["x_perm"][r]].astype(np.float32) * st["x_scale"][r, None]
+            else:
+                x = L.h[st["perm_src"][r] // cfg.K]
+            y, hm = oracle.expert_rows(x.astype(np.float64), *w, want_hm=True)
+            gh.assert_close(st["hm"][r], hm, f"hm slot {s} rows {r.min()}..{r.max()}")
+            worst = max(worst, gh.assert_close(st["y"][r], y, f"y slot {s}"))
+    return worst
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("n,groups", [(2, None), (5, None), (4, None), (3, None), (2, (8, 4))])
 def test_full_size_sampled(n, groups):
     """Full workload sizes in the launch configuration the benchmark times
-    (with --groups G,M for the group-limited case); routing of a token sample
-    and the whole dispatch are compared exactly, layer outputs on the sample
-    within the output bar."""
+    (with --groups G,M for the group-limited case):
+      * routing of a token sample and the whole dispatch exactly;
+      * the expert GEMMs (hm and y, every feature) on rows of every
+        (slot, 256-row tile): the full-length K loops and workgroups that
+        chain several items, element by element;
+      * layer outputs on the token sample within the output bar."""
     cfg = moe_synth.config(n)
     if groups:
         cfg = moe_synth.config(n, n_groups=groups[0], topk_groups=groups[1])
@@ -382,10 +421,19 @@ def test_full_size_sampled(n, groups):
     tok = np.sort(rng.choice(cfg.T, FULL_SAMPLE[n], replace=False))
     tie = _check_routing(L, st, tokens=tok)
     _check_dispatch(L, st)
-    ref = oracle_sample = gh.oracle_forward(L, tokens=tok)
-    _ = oracle_sample
+    rows = _strata_rows(st["offsets"], rng)
+    if st["hm_gather"] is not None:  # rows gathered from h give the same hm
+        assert np.array_equal(st["hm_gather"].view(np.uint8), st["hm"].view(np.uint8))
+    dy = _check_ffn_rows(L, st, rows)
+    for j in range(cfg.n_shared):  # shared experts: every token is a row
+        t = _strata_rows(np.array([0, cfg.T]), rng, tile=64)
+        y = oracle.expert_rows(L.h[t].astype(np.float64), *[m[j] for m in L.shared])
+        gh.assert_close(st["shared_y"][j * cfg.T + t], y, f"shared expert {j}")
+    L.experts.clear()
+    ref = gh.oracle_forward(L, tokens=tok)
     err = gh.assert_close(out[tok], ref["out"], "layer output (sample)", rows=~tie)
-    print(f"[full] workload {n} P={st['P']} sample={len(tok)} max|d|={err:.3e}")
+    print(f"[full] workload {n} P={st['P']} ffn rows={len(rows)} (max |dy| {dy:.3e}) "
+          f"sample={len(tok)} max|d|={err:.3e}")
 
 
 @pytest.mark.slow
