@@ -277,7 +277,7 @@ def time_workload(ctx, K: int, warmup: int, references: bool = True):
         if references:
             staged_step(ctx)
     torch.cuda.synchronize()
-    EVERY = 5
+    EVERY = max(1, K // 5)
     ev_up = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for i in range(0, K, EVERY)}
     no_ev = moe.make_profile([])
@@ -557,6 +557,112 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int
     print(json.dumps(rec, indent=2))
 
 
+def kernel_label(name: str) -> str:
+    """Short label of a libmoe kernel from its rocprofv3 name (demangled or
+    mangled): the GEMM kind and epilogue, else the kernel's own name."""
+    import re
+    n = name.replace(" ", "")
+    if "tiled_gemm_kernel" in n:
+        m = re.search(r"tiled_gemm_kernel<(\d+),(\d+),(\d+),(true|false)>", n) or re.search(
+            r"tiled_gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELb([01])E", n)
+        if m:
+            epi = {"0": "down", "1": "gate/up", "2": "router"}[m.group(3)]
+            return f"tiled_gemm_kernel {epi} ({m.group(1)}-row tiles)"
+    if "stream_gemm_kernel" in n:
+        m = re.search(r"stream_gemm_kernel<[^,]+,(\d+),(\d+),(\d+),", n) or re.search(
+            r"stream_gemm_kernelI(?:DF16_|f)Li(\d+)ELi(\d+)ELi(\d+)E", n)
+        if m:
+            epi = {"0": "down", "1": "gate/up", "2": "router"}[m.group(3)]
+            return f"stream_gemm_kernel {epi}"
+    for k in ("topk_kernel", "dispatch_small_kernel", "dispatch_rank_kernel",
+              "dispatch_place_kernel", "dispatch_scan_kernel", "dispatch_index_kernel",
+              "dispatch_rows_kernel", "combine_kernel", "counts_kernel"):
+        if k in n:
+            return k
+    return ""
+
+
+def summarize_pmc_all(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int):
+    """FETCH_SIZE / WRITE_SIZE per launch of every libmoe kernel of the run
+    (medians), scaled by the calibration copy; writes
+    profiles/traffic_layer_kernels_<workload>.json."""
+    import csv
+    import collections
+
+    out = collections.defaultdict(dict)
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals, cp = collections.defaultdict(list), []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r.get("Counter_Name") != counter:
+                        continue
+                    name = r.get("Kernel_Name", "")
+                    v = float(r["Counter_Value"])
+                    if "AUnaryFunctor" in name and "MulFunctor" in name:
+                        cp.append(v)
+                    elif kernel_label(name):
+                        vals[kernel_label(name)].append(v)
+        if not cp:
+            raise SystemExit(f"no calibration copy rows for {counter} in {d}")
+        factor = copy_bytes / 1024.0 / statistics.median(cp)
+        for k, v in vals.items():
+            out[k][counter + "_bytes"] = statistics.median(v) * 1024.0 * factor
+            out[k][counter + "_launches"] = len(v)
+        out["_copy_factor"][counter] = factor
+    rec = dict(workload=workload, kernels=dict(out),
+               command=("cd /tmp && rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format "
+                        "csv -d DIR -o run -- python3 bench.py --workload N --steps 3 --warmup 1 "
+                        "--no-cpu-baseline --no-prefill --copy-calibration; python3 bench.py "
+                        "--summarize-pmc-all FETCH_DIR WRITE_DIR --workload N"))
+    p = os.path.join(ROOT, "profiles", f"traffic_layer_kernels_{workload}.json")
+    with open(p, "w") as f:
+        json.dump(rec, f, indent=2)
+    print(json.dumps(rec, indent=2))
+
+
+def summarize_trace(trace_dir: str):
+    """Per-kernel launch statistics of a rocprofv3 --kernel-trace run of
+    this script: libmoe kernels grouped by name and grid (the same kernel
+    serves launches of different shapes), split into the main workload and
+    the prefill leg (which starts at the first LDS-tiled GEMM; the main
+    workloads at decode sizes use none)."""
+    import csv
+    import collections
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    legs = collections.OrderedDict(main=[], prefill=[])
+    leg = "main"
+    for r in rows:
+        lab = kernel_label(r["Kernel_Name"])
+        if not lab:
+            continue
+        if "tiled_gemm_kernel" in lab:
+            leg = "prefill"
+        wg = int(r["Workgroup_Size_X"])
+        grid = (int(r["Grid_Size_X"]) // max(wg, 1), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        legs[leg].append((lab, grid, r["Kernel_Name"], dur))
+    out = {}
+    for leg, ks in legs.items():
+        g = collections.defaultdict(list)
+        names = {}
+        for lab, grid, name, dur in ks:
+            g[(lab, grid)].append(dur)
+            names[(lab, grid)] = name
+        tot = sum(sum(v) for v in g.values())
+        out[leg] = [dict(kernel=lab, grid=list(grid), name=names[(lab, grid)], calls=len(v),
+                         avg_us=round(statistics.mean(v), 2),
+                         median_us=round(statistics.median(v), 2),
+                         share=round(sum(v) / tot, 4) if tot else 0.0)
+                    for (lab, grid), v in sorted(g.items(), key=lambda kv: -sum(kv[1]))]
+    print(json.dumps(out, indent=1))
+    return out
+
+
 # ------------------------------------------------------------------ main
 
 
@@ -623,6 +729,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (PMC scale)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="per-kernel launch statistics of a rocprofv3 --kernel-trace run")
+    ap.add_argument("--summarize-pmc-all", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="per-kernel HBM traffic of every libmoe kernel of the two PMC runs")
     ap.add_argument("--eplb", action="store_true",
                     help="also report the EPLB-lite monitor cost and rank balance")
     ap.add_argument("--groups", metavar="G,M", default=None,
@@ -630,6 +740,13 @@ def main():
     args = ap.parse_args()
     groups = tuple(int(v) for v in args.groups.split(",")) if args.groups else None
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return 0
+    if args.summarize_pmc_all:
+        import moe_synth
+        summarize_pmc_all(*args.summarize_pmc_all, moe_synth.config(args.workload).name, 1 << 30)
+        return 0
     if args.summarize_pmc:
         import moe_synth
         summarize_pmc(*args.summarize_pmc, moe_synth.config(args.workload).name, 1 << 30,

@@ -146,3 +146,58 @@ def test_cpu_baseline_runs_single_and_multi_threaded():
     assert rec["value"] > 0 and rec["single_thread"]["value"] > 0
     assert 1 <= rec["cores"] <= 16 and rec["single_thread"]["cores"] == 1
     assert rec["cpu_model"]
+
+
+def test_kernel_labels_name_each_layer_kernel():
+    assert bench.kernel_label(STREAM.format(1)) == "stream_gemm_kernel gate/up"
+    assert bench.kernel_label(STREAM.format(0)) == "stream_gemm_kernel down"
+    assert bench.kernel_label(STREAM_F32.format(2)) == "stream_gemm_kernel router"
+    assert bench.kernel_label(TILED.format("256, 2, 1, true")) == \
+        "tiled_gemm_kernel gate/up (256-row tiles)"
+    assert bench.kernel_label(TILED_MANGLED.format(0).replace("Li2ELi1", "Li1ELi0")) == \
+        "tiled_gemm_kernel down (256-row tiles)"
+    assert bench.kernel_label("void moe::(anonymous namespace)::topk_kernel<4, 14>(float const*)") \
+        == "topk_kernel"
+    assert bench.kernel_label(COPY) == ""
+
+
+def test_pmc_summary_of_every_kernel(tmp_path, monkeypatch):
+    gib = 1 << 30
+    up, down = TILED.format("256, 2, 1, true"), TILED.format("256, 1, 0, false")
+    _counter_csv(tmp_path / "fetch", [(up, "FETCH_SIZE", 100.0), (up, "FETCH_SIZE", 104.0),
+                                      (down, "FETCH_SIZE", 50.0), (COPY, "FETCH_SIZE", gib / 2048)])
+    _counter_csv(tmp_path / "write", [(up, "WRITE_SIZE", 3.0), (down, "WRITE_SIZE", 7.0),
+                                      (COPY, "WRITE_SIZE", gib / 1024)])
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    bench.summarize_pmc_all(str(tmp_path / "fetch"), str(tmp_path / "write"), "w", gib)
+    rec = json.loads((tmp_path / "profiles" / "traffic_layer_kernels_w.json").read_text())
+    k = rec["kernels"]
+    assert k["tiled_gemm_kernel gate/up (256-row tiles)"]["FETCH_SIZE_bytes"] == \
+        pytest.approx(102.0 * 1024 * 2)
+    assert k["tiled_gemm_kernel down (256-row tiles)"]["WRITE_SIZE_bytes"] == pytest.approx(7 * 1024)
+
+
+def test_trace_summary_splits_the_prefill_leg(tmp_path):
+    """Kernel-trace rows of one benchmark run: the main workload's kernels,
+    then the prefill leg from the first LDS-tiled GEMM on; grouped by
+    kernel and grid."""
+    d = tmp_path / "trace"
+    d.mkdir()
+    cols = "Kernel_Name,Start_Timestamp,End_Timestamp,Workgroup_Size_X,Grid_Size_X,Grid_Size_Y,Grid_Size_Z"
+    rows = [(STREAM.format(1), 0, 2000, 256, 256 * 32, 258, 1),
+            (STREAM.format(1), 5000, 7000, 256, 256 * 32, 258, 1),
+            (STREAM.format(1), 8000, 8100, 256, 256 * 32, 2, 2),
+            (TILED.format("128, 1, 2, false"), 10000, 10080, 512, 512 * 256, 1, 1),
+            (TILED.format("256, 2, 1, true"), 11000, 12000, 512, 512 * 256, 1, 1)]
+    with open(d / "run_kernel_trace.csv", "w") as f:
+        f.write(cols + "\n")
+        for r in rows:
+            f.write('"' + r[0] + '",' + ",".join(str(v) for v in r[1:]) + "\n")
+    out = bench.summarize_trace(str(d))
+    main = {(k["kernel"], tuple(k["grid"])): k for k in out["main"]}
+    assert main[("stream_gemm_kernel gate/up", (32, 258, 1))]["calls"] == 2
+    assert main[("stream_gemm_kernel gate/up", (32, 258, 1))]["avg_us"] == 2.0
+    assert ("stream_gemm_kernel gate/up", (32, 2, 2)) in main
+    pre = [k["kernel"] for k in out["prefill"]]
+    assert pre == ["tiled_gemm_kernel gate/up (256-row tiles)", "tiled_gemm_kernel router (128-row tiles)"]
