@@ -24,7 +24,7 @@ EXPORTED = (
     "moe_layer_forward_noalloc",
     "moe_workspace_bytes", "moe_status_str", "moe_version", "moe_expert_counts",
     "moe_eplb_state_bytes", "moe_eplb_init", "moe_eplb_observe", "moe_eplb_loads",
-    "moe_eplb_rebalance", "moe_eplb_slot_map",
+    "moe_eplb_rebalance", "moe_eplb_slot_map", "moe_eplb_cleanup",
 )
 _HOST_ONLY = ("moe_workspace_bytes", "moe_status_str", "moe_version", "moe_eplb_state_bytes")
 
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
         L.moe_eplb_loads.argtypes = [P, P, P]
         L.moe_eplb_rebalance.argtypes = [P, P, P]
         L.moe_eplb_slot_map.argtypes = [P, I32, P, P, P, P]
+        L.moe_eplb_cleanup.argtypes = [P, I32, P, P]
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_version.restype = ctypes.c_char_p
@@ -324,3 +325,15 @@ def moe_eplb_slot_map(state, cfg: EplbConfig, rank: int):
         _host(state, np.uint8), rank, _host(off, np.int32), _host(slot, np.int32),
         _host(se, np.int32), ctypes.byref(n)))
     return off, slot[: off[E]].copy(), se[: n.value].copy()
+
+
+def moe_eplb_cleanup(state, cfg: EplbConfig):
+    """Step 4 of section 6.2: reclaim the original-position copies of the
+    migrations since the last cleanup; returns [(expert, rank, slot)]."""
+    import numpy as np
+    cap = cfg.n_experts * cfg.n_ranks
+    out = np.zeros((cap, 3), np.int32)
+    n = ctypes.c_int32()
+    _check("moe_eplb_cleanup", lib().moe_eplb_cleanup(_host(state, np.uint8), cap,
+                                                      ctypes.byref(n), _host(out, np.int32)))
+    return [tuple(int(v) for v in r) for r in out[: n.value]]

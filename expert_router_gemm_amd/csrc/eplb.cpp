@@ -13,6 +13,10 @@
 //             current placement; the caller keeps two device copies and
 //             switches between forwards (the page's double-buffered routing
 //             table: work already queued keeps reading the old one)
+//   cleanup   once the old table has drained, the copy each migration was
+//             taken from (its original position) is reclaimed, so the
+//             migration becomes a move; a reclaimed home slot stays empty, a
+//             reclaimed spare slot becomes a hole the next copy fills
 //
 // All state lives in caller memory (moe_eplb_state_bytes); nothing here
 // touches a device.  Loads are double sums accumulated in expert order, so
@@ -36,15 +40,19 @@ struct Hdr {
 
 struct View {
     Hdr *h;
-    int32_t *ring;     // [W][E]
-    int64_t *sum;      // [E] window sums
-    int32_t *ncopy;    // [E]
-    int32_t *copies;   // [E][R]: ranks, home first
-    int32_t *nadded;   // [R]
-    int32_t *added;    // [R][spare]: experts added on each rank, in order
+    int32_t *ring;       // [W][E]
+    int64_t *sum;        // [E] window sums
+    int32_t *ncopy;      // [E]
+    int32_t *copies;     // [E][R]: ranks holding a copy, in creation order
+    int32_t *nadded;     // [R]: spare slots in use or holes
+    int32_t *added;      // [R][spare]: expert in each spare slot, -1 = hole
+    int32_t *home_live;  // [E]: the home copy has not been reclaimed
+    uint8_t *pend;       // [E][R]: a migration took e from rank r since the last cleanup
 };
 
 size_t align8(size_t n) { return (n + 7) & ~(size_t)7; }
+
+constexpr int kParts = 8;
 
 size_t layout(const moe_eplb_config &c, size_t *off) {
     size_t o = align8(sizeof(Hdr));
@@ -60,6 +68,10 @@ size_t layout(const moe_eplb_config &c, size_t *off) {
     o += align8((size_t)c.n_ranks * 4);
     off[5] = o;
     o += align8((size_t)c.n_ranks * (c.spare_slots > 0 ? c.spare_slots : 1) * 4);
+    off[6] = o;
+    o += align8((size_t)c.n_experts * 4);
+    off[7] = o;
+    o += align8((size_t)c.n_experts * c.n_ranks);
     return o;
 }
 
@@ -76,7 +88,7 @@ View view(S *state) {
     char *b = (char *)state;
     View v;
     v.h = (Hdr *)b;
-    size_t off[6];
+    size_t off[kParts];
     layout(v.h->cfg, off);
     v.ring = (int32_t *)(b + off[0]);
     v.sum = (int64_t *)(b + off[1]);
@@ -84,7 +96,21 @@ View view(S *state) {
     v.copies = (int32_t *)(b + off[3]);
     v.nadded = (int32_t *)(b + off[4]);
     v.added = (int32_t *)(b + off[5]);
+    v.home_live = (int32_t *)(b + off[6]);
+    v.pend = (uint8_t *)(b + off[7]);
     return v;
+}
+
+int spare_stride(const moe_eplb_config &c) { return c.spare_slots > 0 ? c.spare_slots : 1; }
+
+// First free spare slot of rank r: a hole, else the next unused one; -1
+// when every spare slot holds a copy.
+int free_spare(const View &v, int r) {
+    const moe_eplb_config &c = v.h->cfg;
+    const int sp = spare_stride(c);
+    for (int j = 0; j < v.nadded[r]; ++j)
+        if (v.added[r * sp + j] < 0) return j;
+    return v.nadded[r] < c.spare_slots ? v.nadded[r] : -1;
 }
 
 bool holds(const View &v, int e, int r) {
@@ -119,7 +145,7 @@ extern "C" {
 
 __attribute__((visibility("default"))) size_t moe_eplb_state_bytes(const moe_eplb_config *cfg) {
     if (!valid(cfg)) return 0;
-    size_t off[6];
+    size_t off[kParts];
     return layout(*cfg, off);
 }
 
@@ -127,7 +153,7 @@ __attribute__((visibility("default"))) moe_status moe_eplb_init(const moe_eplb_c
                                                                 void *state, size_t state_bytes) {
     if (!valid(cfg)) return MOE_ERR_SHAPE;
     if (!state) return MOE_ERR_INVALID_ARG;
-    size_t off[6];
+    size_t off[kParts];
     const size_t need = layout(*cfg, off);
     if (state_bytes < need) return MOE_ERR_WORKSPACE;
     memset(state, 0, need);
@@ -138,6 +164,7 @@ __attribute__((visibility("default"))) moe_status moe_eplb_init(const moe_eplb_c
     for (int e = 0; e < E; ++e) {
         v.ncopy[e] = 1;
         v.copies[e * R] = e / per;  // home copy, section 2.1 placement
+        v.home_live[e] = 1;
     }
     return MOE_OK;
 }
@@ -211,14 +238,16 @@ __attribute__((visibility("default"))) moe_status moe_eplb_rebalance(void *state
             tried[best] = 1;
             int tgt = -1;
             for (int r = 0; r < R; ++r) {
-                if (holds(v, best, r) || v.nadded[r] >= c.spare_slots) continue;
+                if (holds(v, best, r) || free_spare(v, r) < 0) continue;
                 if (tgt < 0 || load[r] < load[tgt]) tgt = r;  // ties: lower rank
             }
             if (tgt < 0) continue;
             v.copies[best * R + v.ncopy[best]] = tgt;
             v.ncopy[best] += 1;
-            v.added[tgt * (c.spare_slots > 0 ? c.spare_slots : 1) + v.nadded[tgt]] = best;
-            v.nadded[tgt] += 1;
+            const int j = free_spare(v, tgt);
+            v.added[tgt * spare_stride(c) + j] = best;
+            if (j == v.nadded[tgt]) v.nadded[tgt] += 1;
+            v.pend[best * R + hot] = 1;  // the copy this migration was taken from
             if (moves) {
                 moves[2 * *n_moves] = best;
                 moves[2 * *n_moves + 1] = tgt;
@@ -243,7 +272,8 @@ __attribute__((visibility("default"))) moe_status moe_eplb_slot_map(
     if (rank < 0 || rank >= R) return MOE_ERR_SHAPE;
     const int S = per + v.nadded[rank];
     if (slot_expert) {
-        for (int s = 0; s < per; ++s) slot_expert[s] = rank * per + s;
+        for (int s = 0; s < per; ++s)
+            slot_expert[s] = v.home_live[rank * per + s] ? rank * per + s : -1;
         for (int j = 0; j < v.nadded[rank]; ++j) slot_expert[per + j] = v.added[rank * sp + j];
     }
     if (n_slots) *n_slots = S;
@@ -253,7 +283,7 @@ __attribute__((visibility("default"))) moe_status moe_eplb_slot_map(
         for (int i = 0; i < v.ncopy[e]; ++i) {
             int s = -1;
             if (v.copies[e * R + i] == rank) {
-                if (i == 0) {
+                if (e / per == rank && v.home_live[e]) {
                     s = e - rank * per;
                 } else {
                     for (int j = 0; j < v.nadded[rank]; ++j)
@@ -264,6 +294,48 @@ __attribute__((visibility("default"))) moe_status moe_eplb_slot_map(
         }
         rep_off[e + 1] = n;
     }
+    return MOE_OK;
+}
+
+__attribute__((visibility("default"))) moe_status moe_eplb_cleanup(void *state,
+                                                                   int32_t capacity,
+                                                                   int32_t *n_reclaimed,
+                                                                   int32_t *reclaimed) {
+    if (!state || !n_reclaimed || capacity < 0 || (capacity > 0 && !reclaimed))
+        return MOE_ERR_INVALID_ARG;
+    View v = view(state);
+    const moe_eplb_config &c = v.h->cfg;
+    const int E = c.n_experts, R = c.n_ranks, per = E / R, sp = spare_stride(c);
+    int n = 0;
+    for (int e = 0; e < E; ++e) {
+        for (int r = 0; r < R; ++r) {
+            if (!v.pend[e * R + r]) continue;
+            v.pend[e * R + r] = 0;
+            if (!holds(v, e, r) || v.ncopy[e] < 2) continue;  // keep the last copy
+            int slot = -1;
+            if (e / per == r && v.home_live[e]) {
+                slot = e - r * per;
+                v.home_live[e] = 0;
+            } else {
+                for (int j = 0; j < v.nadded[r]; ++j)
+                    if (v.added[r * sp + j] == e) {
+                        slot = per + j;
+                        v.added[r * sp + j] = -1;
+                    }
+            }
+            int w = 0;  // drop r from e's copies, keeping the others' order
+            for (int i = 0; i < v.ncopy[e]; ++i)
+                if (v.copies[e * R + i] != r) v.copies[e * R + w++] = v.copies[e * R + i];
+            v.ncopy[e] = w;
+            if (n < capacity) {
+                reclaimed[3 * n] = e;
+                reclaimed[3 * n + 1] = r;
+                reclaimed[3 * n + 2] = slot;
+            }
+            ++n;
+        }
+    }
+    *n_reclaimed = n;
     return MOE_OK;
 }
 

@@ -269,12 +269,20 @@ moe_status moe_layer_forward_noalloc(const moe_shape *shape, const moe_weights *
  *            new copy on the least loaded rank (ties: lower rank) that holds
  *            none and has one of its spare_slots free.  Home copies stay.
  *   tables   moe_eplb_slot_map writes one rank's moe_slot_map arrays for
- *            the current placement: home experts in slots 0..E/R-1, added
- *            copies after them in the order they were added; each expert
- *            lists its copies home first, a copy on another rank as -1.
- *            The new expert weights must be in place before a forward uses
- *            the new table; keep the old table for work already queued (the
- *            page's double-buffered routing table).
+ *            the current placement: home experts in slots 0..E/R-1, spare
+ *            slots after them; each expert lists its copies in the order
+ *            they were created (the home copy first while it lives), a copy
+ *            on another rank as -1.  The new expert weights must be in place
+ *            before a forward uses the new table; keep the old table for
+ *            work already queued (the page's double-buffered routing table).
+ *   cleanup  moe_eplb_cleanup, called once all work queued with the old
+ *            table has finished: the copy each migration since the last
+ *            cleanup was taken from (its original position on the
+ *            overloaded rank) is reclaimed, unless it is the expert's last
+ *            copy -- the migration becomes a move (the page's optional
+ *            step 4).  A reclaimed home slot stays empty; a reclaimed spare
+ *            slot becomes a hole that the next copy placed on that rank
+ *            fills, so slot numbers never shift.
  * The monitor state is caller memory of moe_eplb_state_bytes(cfg) bytes;
  * these calls are host-only and never touch a device.  Calls on one state
  * must not overlap. */
@@ -308,9 +316,17 @@ moe_status moe_eplb_loads(const void *state, double *loads, double *imbalance);
 moe_status moe_eplb_rebalance(void *state, int32_t *n_moves, int32_t *moves);
 /* (host) One rank's table: rep_off [E+1], rep_slot [E + R * spare_slots],
  * slot_expert [E/R + spare_slots] (may be NULL: the expert each local slot
- * must hold), *n_slots (may be NULL). */
+ * must hold, -1 for a reclaimed or empty slot), *n_slots (may be NULL). */
 moe_status moe_eplb_slot_map(const void *state, int32_t rank, int32_t *rep_off,
                              int32_t *rep_slot, int32_t *slot_expert, int32_t *n_slots);
+/* (host) Step 4: reclaim the original-position copies of the migrations
+ * since the last cleanup (see above), in expert order then rank order.
+ * *n_reclaimed gets the number reclaimed; the first `capacity` of them are
+ * written to reclaimed (int32 [capacity][3]: expert, rank, local slot on
+ * that rank whose weights may now be released; may be NULL if capacity is
+ * 0).  At most E * R copies are reclaimed by one call. */
+moe_status moe_eplb_cleanup(void *state, int32_t capacity, int32_t *n_reclaimed,
+                            int32_t *reclaimed);
 
 /* (host) Workspace bytes that moe_layer_forward needs for T tokens; also
  * enough for moe_dispatch and moe_expert_ffn with cap_rows <= T*K (or

@@ -11,7 +11,10 @@ stopping) and 6.3 (redundant experts), read for one EP group:
                 and give each a copy on an idle rank; new tokens may then go
                 to either copy (section 6.3: a random replica), the old copy
                 stays where it is
-  4. cleanup:   optional on the page; not modelled
+  4. cleanup:   once every request routed with the old table has been
+                served, the copy at each migrated expert's original
+                position may be reclaimed (optional on the page, under
+                memory pressure): a migration then becomes a move
 
 Readings taken where the page leaves a step open:
   * the window counts forwards, not milliseconds: the last W observed
@@ -27,7 +30,15 @@ Readings taken where the page leaves a step open:
     each added copy the loads are recomputed (greedy);
   * max_moves copies are added per triggered rebalance (the page: 1-2);
   * ranks are numbered by the contiguous placement of section 2.1; expert
-    e's home copy is on rank e // (E / R) and is never removed.
+    e's home copy is on rank e // (E / R) in that rank's home slot
+    e % (E / R); rebalancing never removes a copy;
+  * cleanup runs when the caller says the old table has drained; the
+    "original position" of a migration is the copy on the overloaded rank
+    it was taken from; each (expert, origin) recorded since the last
+    cleanup loses that copy, in expert order then rank order, unless it is
+    the expert's last one; a reclaimed home slot stays empty, a reclaimed
+    added copy leaves a hole in its rank's spare slots that the next copy
+    placed on that rank fills (slot numbers never shift).
 
 Plain loops only; every function states the step it follows.
 """
@@ -48,7 +59,10 @@ class EplbOracle:
         self.hist: List[List[int]] = []          # last W per-forward histograms
         # copies[e]: ranks holding expert e, home first, then added copies in order
         self.copies: List[List[int]] = [[e // self.per] for e in range(n_experts)]
-        self.added: List[List[int]] = [[] for _ in range(n_ranks)]  # experts added per rank
+        # spare slots of each rank in slot order: the expert held, or -1 (a hole)
+        self.added: List[List[int]] = [[] for _ in range(n_ranks)]
+        self.home_live: List[bool] = [True] * n_experts
+        self.pending: List[List[bool]] = [[False] * n_ranks for _ in range(n_experts)]
 
     # 1. monitor
     def observe(self, counts) -> None:
@@ -94,12 +108,17 @@ class EplbOracle:
             done = False
             for e in cands:
                 targets = [r for r in range(self.R)
-                           if r not in self.copies[e] and len(self.added[r]) < self.spare]
+                           if r not in self.copies[e] and self._free_spare(r) >= 0]
                 if not targets:
                     continue
                 tgt = min(targets, key=lambda r: (load[r], r))
                 self.copies[e].append(tgt)
-                self.added[tgt].append(e)
+                j = self._free_spare(tgt)
+                if j < len(self.added[tgt]):
+                    self.added[tgt][j] = e        # fill a hole
+                else:
+                    self.added[tgt].append(e)
+                self.pending[e][hot] = True       # the copy it was taken from
                 moves.append((e, tgt))
                 done = True
                 break
@@ -107,19 +126,56 @@ class EplbOracle:
                 break
         return moves
 
+    def _free_spare(self, r: int) -> int:
+        """Index of the first free spare slot of rank r (a hole, else the
+        next unused one), or -1 when all spare_slots hold copies."""
+        for j, e in enumerate(self.added[r]):
+            if e < 0:
+                return j
+        return len(self.added[r]) if len(self.added[r]) < self.spare else -1
+
+    # 4. cleanup (the old table has drained)
+    def cleanup(self) -> List[Tuple[int, int, int]]:
+        """Reclaim the original-position copies of the migrations recorded
+        since the last cleanup; returns (expert, rank, slot) per reclaimed
+        copy (slot: its local slot on that rank)."""
+        out = []
+        for e in range(self.E):
+            for r in range(self.R):
+                if not self.pending[e][r]:
+                    continue
+                self.pending[e][r] = False
+                if r not in self.copies[e] or len(self.copies[e]) < 2:
+                    continue
+                if r == e // self.per and self.home_live[e]:
+                    slot = e - r * self.per
+                    self.home_live[e] = False
+                else:
+                    j = self.added[r].index(e)
+                    slot = self.per + j
+                    self.added[r][j] = -1
+                self.copies[e].remove(r)
+                out.append((e, r, slot))
+        return out
+
     # the table one rank's forward reads (section 6.3 replica lists)
     def slot_map(self, rank: int):
         """(rep_off [E+1], rep_slot [nnz], slot_experts [S]) for ``rank``:
-        home experts in slots 0..per-1, added copies after them in the
-        order they were added; each expert lists its copies home first, a
-        copy on another rank as -1."""
+        home experts in slots 0..per-1, spare slots after them (-1 in
+        slot_experts: a reclaimed slot or hole); each expert lists its
+        copies in the order they were created (home first while it lives),
+        a copy on another rank as -1."""
         slot_of = {}
-        slot_experts = list(range(rank * self.per, (rank + 1) * self.per))
-        for e in slot_experts:
-            slot_of[e] = e - rank * self.per
-        for e in self.added[rank]:
-            slot_of[e] = len(slot_experts)
+        slot_experts = []
+        for s in range(self.per):
+            e = rank * self.per + s
+            slot_experts.append(e if self.home_live[e] else -1)
+            if self.home_live[e]:
+                slot_of[e] = s
+        for j, e in enumerate(self.added[rank]):
             slot_experts.append(e)
+            if e >= 0:
+                slot_of[e] = self.per + j
         off, slots = [0], []
         for e in range(self.E):
             for r in self.copies[e]:

@@ -22,10 +22,12 @@ def _pair(E, R, W, moves, spare, thr=1.2):
     return cfg, st, EplbOracle(E, R, window=W, threshold=thr, max_moves=moves, spare_slots=spare)
 
 
-def _run(seq, E, R, W, moves, spare, thr=1.2):
+def _run(seq, E, R, W, moves, spare, thr=1.2, cleanup_every=0):
     cfg, st, o = _pair(E, R, W, moves, spare, thr)
     n_moves = 0
-    for counts in seq:
+    for i, counts in enumerate(seq):
+        if cleanup_every and i % cleanup_every == cleanup_every - 1:
+            assert moe.moe_eplb_cleanup(st, cfg) == o.cleanup()
         counts = np.ascontiguousarray(counts, np.int32)
         moe.moe_eplb_observe(st, counts)
         o.observe(counts)
@@ -57,6 +59,40 @@ def test_planner_matches_oracle_on_long_tail_sequences(seed):
     moved = _run(seq, E, R, W=int(rng.integers(1, 6)), moves=int(rng.integers(1, 3)),
                  spare=int(rng.integers(1, 4)))
     assert moved > 0  # long tails trigger at least one rebalance
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_cleanup_matches_oracle_on_long_tail_sequences(seed):
+    """Step 4 interleaved with the planner: the same reclaimed copies and
+    slots, then the same loads, moves and tables (holes and empty home
+    slots included)."""
+    rng = np.random.default_rng(100 + seed)
+    E, R = [(64, 8), (16, 4), (256, 8), (32, 2)][seed]
+    hot = rng.choice(E, max(1, int(0.3 * E)), replace=False)
+    p = np.ones(E)
+    p[hot] = rng.uniform(2, 8)
+    p[: E // R] *= 2.0
+    p /= p.sum()
+    seq = [rng.multinomial(int(rng.integers(100, 5000)), p) for _ in range(40)]
+    moved = _run(seq, E, R, W=int(rng.integers(1, 4)), moves=int(rng.integers(1, 3)),
+                 spare=int(rng.integers(1, 3)), cleanup_every=int(rng.integers(2, 5)))
+    assert moved > 0
+
+
+def test_cleanup_validation_and_capacity():
+    cfg, st, o = _pair(8, 2, 1, 1, 1)
+    c = np.array([10, 1, 1, 1, 1, 1, 1, 1], np.int32)
+    moe.moe_eplb_observe(st, c)
+    assert moe.moe_eplb_rebalance(st, 1) == [(0, 1)]
+    L = moe.lib()
+    import ctypes
+    n = ctypes.c_int32()
+    assert L.moe_eplb_cleanup(st.ctypes.data, 0, ctypes.byref(n), None) == 0  # count only
+    assert n.value == 1
+    assert L.moe_eplb_cleanup(st.ctypes.data, 0, ctypes.byref(n), None) == 0
+    assert n.value == 0                                                    # already reclaimed
+    assert L.moe_eplb_cleanup(st.ctypes.data, 1, ctypes.byref(n), None) != 0  # no output array
+    assert L.moe_eplb_cleanup(None, 0, ctypes.byref(n), None) != 0
 
 
 def test_planner_matches_oracle_on_worked_and_edge_cases():

@@ -133,3 +133,27 @@ def test_double_buffered_table_swap_matches_oracle():
     slots = oracle.slot_map(ref["topk_idx"], offB, slotB, cfg.seed)
     assert (slots == per).sum() > 0
     print(f"[eplb] move {moves} imbalance {imb:.3f} pairs on the copy {(slots == per).sum()}")
+
+    # step 4: once table A's work has drained, cleanup reclaims the copy the
+    # migration was taken from (rank 3's home copy of e_new); rank 0's table
+    # C then sends every pair of e_new to its copy here
+    rec = moe.moe_eplb_cleanup(st, ecfg)
+    assert rec == o.cleanup() == [(e_new, 3, e_new - 3 * per)]
+    offC, slotC, seC = moe.moe_eplb_slot_map(st, ecfg, rank)
+    assert list(seC) == list(seB)  # rank 0's slots unchanged
+    assert list(slotC[offC[e_new]:offC[e_new + 1]]) == [per]
+    tab[0][0].copy_(torch.from_numpy(offC))
+    tab[0][1].zero_()
+    tab[0][1][: len(slotC)].copy_(torch.from_numpy(slotC))
+    mapC = moe.make_slot_map(tab[0][0], tab[0][1], cfg.seed)
+    outC = torch.empty_like(outA)
+    moe.moe_layer_forward(shape, w, mapC, cfg.T, hd, outC, ws)
+    torch.cuda.synchronize()
+    refC = oracle.layer_forward(h=h, w_router=wr, bias=bias, w_sg=None,
+                                slot_weights=[host[int(e)] for e in seC], shared=None,
+                                rep_off=offC, rep_slot=slotC, seed=cfg.seed, K=K,
+                                fp8_dispatch=False)
+    gh.assert_close(outC.cpu().numpy(), refC["out"], "layer output (table C)", rows=~tie)
+    slotsC = oracle.slot_map(refC["topk_idx"], offC, slotC, cfg.seed)
+    assert (slotsC == per).sum() == (refC["topk_idx"] == e_new).sum()
+    print(f"[eplb] cleanup {rec}: all {(slotsC == per).sum()} pairs of expert {e_new} on the copy")

@@ -112,3 +112,67 @@ def test_bincount_and_simulation_smoke():
     seq = [[10, 10, 10, 100]] * 3
     out = simulate(seq, n_experts=4, n_ranks=2, window=2, max_moves=1, spare_slots=1)
     assert out == [(0, [(3, 0)])]
+
+
+def test_cleanup_worked_case_moves_then_reuses_a_hole():
+    """Step 4 by hand.  E = 8 on R = 2 ranks (4 each), one spare slot per
+    rank; expert 0 (rank 0) takes 10 tokens, the others 1."""
+    o = EplbOracle(8, 2, window=1, threshold=1.2, max_moves=1, spare_slots=1)
+    o.observe([10, 1, 1, 1, 1, 1, 1, 1])
+    assert o.loads() == [13.0, 4.0]
+    # migrate: expert 0 gets a copy in rank 1's spare slot (slot 4); both
+    # copies serve: loads 5 + 3 = 8 and 5 + 4 = 9
+    assert o.rebalance() == [(0, 1)]
+    assert o.loads() == [8.0, 9.0]
+    # cleanup: the copy it was taken from -- rank 0's home slot 0 -- is
+    # reclaimed; expert 0 now lives on rank 1 only: loads 3 and 14
+    assert o.cleanup() == [(0, 0, 0)]
+    assert o.copies[0] == [1] and o.loads() == [3.0, 14.0]
+    assert o.cleanup() == []                         # nothing recorded since
+    off, slots, se = o.slot_map(0)
+    assert se.tolist() == [-1, 1, 2, 3]              # home slot 0 stays empty
+    assert slots[off[0]:off[1]].tolist() == [-1]
+    off, slots, se = o.slot_map(1)
+    assert se.tolist() == [4, 5, 6, 7, 0]
+    assert slots[off[0]:off[1]].tolist() == [4]
+    # rank 1 is now the hot one (14 / 8.5): expert 0 (10 per copy) gets a
+    # copy in rank 0's spare slot; cleanup then reclaims rank 1's copy,
+    # leaving a hole in its spare slot
+    assert o.rebalance() == [(0, 0)]
+    assert o.cleanup() == [(0, 1, 4)]
+    assert o.copies[0] == [0] and o.added == [[0], [-1]]
+    assert o.slot_map(0)[2].tolist() == [-1, 1, 2, 3, 0]
+    assert o.slot_map(1)[2].tolist() == [4, 5, 6, 7, -1]
+    # rank 1 hot (15 vs 4), but rank 0's only spare slot holds expert 0:
+    # no copy can be placed
+    o.observe([1, 1, 1, 1, 1, 1, 1, 12])
+    assert o.loads() == [4.0, 15.0] and o.rebalance() == []
+    # rank 0 hot (expert 1: 12): its copy takes rank 1's hole, slot 4
+    o.observe([1, 12, 1, 1, 1, 1, 1, 1])
+    assert o.loads() == [15.0, 4.0]
+    assert o.rebalance() == [(1, 1)] and o.added[1] == [1]
+    off, slots, se = o.slot_map(1)
+    assert se.tolist() == [4, 5, 6, 7, 1] and slots[off[1]:off[2]].tolist() == [-1, 4]
+
+
+def test_cleanup_keeps_the_last_copy_and_conserves_load():
+    o = EplbOracle(16, 4, window=2, max_moves=2, spare_slots=2)
+    rng = np.random.default_rng(11)
+    p = np.ones(16)
+    p[[1, 2, 9]] = 6.0
+    p /= p.sum()
+    for it in range(30):
+        o.observe(rng.multinomial(800, p))
+        o.rebalance()
+        if it % 3 == 2:
+            for e, r, s in o.cleanup():
+                assert r not in o.copies[e]
+                assert (s == e % 4 and r == e // 4) or s >= 4
+        assert all(len(c) >= 1 for c in o.copies)
+        assert sum(o.loads()) == pytest.approx(sum(o.window_counts()))
+        for r in range(4):
+            held = [e for e in range(16) if r in o.copies[e]]
+            off, slots, se = o.slot_map(r)
+            assert sorted(e for e in se.tolist() if e >= 0) == held
+    o.pending[3][0] = True                           # expert 3's only copy
+    assert len(o.copies[3]) == 1 and o.cleanup() == []
