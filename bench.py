@@ -85,7 +85,10 @@ def log(msg):
 # ------------------------------------------------------------------ setup
 
 
-def setup(n: int, keep_host: bool = True, groups=None):
+LAYOUT_NAME = {"frag": "fragment (MOE_W_FRAG)", "rowmajor": "row-major"}
+
+
+def setup(n: int, keep_host: bool = True, groups=None, w_layout: str = "frag"):
     import numpy as np
     import torch
 
@@ -121,14 +124,23 @@ def setup(n: int, keep_host: bool = True, groups=None):
     if cfg.n_shared:
         shared = moe_synth.gen_shared_weights(cfg)
         d.update(SG=t(shared[0]), SU=t(shared[1]), SD=t(shared[2]))
+    if w_layout == "frag":
+        # expert weights in the fragment layout (moe_pack_weights, once at
+        # load time; the row-major copies are freed)
+        for k in ("G", "U", "D", "SG", "SU", "SD"):
+            if k in d:
+                d[k] = moe.pack_weights(d[k])
+        G, U, D = d["G"], d["U"], d["D"]
     torch.cuda.synchronize()
-    log(f"[bench] generated and uploaded {cfg.name} in {time.time() - t0:.1f}s")
+    log(f"[bench] generated and uploaded {cfg.name} ({w_layout} expert weights) in "
+        f"{time.time() - t0:.1f}s")
     fp8 = cfg.dispatch == "fp8"
     shape = moe.make_shape(hidden=cfg.H, inter=cfg.I, n_experts=cfg.E, top_k=cfg.K, n_slots=S,
                            n_shared=cfg.n_shared,
                            act=moe.MOE_F32 if cfg.dtype == "f32" else moe.MOE_F16,
                            dispatch=moe.MOE_FP8_E4M3 if fp8 else None, shared=cfg.n_shared > 0,
-                           n_groups=cfg.n_groups, topk_groups=cfg.topk_groups)
+                           n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+                           w_layout=moe.MOE_W_FRAG if w_layout == "frag" else moe.MOE_W_ROWMAJOR)
     T, K = cfg.T, cfg.K
     bufs = dict(
         ws=torch.empty(moe.moe_workspace_bytes(shape, T), dtype=torch.uint8, device=dev),
@@ -152,7 +164,7 @@ def setup(n: int, keep_host: bool = True, groups=None):
                             sh_gate=d.get("SG"), sh_up=d.get("SU"), sh_down=d.get("SD"))
     smap = moe.make_slot_map(d["ro"], d["rs"], cfg.seed)
     return dict(cfg=cfg, shape=shape, d=d, b=bufs, wmap=wmap, smap=smap, S=S, h=h, wr=wr,
-                bias=bias, host_experts=host_experts, shared=shared, rep=rep)
+                bias=bias, host_experts=host_experts, shared=shared, rep=rep, w_layout=w_layout)
 
 
 def staged_step(ctx, ev=None):
@@ -492,15 +504,16 @@ def cpu_baseline(ctx, budget_s: float = 20.0):
 
 def is_dominant(kernel_name: str, kind: str) -> bool:
     """The gate/up launch of the dominant kernel, demangled or mangled.
-    Stream GEMM: template arguments <TW, XM, NSUB, EPI, KW, U> with EPI =
-    SwiGLU (1).  Tiled GEMM: <TBM, NM, EPI, GATHER> = <256, 2, 1, true>."""
+    Stream GEMM: template arguments <TW, XM, NSUB, EPI, KW, U, FR> with EPI =
+    SwiGLU (1).  Tiled GEMM: <TBM, NM, EPI, GATHER, FR> = <256, 2, 1, true,
+    either weight layout>."""
     import re
     if DOMINANT[kind] not in kernel_name:
         return False
     if kind == "tiled":
         n = kernel_name.replace(" ", "")
-        return ("tiled_gemm_kernel<256,2,1,true>" in n
-                or "tiled_gemm_kernelILi256ELi2ELi1ELb1E" in n)
+        return bool(re.search(r"tiled_gemm_kernel<256,2,1,true(,(true|false))?>", n)
+                    or "tiled_gemm_kernelILi256ELi2ELi1ELb1E" in n)
     n = kernel_name.replace(" ", "")
     m = re.search(r"stream_gemm_kernel<[^,]+,(\d+),(\d+),(\d+),", n)
     if m:
@@ -563,7 +576,7 @@ def kernel_label(name: str) -> str:
     import re
     n = name.replace(" ", "")
     if "tiled_gemm_kernel" in n:
-        m = re.search(r"tiled_gemm_kernel<(\d+),(\d+),(\d+),(true|false)>", n) or re.search(
+        m = re.search(r"tiled_gemm_kernel<(\d+),(\d+),(\d+),(true|false)", n) or re.search(
             r"tiled_gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELb([01])E", n)
         if m:
             epi = {"0": "down", "1": "gate/up", "2": "router"}[m.group(3)]
@@ -674,13 +687,13 @@ def free_gpu(ctx):
     torch.cuda.empty_cache()
 
 
-def prefill_record(K: int, warmup: int):
+def prefill_record(K: int, warmup: int, w_layout: str = "frag"):
     """The prefill workload timed like the main one; tokens/s, the MFMA
     fraction of its gate/up launch and of the whole layer."""
     import torch
 
     import expert_router_gemm_amd as moe
-    ctx = setup(PREFILL_WORKLOAD, keep_host=False)
+    ctx = setup(PREFILL_WORKLOAD, keep_host=False, w_layout=w_layout)
     cfg = ctx["cfg"]
     t = time_workload(ctx, K, warmup, references=False)
     prof_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
@@ -690,6 +703,7 @@ def prefill_record(K: int, warmup: int):
     t["stage_ms"] = {n: prof_ev[j].elapsed_time(prof_ev[j + 1]) for j, n in enumerate(names)}
     work = algorithmic_work(cfg, _counts_of(ctx))
     rec = {"workload": cfg.name, "tokens": cfg.T, "local_slots": ctx["S"],
+           "weight_layout": LAYOUT_NAME[w_layout],
            "value": round(cfg.T / (t["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
            "steps": K, "warmup": warmup, "ms_per_step": round(t["ms_per_step"], 4),
            "roofline": kernel_roofline(cfg, work, t["up_ms"], "tiled"),
@@ -735,6 +749,8 @@ def main():
                     help="per-kernel HBM traffic of every libmoe kernel of the two PMC runs")
     ap.add_argument("--eplb", action="store_true",
                     help="also report the EPLB-lite monitor cost and rank balance")
+    ap.add_argument("--w-layout", choices=["frag", "rowmajor"], default="frag",
+                    help="expert weight layout: the fragment layout (default) or row-major")
     ap.add_argument("--groups", metavar="G,M", default=None,
                     help="group-limited routing: keep M of G contiguous expert groups")
     args = ap.parse_args()
@@ -765,7 +781,7 @@ def main():
     import expert_router_gemm_amd as moe
     moe.lib()
     want_cpu = not args.no_cpu_baseline
-    ctx = setup(args.workload, keep_host=want_cpu, groups=groups)
+    ctx = setup(args.workload, keep_host=want_cpu, groups=groups, w_layout=args.w_layout)
     cfg = ctx["cfg"]
     kind = dominant_kind(args.workload)
 
@@ -811,7 +827,8 @@ def main():
                    "shared_experts": cfg.n_shared, "dispatch": cfg.dispatch,
                    "ep_size": cfg.ep_size, "ep_rank": cfg.ep_rank,
                    "long_tail": cfg.long_tail,
-                   "group_limit": list(groups) if groups else None},
+                   "group_limit": list(groups) if groups else None,
+                   "weight_layout": LAYOUT_NAME[args.w_layout]},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer": layer,
@@ -820,7 +837,7 @@ def main():
         rec["eplb"] = eplb
     free_gpu(ctx)
     if not args.no_prefill and args.workload != PREFILL_WORKLOAD:
-        rec["prefill"] = prefill_record(args.steps, args.warmup)
+        rec["prefill"] = prefill_record(args.steps, args.warmup, args.w_layout)
         log(f"[bench] prefill {rec['prefill']['workload']}: {rec['prefill']['value']:.0f} "
             f"tokens/s, gate/up {rec['prefill']['roofline']['achieved']} TFLOP/s")
     print(json.dumps(rec))

@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_F32, MOE_F16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_F_SHARED = 1
 MOE_X_PERMUTED, MOE_X_SHARED, MOE_X_GATHER = 0, 1, 2
+MOE_W_ROWMAJOR, MOE_W_FRAG = 0, 1
 
 EXPORTED = (
     "moe_route", "moe_dispatch", "moe_expert_ffn_up", "moe_expert_ffn_down",
     "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_profiled",
-    "moe_layer_forward_noalloc",
+    "moe_layer_forward_noalloc", "moe_pack_weights",
     "moe_workspace_bytes", "moe_status_str", "moe_version", "moe_expert_counts",
     "moe_eplb_state_bytes", "moe_eplb_init", "moe_eplb_observe", "moe_eplb_loads",
     "moe_eplb_rebalance", "moe_eplb_slot_map", "moe_eplb_cleanup",
@@ -41,7 +42,7 @@ class Shape(ctypes.Structure):
                 ("n_slots", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("dispatch", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("n_groups", ctypes.c_int32),
-                ("topk_groups", ctypes.c_int32)]
+                ("topk_groups", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
 
     def __repr__(self):
         return "Shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -95,6 +96,7 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward_noalloc.argtypes = [SP, ctypes.POINTER(Weights),
                                                 ctypes.POINTER(SlotMap), I32, P, P, P]
         L.moe_workspace_bytes.argtypes = [SP, I32]
+        L.moe_pack_weights.argtypes = [I32, ctypes.c_int64, I32, I32, P, P, P]
         L.moe_workspace_bytes.restype = SZ
         L.moe_expert_counts.argtypes = [SP, I32, P, P, P]
         EP = ctypes.POINTER(EplbConfig)
@@ -157,10 +159,11 @@ def _check(fn: str, st: int):
 
 
 def make_shape(*, hidden, inter, n_experts, top_k, n_slots, n_shared=0, act=MOE_F16,
-               dispatch=None, shared=False, n_groups=0, topk_groups=0) -> Shape:
+               dispatch=None, shared=False, n_groups=0, topk_groups=0,
+               w_layout=MOE_W_ROWMAJOR) -> Shape:
     return Shape(hidden, inter, n_experts, top_k, n_slots, n_shared, act,
                  act if dispatch is None else dispatch, MOE_F_SHARED if shared else 0,
-                 n_groups, topk_groups)
+                 n_groups, topk_groups, w_layout)
 
 
 def moe_workspace_bytes(shape: Shape, T: int) -> int:
@@ -224,6 +227,27 @@ def moe_layer_forward_noalloc(shape, weights: Weights, slot_map: SlotMap, T, h, 
 
 
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_pack_weights(dtype, n_mats, rows, cols, src, dst, stream=None):
+    _check("moe_pack_weights", lib().moe_pack_weights(
+        int(dtype), int(n_mats), int(rows), int(cols), _p(src), _p(dst), _stream(stream)))
+
+
+def pack_weights(w, stream=None):
+    """MOE_W_FRAG copy of the row-major expert weights ``w`` (fp16 or fp32,
+    [..., rows, cols]); the result has w's shape and dtype."""
+    import torch
+    dtype = {torch.float16: MOE_F16, torch.float32: MOE_F32}.get(w.dtype)
+    if dtype is None:
+        raise ValueError("pack_weights takes fp16 or fp32 weights")
+    if w.dim() < 2:
+        raise ValueError("pack_weights takes [..., rows, cols]")
+    rows, cols = w.shape[-2], w.shape[-1]
+    out = torch.empty_like(w, memory_format=torch.contiguous_format)
+    moe_pack_weights(dtype, w.numel() // (rows * cols) if w.numel() else 0, rows, cols, w, out,
+                     stream)
+    return out
 
 
 def make_profile(events) -> Profile:

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["moe_api.cpp", "noalloc.hip", "eplb.cpp", "gemm_stream.hip", "gemm_tiled.hip",
-           "route_topk.hip", "dispatch.hip", "combine.hip", "expert_counts.hip"]
+           "route_topk.hip", "dispatch.hip", "combine.hip", "expert_counts.hip", "pack.hip"]
 
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 

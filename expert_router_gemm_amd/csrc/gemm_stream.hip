@@ -33,10 +33,16 @@
 // MFMA mapping (v_mfma_f32_16x16x32_f16, or 4x v_mfma_f32_16x16x4_f32 for
 // fp32): A = 16 weight rows (features), B = x^T (16 rows = tokens).  Lane l
 // reads 16 contiguous bytes of weight row l%16 and of token row l%16 at the
-// same K offset, so a wave instruction covers 16 rows x 64 bytes and two
-// consecutive K chunks cover whole 128-byte lines.  Loads are double
-// buffered in registers, U chunks per buffer, to keep several KB per wave in
-// flight against HBM latency.
+// same K offset.  With row-major weights a wave instruction covers 16 rows x
+// 64 bytes and two consecutive K chunks cover whole 128-byte lines; with
+// weights in the fragment layout (frag_offset) the same 16 x 64 bytes are
+// one contiguous 1 KB, and those loads carry the nontemporal hint (every
+// weight byte is read once).  Measured on MI355X, the fragment layout with
+// the hint streams the gate/up weights about 11% faster than row-major
+// loads (about 6.9 against 6.2 TB/s); the hint on row-major loads, whose
+// two halves of a 128-byte line come from two instructions, is slower
+// instead.  Loads are double buffered in registers, U chunks per buffer, to
+// keep several KB per wave in flight against HBM latency.
 #include "common.h"
 #include "kernels.h"
 
@@ -82,20 +88,25 @@ struct XFrag<f16, DT_FP8> {  // 8 fp8 codes, decoded to fp16 * 2^-8
     __device__ static __forceinline__ f16x8 cvt(const raw &v) { return e4m3x8_to_f16x8_scaled(v); }
 };
 
-// Weight loads: every weight byte is read exactly once per launch.
-template <typename T>
+// Weight loads: every weight byte is read exactly once per launch; NT marks
+// the load nontemporal (fragment layout only, see above).
+template <bool NT, typename T>
 __device__ __forceinline__ typename Frag<T>::vec wload16(const T *p) {
-    return load16(p);
+    if constexpr (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<const typename Frag<T>::vec *>(p));
+    else
+        return load16(p);
 }
 
 // NSUB 16-feature subtiles per wave; NM = weight tiles per K chunk (SwiGLU:
 // gate subtiles 0..NSUB-1, then the up subtiles; otherwise NM = NSUB).
+// FR: weights in the fragment layout (N a multiple of 16).
 // KW == 1: the wave runs K slice kz of ksplit and finishes its features.
 // KW == 4: the block's 4 waves share the same NSUB = 4 subtiles, wave w
 // runs quarter w of K; the partials meet in LDS (red) and are summed in K
 // order, then wave w finishes subtile w.  Every activation fragment then
 // serves 4x as many weight rows while a block still streams 64 features.
-template <typename TW, int XM, int NSUB, int EPI, int KW, int MT, int U>
+template <typename TW, int XM, int NSUB, int EPI, int KW, int MT, int U, bool FR>
 __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, int rstart,
                                             int r0, int r1, int kz, f32x4 *red) {
     constexpr bool SW = EPI == EPI_SWIGLU;
@@ -116,15 +127,25 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
 
     // weight rows (clamped: rows past N are read but never stored).  Tile m
     // covers rows f0 + 16 * (m % NSUB) .. +15 of the gate matrix (w0) for
-    // m < NSUB and of the up matrix (w1) above (SwiGLU).
+    // m < NSUB and of the up matrix (w1) above (SwiGLU).  Fragment layout:
+    // the tile's first fragment of this K slice; a K chunk is 1 KB further.
+    constexpr int WSTEP = FR ? 16 * CK : CK;  // elements from one K chunk to the next
     const TW *wp[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-        int wrow = f0 + 16 * (m % NSUB) + lr;
-        if (wrow > a.N - 1) wrow = a.N - 1;
-        const size_t off = (size_t)g * a.w_group_stride + (size_t)wrow * K + (size_t)ksl * KS +
-                           (size_t)lg * EL;
-        wp[m] = reinterpret_cast<const TW *>(m < NSUB ? a.w0 : a.w1) + off;
+        size_t off;
+        if constexpr (FR) {
+            int gi = f0 / 16 + (m % NSUB);
+            if (gi > a.N / 16 - 1) gi = a.N / 16 - 1;
+            off = ((size_t)gi * (K / CK) + (size_t)ksl * (KS / CK)) * (16 * CK) +
+                  (size_t)lane * EL;
+        } else {
+            int wrow = f0 + 16 * (m % NSUB) + lr;
+            if (wrow > a.N - 1) wrow = a.N - 1;
+            off = (size_t)wrow * K + (size_t)ksl * KS + (size_t)lg * EL;
+        }
+        wp[m] = reinterpret_cast<const TW *>(m < NSUB ? a.w0 : a.w1) +
+                (size_t)g * a.w_group_stride + off;
     }
     // token rows (clamped to the group's last row; extra columns are dropped)
     size_t xo[MT];
@@ -150,7 +171,7 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
 #define MOE_LOAD(WBUF, XBUF, c)                                                  \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                              \
         _Pragma("unroll") for (int m = 0; m < NM; ++m) WBUF[u][m] =              \
-            wload16(wp[m] + (size_t)((c) + u) * CK);                             \
+            wload16<FR>(wp[m] + (size_t)((c) + u) * WSTEP);                      \
         _Pragma("unroll") for (int t = 0; t < MT; ++t) XBUF[u][t] =              \
             XF::load(a.x, xo[t] + (size_t)((c) + u) * CK);                       \
     }
@@ -266,7 +287,7 @@ __device__ __forceinline__ void stream_pass(const StreamArgs &a, int g, int f0, 
     }
 }
 
-template <typename TW, int XM, int NSUB, int EPI, int KW, int U>
+template <typename TW, int XM, int NSUB, int EPI, int KW, int U, bool FR>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
     constexpr int FPW = 16 * NSUB;  // features per wave
     constexpr int NM = EPI == EPI_SWIGLU ? 2 * NSUB : NSUB;
@@ -303,26 +324,38 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
         constexpr int U2 = U;
         constexpr int U4 = KW > 1 ? 1 : (U > 2 ? 2 : U);
         if (n <= 16)
-            stream_pass<TW, XM, NSUB, EPI, KW, 1, U>(b, g, f0, rs, r0, r1, kz, red);
+            stream_pass<TW, XM, NSUB, EPI, KW, 1, U, FR>(b, g, f0, rs, r0, r1, kz, red);
         else if (n <= 32)
-            stream_pass<TW, XM, NSUB, EPI, KW, 2, U2>(b, g, f0, rs, r0, r1, kz, red);
+            stream_pass<TW, XM, NSUB, EPI, KW, 2, U2, FR>(b, g, f0, rs, r0, r1, kz, red);
         else
-            stream_pass<TW, XM, NSUB, EPI, KW, 4, U4>(b, g, f0, rs, r0, r1, kz, red);
+            stream_pass<TW, XM, NSUB, EPI, KW, 4, U4, FR>(b, g, f0, rs, r0, r1, kz, red);
     }
 }
 
-template <typename TW, int XM, int NSUB, int EPI, int U = kU, int KW = 1>
-hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t s) {
+template <typename TW, int XM, int NSUB, int EPI, int U, int KW, bool FR>
+hipError_t launch_l(const StreamArgs &a, int n_groups, int zblocks, hipStream_t s) {
     constexpr int FPB = (KW > 1 ? 1 : 4) * 16 * NSUB;  // features per block
     dim3 grid((a.N + FPB - 1) / FPB, n_groups + a.n_sec, zblocks * a.ksplit);
     constexpr int CK = 4 * Frag<TW>::kElems;
     const int NC = a.K / (a.ksplit * KW) / CK;
     if (a.ksplit < 1 || a.K % (a.ksplit * KW * 4 * CK) != 0) return hipErrorInvalidValue;
+    if (FR && a.N % 16 != 0) return hipErrorInvalidValue;
     if (NC % (2 * U) == 0)
-        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NSUB, EPI, KW, U>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NSUB, EPI, KW, U, FR>), grid, dim3(256), 0,
+                           s, a);
     else
-        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NSUB, EPI, KW, 2>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((stream_gemm_kernel<TW, XM, NSUB, EPI, KW, 2, FR>), grid, dim3(256), 0,
+                           s, a);
     return hipGetLastError();
+}
+
+// Expert GEMMs take either weight layout; the router's weights are row-major.
+template <typename TW, int XM, int NSUB, int EPI, int U = kU, int KW = 1>
+hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t s) {
+    if constexpr (EPI != EPI_LOGITS) {
+        if (a.w_frag) return launch_l<TW, XM, NSUB, EPI, U, KW, true>(a, n_groups, zblocks, s);
+    }
+    return launch_l<TW, XM, NSUB, EPI, U, KW, false>(a, n_groups, zblocks, s);
 }
 
 }  // namespace

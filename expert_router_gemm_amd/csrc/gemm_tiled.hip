@@ -15,7 +15,10 @@
 // Operands go from global memory straight into LDS (buffer/global loads with
 // the lds modifier: no register staging), two stages for 256-row tiles and
 // three for 128-row ones, one barrier per K step, XOR-swizzled LDS rows (see
-// swz()).
+// swz()).  Expert weights in the fragment layout (frag_offset) are staged
+// fragment by fragment: one wave load is one contiguous 1 KB fragment and
+// lands in LDS in the order the MFMA reads it (lane l's 16 bytes at 16 l),
+// so those reads need no swizzle.
 //
 // The grid is persistent (all resident workgroup slots): see tiled_gemm_kernel;
 // a workgroup's items share one pipeline where rows are not gathered (see
@@ -193,7 +196,7 @@ __device__ __forceinline__ void wait_vm() {
 // filled row tile of a group) skips its fragment reads and MFMAs.  Items
 // chain (the steps past an item's end load the next item's first ones)
 // unless x rows are gathered.
-template <int TBM, int NM, int EPI, bool GATHER>
+template <int TBM, int NM, int EPI, bool GATHER, bool FR>
 __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 *Bs,
                                               const int *tstart, int n_groups, int n_ntiles,
                                               int ks, const ItemSeq seq) {
@@ -225,9 +228,16 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
 #pragma unroll
     for (int i = 0; i < XL; ++i) xoff[i] = (wave * XW + i * RPI + rsub) * K * 2 + gch * 16;
     const int wmat = (wave * 32) / FN;  // the weight matrix this wave stages
+    // fragment layout: load i is fragment (16-row group wr0/16 + i/2, 64-byte
+    // K chunk i%2 of the step); LDS holds a stage's fragments in (row group,
+    // chunk) order, 2 KB per row group.  The step's K offset kb (bytes of a
+    // row-major row) is 16 kb bytes into the fragments.
+    static_assert(!FR || WL == 4, "a wave stages two row groups x two K chunks");
+    const int wr0 = (wave * 32) % FN;  // first row this wave stages, in its matrix
 #pragma unroll
     for (int i = 0; i < WL; ++i)
-        woff[i] = ((wave * 32 + i * RPI + rsub) % FN) * K * 2 + gch * 16;
+        woff[i] = FR ? ((wr0 / 16 + i / 2) * (K / 32) + i % 2) * 1024 + lane * 16
+                     : ((wave * 32 + i * RPI + rsub) % FN) * K * 2 + gch * 16;
     constexpr int ASTAGE = TBM * BK * 2, BSTAGE = WR * BK * 2;  // bytes
     const uint32_t a_m0 = lds_addr(As) + wave * XW * BK * 2;
     const uint32_t b_m0 = lds_addr(Bs) + wave * 32 * BK * 2;
@@ -266,7 +276,8 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
         const f16 *wb1 = to_nxt ? nxt.wb[NM - 1] : cur.wb[NM - 1];
         const u32x4 wr = srd(wmat == 0 ? wb0 : wb1, to_nxt ? nxt.wbytes : cur.wbytes);
 #pragma unroll
-        for (int i = 0; i < WL; ++i) dma_buf16(wr, b_m0 + st * BSTAGE + i * 1024, woff[i], kb);
+        for (int i = 0; i < WL; ++i)
+            dma_buf16(wr, b_m0 + st * BSTAGE + i * 1024, woff[i], FR ? kb * 16 : kb);
     };
 
     // Fragment reads: the weight fragments first, then the row fragments in
@@ -282,9 +293,11 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJ; ++j) {
+                const int wrow = m * FN + wn * (FN / WNW) + j * 16;  // fragment's first row
                 bf[m][j] = *reinterpret_cast<const f16x8 *>(
-                    B + swz(m * FN + wn * (FN / WNW) + j * 16 + lr, ch));
+                    FR ? B + ((wrow / 16) * 2 + kq / 4) * 512 + lane * 8 : B + swz(wrow + lr, ch));
+            }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -458,7 +471,7 @@ constexpr size_t tile_lds_bytes() {
     return (size_t)n_stages<TBM>() * (TBM + WR) * BK * sizeof(f16);
 }
 
-template <int TBM, int NM, int EPI, bool GATHER>
+template <int TBM, int NM, int EPI, bool GATHER, bool FR>
 __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int n_ntiles,
                                                               int n_groups) {
     extern __shared__ __attribute__((aligned(16))) f16 lds[];
@@ -507,12 +520,12 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
         seq.end = total;
         seq.chunked = false;
     }
-    run_items_dma<TBM, NM, EPI, GATHER>(a, As, Bs, tstart, n_groups, n_ntiles, ks, seq);
+    run_items_dma<TBM, NM, EPI, GATHER, FR>(a, As, Bs, tstart, n_groups, n_ntiles, ks, seq);
 }
 
 // max_tiles bounds the 128-row tiles (so also the taller ones): it only
 // sizes the grid, surplus workgroups find no item and exit.
-template <int TBM, int NM, int EPI, bool GATHER>
+template <int TBM, int NM, int EPI, bool GATHER, bool FR>
 hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream_t s) {
     if (n_groups <= 0 || n_groups > kMaxGroups) return hipErrorInvalidValue;
     const int n_ntiles = (a.N + WR / NM - 1) / (WR / NM);
@@ -526,13 +539,13 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
     int slots = dev < kMaxDevices ? resident[dev].load(std::memory_order_acquire) : 0;
     if (slots <= 0) {
-        hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<TBM, NM, EPI, GATHER>,
+        hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         int cus = 256, per_cu = 1;
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, tiled_gemm_kernel<TBM, NM, EPI, GATHER>, kThreads, lds) != hipSuccess ||
+                &per_cu, tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR>, kThreads, lds) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
         slots = cus * per_cu;
@@ -542,7 +555,7 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
     long grid = slots;
     const long items = max_tiles * n_ntiles * (EPI == 2 ? a.ksplit : 1);
     if (items < grid) grid = items > 0 ? items : 1;
-    hipLaunchKernelGGL((tiled_gemm_kernel<TBM, NM, EPI, GATHER>), dim3((unsigned)grid), dim3(kThreads),
+    hipLaunchKernelGGL((tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR>), dim3((unsigned)grid), dim3(kThreads),
                        lds, s, a, n_ntiles, n_groups);
     return hipGetLastError();
 }
@@ -561,11 +574,19 @@ bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype) {
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,
                              hipStream_t s) {
     constexpr int XB = kExpertRows;
-    if (mode == STREAM_SWIGLU)
-        return a.gather ? launch_t<XB, 2, 1, true>(a, n_groups, max_tiles, s)
-                        : launch_t<XB, 2, 1, false>(a, n_groups, max_tiles, s);
-    if (mode == STREAM_STORE) return launch_t<XB, 1, 0, false>(a, n_groups, max_tiles, s);
-    return launch_t<kTiledRouterRows, 1, 2, false>(a, n_groups, max_tiles, s);
+    if (a.w_frag && a.N % 16 != 0) return hipErrorInvalidValue;
+    if (mode == STREAM_SWIGLU) {
+        if (a.w_frag)
+            return a.gather ? launch_t<XB, 2, 1, true, true>(a, n_groups, max_tiles, s)
+                            : launch_t<XB, 2, 1, false, true>(a, n_groups, max_tiles, s);
+        return a.gather ? launch_t<XB, 2, 1, true, false>(a, n_groups, max_tiles, s)
+                        : launch_t<XB, 2, 1, false, false>(a, n_groups, max_tiles, s);
+    }
+    if (mode == STREAM_STORE)
+        return a.w_frag ? launch_t<XB, 1, 0, false, true>(a, n_groups, max_tiles, s)
+                        : launch_t<XB, 1, 0, false, false>(a, n_groups, max_tiles, s);
+    // router weights are row-major
+    return launch_t<kTiledRouterRows, 1, 2, false, false>(a, n_groups, max_tiles, s);
 }
 
 }  // namespace moe

@@ -21,6 +21,8 @@ struct StreamArgs {
     const void *w0;         // [G][N][K]: gate (SWIGLU) or the only matrix
     const void *w1;         // [G][N][K]: up (SWIGLU only)
     size_t w_group_stride;  // elements from one group's matrix to the next
+    int w_frag;             // weights (w0, w1, w0b, w1b) in the fragment
+                            // layout (see frag_offset), else row-major
     void *out;              // [rows][out_ld]
     int out_ld;
     int N, K;
@@ -37,6 +39,18 @@ struct StreamArgs {
     const void *w0b, *w1b;
     int rows2, row2_base;
 };
+
+// Fragment layout of a [N][K] weight matrix (N a multiple of 16, K * esize
+// a multiple of 64 bytes): 1 KB fragments, fragment (i, j) = rows 16i..16i+15
+// x the 64 bytes of K from byte 64j, stored at byte (i * (K*esize/64) + j) *
+// 1024; inside it, byte 256q + 16r + c is row 16i + r, row byte 64j + 16q +
+// c.  Lane 16q + r of a wave thus reads one contiguous 1 KB per fragment --
+// the MFMA operand layout (row r, K quarter q) that a row-major wave load
+// gathers from 16 rows.  Byte offset of (row n, row byte b):
+__host__ __device__ inline size_t frag_offset(size_t n, size_t b, size_t row_bytes) {
+    return ((n >> 4) * (row_bytes >> 6) + (b >> 6)) * 1024 + ((b >> 4) & 3) * 256 +
+           (n & 15) * 16 + (b & 15);
+}
 
 // dtype: DT_F16 / DT_F32 (weights and output); x_dtype: dtype or DT_FP8.
 // Grid: ceil(N/64) x n_groups x zblocks; see gemm_stream.hip.
@@ -99,5 +113,11 @@ struct CombineArgs {
     void *out;
 };
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- layout
+// dst[m] = fragment layout of the row-major src[m] ([rows][row_bytes]),
+// m < n_mats (rows % 16 == 0, row_bytes % 64 == 0, no overlap).
+hipError_t launch_pack_frag(const void *src, void *dst, long n_mats, int rows, int row_bytes,
+                            hipStream_t s);
 
 }  // namespace moe

@@ -25,6 +25,9 @@ constexpr int64_t kMaxTokens = 1 << 20;
 // hidden and inter: the LDS-tiled GEMM forms a tile's byte ranges and row
 // offsets (up to 256 rows of K fp16 values) in 32 bits
 constexpr int kMaxDim = 65536;
+// moe_pack_weights: matrices per call (a whole layer's gate, up or down
+// weights, replicas included, is at most a few thousand).
+constexpr int64_t kMaxPackMats = 1 << 20;
 
 inline size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -80,6 +83,7 @@ size_t route_ws_bytes(const moe_shape &s, int T) {
 moe_status check_shape(const moe_shape *s) {
     if (!s) return MOE_ERR_INVALID_ARG;
     if (s->flags & ~MOE_F_SHARED) return MOE_ERR_INVALID_ARG;
+    if (s->w_layout != MOE_W_ROWMAJOR && s->w_layout != MOE_W_FRAG) return MOE_ERR_INVALID_ARG;
     if (s->hidden <= 0 || s->inter <= 0 || s->hidden % 128 || s->inter % 128) return MOE_ERR_SHAPE;
     if (s->hidden > kMaxDim || s->inter > kMaxDim) return MOE_ERR_SHAPE;
     if (s->n_experts < 1 || s->n_experts > kMaxExperts) return MOE_ERR_SHAPE;
@@ -296,6 +300,7 @@ hipError_t ffn_up_impl(const moe_shape &s, int n_groups, int zblocks, long est_r
     a.w0 = w_gate;
     a.w1 = w_up;
     a.w_group_stride = (size_t)s.inter * s.hidden;
+    a.w_frag = s.w_layout == MOE_W_FRAG;
     a.out = hm;
     a.out_ld = s.inter;
     a.N = s.inter;
@@ -315,6 +320,7 @@ hipError_t ffn_down_impl(const moe_shape &s, int n_groups, int zblocks, long est
     a.rows_per_group = rows_per_group;
     a.w0 = w_down;
     a.w_group_stride = (size_t)s.hidden * s.inter;
+    a.w_frag = s.w_layout == MOE_W_FRAG;
     a.out = y;
     a.out_ld = s.hidden;
     a.N = s.hidden;
@@ -529,6 +535,24 @@ MOE_EXPORT moe_status moe_expert_counts(const moe_shape *shape, int32_t T,
     TRY(device_ok());
     LAUNCH(launch_expert_counts(topk_idx, (long)T * shape->top_k, shape->n_experts, counts,
                                 (hipStream_t)stream));
+    return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_pack_weights(int32_t dtype, int64_t n_mats, int32_t rows,
+                                       int32_t cols, const void *src, void *dst, void *stream) {
+    if (dtype != MOE_F16 && dtype != MOE_F32) return MOE_ERR_DTYPE;
+    const int esize = dtype == MOE_F16 ? 2 : 4;
+    if (n_mats < 0 || n_mats > kMaxPackMats) return MOE_ERR_SHAPE;
+    if (rows < 16 || rows > kMaxDim || rows % 16) return MOE_ERR_SHAPE;
+    if (cols < 1 || cols > kMaxDim || ((int64_t)cols * esize) % 64) return MOE_ERR_SHAPE;
+    TRY(need(src));
+    TRY(need(dst));
+    const uint64_t bytes = (uint64_t)n_mats * (uint64_t)rows * (uint64_t)cols * (uint64_t)esize;
+    const uint64_t a = (uint64_t)(uintptr_t)src, b = (uint64_t)(uintptr_t)dst;
+    if (bytes > 0 && a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // overlap
+    if (n_mats == 0) return MOE_OK;
+    TRY(device_ok());
+    LAUNCH(launch_pack_frag(src, dst, (long)n_mats, rows, cols * esize, (hipStream_t)stream));
     return MOE_OK;
 }
 

@@ -27,6 +27,8 @@
  *     length n to m outputs is stored [m][n], i.e. the transpose of the
  *     page's [in, out] math shapes (router [7168, 256], gate/up
  *     [7168, 2048], down [2048, 7168]).  Every row starts 16-byte aligned.
+ *     Expert weights (routed and shared) may instead be in the fragment
+ *     layout MOE_W_FRAG (moe_shape.w_layout, moe_pack_weights).
  *   - dtype: MOE_F16 (fp16 activations and weights, fp32 accumulation,
  *     fp16 outputs) or MOE_F32 (fp32 throughout).  Dispatched rows may be
  *     MOE_FP8_E4M3 with one fp32 scale per row (F16 layers only).
@@ -75,6 +77,25 @@ typedef enum { MOE_F32 = 0, MOE_F16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 /* moe_shape.flags */
 #define MOE_F_SHARED 1u /* layer has shared experts: add their gated sum */
 
+/* moe_shape.w_layout: how the expert weights (w_gate, w_up, w_down and the
+ * shared experts' sh_*) of a layer are stored; the router stays row-major.
+ *   MOE_W_ROWMAJOR  each matrix [rows][cols] row-major.
+ *   MOE_W_FRAG      each matrix [rows][cols] (rows % 16 == 0, a row of
+ *                   rb = cols * esize bytes, rb % 64 == 0) as 1 KB fragments:
+ *                   fragment (i, j), i < rows / 16, j < rb / 64, sits at byte
+ *                   (i * (rb / 64) + j) * 1024 of the matrix and holds rows
+ *                   16i .. 16i+15 x row bytes 64j .. 64j+63; its byte
+ *                   256 q + 16 r + c (q < 4, r < 16, c < 16) is byte
+ *                   64j + 16q + c of row 16i + r.  That is the operand layout
+ *                   of the matrix cores' 16 x 16 x 32 fp16 product, one
+ *                   16-byte piece per lane, so the expert GEMMs read each
+ *                   operand tile as one contiguous 1 KB (decode streams the
+ *                   weights about 11% faster on MI355X).  A matrix keeps its
+ *                   size and position: slot s of w_gate still starts at
+ *                   element s * I * H.  moe_pack_weights converts. */
+#define MOE_W_ROWMAJOR 0
+#define MOE_W_FRAG 1
+
 /* Where the expert GEMM finds the input row of output row r of group g
  * (x_rows argument of moe_expert_ffn_up / moe_expert_ffn). */
 #define MOE_X_PERMUTED 0 /* x[r]: rows already permuted (moe_dispatch's x_perm) */
@@ -105,6 +126,8 @@ typedef struct {
      * 1 <= topk_groups <= n_groups, top_k <= topk_groups * E / n_groups. */
     int32_t n_groups;
     int32_t topk_groups;
+    int32_t w_layout;  /* MOE_W_ROWMAJOR or MOE_W_FRAG (other values:
+                          MOE_ERR_INVALID_ARG) */
 } moe_shape;
 
 /* Expert -> local slot table (device arrays), sections 2.1 and 6.3.
@@ -208,6 +231,19 @@ moe_status moe_expert_ffn(const moe_shape *shape, int32_t n_groups, int32_t cap_
 moe_status moe_combine(const moe_shape *shape, int32_t T, const void *y,
                        const int32_t *inv_pos, const float *topk_w, const void *shared_y,
                        const float *shared_gate, void *out, void *stream);
+
+/* Expert weights into the fragment layout (see MOE_W_FRAG), once, when
+ * they are loaded: dst[m] = MOE_W_FRAG form of the row-major src[m], for
+ * n_mats matrices [rows][cols] of dtype MOE_F16 or MOE_F32 stored back to
+ * back (e.g. all S slots of w_gate: n_mats = S, rows = I, cols = H).
+ * Limits: 16 <= rows <= 65536, rows % 16 == 0; 1 <= cols <= 65536,
+ * cols * esize % 64 == 0; 0 <= n_mats <= 2^20 (0: nothing enqueued).
+ * src and dst are 16-byte aligned and must not overlap
+ * (MOE_ERR_INVALID_ARG); the caller owns both.  A pure permutation: the
+ * products over the packed weights are bitwise those over the row-major
+ * ones. */
+moe_status moe_pack_weights(int32_t dtype, int64_t n_mats, int32_t rows, int32_t cols,
+                            const void *src, void *dst, void *stream);
 
 /* Steps 1-5 for T tokens: moe_route, moe_dispatch, moe_expert_ffn on the
  * routed groups and (MOE_F_SHARED) on the shared experts, moe_combine.

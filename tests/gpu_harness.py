@@ -22,6 +22,10 @@ DEV = "cuda:0"
 # Stated tolerance on layer outputs (fp16 outputs, fp32 accumulation).
 ATOL, RTOL = 2e-3, 2e-2
 
+# Expert weights are uploaded in the layout the benchmark runs (the
+# fragment layout); tests of the row-major layout ask for it explicitly.
+DEFAULT_W_LAYOUT = moe.MOE_W_FRAG
+
 
 def within_tol(gpu, ref, atol=ATOL, rtol=RTOL):
     gpu = np.asarray(gpu, np.float64)
@@ -84,10 +88,13 @@ class Layer:
 
 def build_layer(cfg, *, rank: Optional[int] = None, T: Optional[int] = None,
                 bias_override: Optional[np.ndarray] = None, keep_host_weights=True,
-                slot_seed: Optional[int] = None) -> Layer:
+                slot_seed: Optional[int] = None, w_layout: Optional[int] = None) -> Layer:
     """Generate the workload's inputs and upload them.
 
-    rank: which EP rank this GPU plays (default: the workload's own)."""
+    rank: which EP rank this GPU plays (default: the workload's own).
+    w_layout: MOE_W_FRAG (default; packed on the device by moe_pack_weights)
+    or MOE_W_ROWMAJOR for the expert weights; host copies stay row-major."""
+    w_layout = DEFAULT_W_LAYOUT if w_layout is None else w_layout
     rank = cfg.ep_rank if rank is None else rank
     rep = moe_synth.replica_expert(cfg)
     rep_off, rep_slot, slot_experts = moe.build_slot_map(cfg.E, cfg.ep_size, rank,
@@ -114,11 +121,17 @@ def build_layer(cfg, *, rank: Optional[int] = None, T: Optional[int] = None,
         shared = moe_synth.gen_shared_weights(cfg)
         d.update(SG=to_dev(shared[0]), SU=to_dev(shared[1]), SD=to_dev(shared[2]))
     d.update(rep_off=to_dev(rep_off), rep_slot=to_dev(rep_slot))
+    if w_layout == moe.MOE_W_FRAG:
+        for k in ("G", "U", "D", "SG", "SU", "SD"):
+            if k in d:
+                d[k] = moe.pack_weights(d[k])  # the row-major copy is freed
+        G, U, D = d["G"], d["U"], d["D"]
+        torch.cuda.synchronize()
     shape = moe.make_shape(hidden=cfg.H, inter=cfg.I, n_experts=cfg.E, top_k=cfg.K, n_slots=S,
                            n_shared=cfg.n_shared, act=act_code(cfg),
                            dispatch=moe.MOE_FP8_E4M3 if cfg.dispatch == "fp8" else None,
                            shared=cfg.n_shared > 0, n_groups=cfg.n_groups,
-                           topk_groups=cfg.topk_groups)
+                           topk_groups=cfg.topk_groups, w_layout=w_layout)
     wmap = moe.make_weights(w_router=d["wr"], bias=d["bias"], w_gate=G, w_up=U, w_down=D,
                             sh_gate=d.get("SG"), sh_up=d.get("SU"), sh_down=d.get("SD"))
     seed = cfg.seed if slot_seed is None else slot_seed

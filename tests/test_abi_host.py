@@ -86,6 +86,7 @@ def _route(shape, T=16, **ptr):
     (dict(n_groups=7, topk_groups=2), 2), (dict(n_groups=8, topk_groups=0), 2),
     (dict(n_groups=8, topk_groups=9), 2), (dict(n_groups=128, topk_groups=1), 2),
     (dict(n_groups=64, topk_groups=1), 2), (dict(n_groups=0, topk_groups=2), 2),
+    (dict(w_layout=2), 1), (dict(w_layout=-1), 1),
 ])
 def test_route_rejects_bad_shapes(kw, status):
     assert _route(_shape(**kw)) == status
@@ -221,3 +222,36 @@ def test_noalloc_entry_validates_before_touching_a_device():
     assert moe.moe_workspace_bytes(s, 256) <= moe.MOE_NOALLOC_SCRATCH_BYTES
     assert moe.moe_workspace_bytes(s, 1024) > moe.MOE_NOALLOC_SCRATCH_BYTES
     assert fwd(s, 1024) == 5                                   # beyond the array
+
+
+def test_pack_weights_validates_before_launch():
+    """moe_pack_weights: dtype, then sizes (rows a multiple of 16, a row a
+    multiple of 64 bytes, both at most 65536), then pointers and overlap."""
+    L = moe.lib()
+    F16, F32 = moe.MOE_F16, moe.MOE_F32
+    pk = lambda dt, n, r, c, src=FAKE, dst=FAKE + (1 << 36): L.moe_pack_weights(  # noqa: E731
+        dt, n, r, c, src, dst, None)
+    assert pk(moe.MOE_FP8_E4M3, 1, 16, 64) == 3
+    assert pk(7, 1, 16, 32) == 3
+    assert pk(F16, 1, 8, 32) == 2            # rows < 16
+    assert pk(F16, 1, 24, 32) == 2           # rows % 16
+    assert pk(F16, 1, 65536 + 16, 32) == 2   # rows > 65536
+    assert pk(F16, 1, 16, 16) == 2           # 32-byte rows
+    assert pk(F32, 1, 16, 8) == 2            # 32-byte rows
+    assert pk(F16, 1, 16, 65536 + 32) == 2   # cols > 65536
+    assert pk(F16, -1, 16, 32) == 2
+    assert pk(F16, (1 << 20) + 1, 16, 32) == 2
+    assert pk(F16, 1, 16, 32, src=None) == 1
+    assert pk(F16, 1, 16, 32, dst=FAKE + 8) == 4
+    assert pk(F16, 2, 16, 32, dst=FAKE + 1024) == 1   # 2 KB from FAKE: overlaps
+    assert pk(F16, 2, 16, 32, src=FAKE + 1024, dst=FAKE) == 1  # ... either way round
+    assert pk(F16, 0, 16, 32) == 0                    # nothing to do
+    assert moe.MOE_W_ROWMAJOR == 0 and moe.MOE_W_FRAG == 1
+
+
+@pytest.mark.skipif(_gpu_present(), reason="a device is present: valid calls would launch")
+def test_valid_pack_without_device_reports_no_device():
+    L = moe.lib()
+    assert L.moe_pack_weights(moe.MOE_F16, 1, 16, 32, FAKE, FAKE + 4096, None) == 6
+    # 1 KB matrices 1 KB apart: adjacent, not overlapping
+    assert L.moe_pack_weights(moe.MOE_F16, 1, 16, 32, FAKE, FAKE + 1024, None) == 6

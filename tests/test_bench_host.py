@@ -14,11 +14,15 @@ import moe_synth
 
 # kernel names as rocprofv3 prints them (PMC runs: mangled; kernel traces:
 # demangled); template arguments <weight, x, subtiles, epilogue, K waves,
-# chunks> and <tile rows, matrices, epilogue, gathered>, epilogue 1 = SwiGLU
-STREAM = "_ZN3moe12_GLOBAL__N_118stream_gemm_kernelIDF16_Li1ELi4ELi{}ELi4ELi2EEEvNS_10StreamArgsE"
-STREAM_F32 = "void moe::(anonymous namespace)::stream_gemm_kernel<float, 1, 4, {}, 4, 2>(moe::StreamArgs)"
+# chunks, fragment layout> and <tile rows, matrices, epilogue, gathered,
+# fragment layout>, epilogue 1 = SwiGLU
+STREAM = ("_ZN3moe12_GLOBAL__N_118stream_gemm_kernelIDF16_Li1ELi4ELi{}ELi4ELi2ELb1EEEv"
+          "NS_10StreamArgsE")
+STREAM_F32 = ("void moe::(anonymous namespace)::stream_gemm_kernel<float, 1, 4, {}, 4, 2, false>"
+              "(moe::StreamArgs)")
 TILED = "void moe::(anonymous namespace)::tiled_gemm_kernel<{}>(moe::StreamArgs, int, int)"
-TILED_MANGLED = "_ZN3moe12_GLOBAL__N_117tiled_gemm_kernelILi256ELi2ELi1ELb{}EEEvNS_10StreamArgsEii"
+TILED_MANGLED = ("_ZN3moe12_GLOBAL__N_117tiled_gemm_kernelILi256ELi2ELi1ELb{}ELb1EEEv"
+                 "NS_10StreamArgsEii")
 COPY = ("void at::native::vectorized_elementwise_kernel<8, at::native::AUnaryFunctor<c10::Half, "
         "c10::Half, c10::Half, at::native::binary_internal::MulFunctor<float> >>(int)")
 
@@ -29,14 +33,15 @@ def test_dominant_kernel_is_the_swiglu_gate_up_launch():
     for epi in (0, 2):  # down projection, router logits
         assert not bench.is_dominant(STREAM.format(epi), "stream")
         assert not bench.is_dominant(STREAM_F32.format(epi), "stream")
-    assert bench.is_dominant(TILED.format("256, 2, 1, true"), "tiled")
+    assert bench.is_dominant(TILED.format("256, 2, 1, true, true"), "tiled")
+    assert bench.is_dominant(TILED.format("256, 2, 1, true, false"), "tiled")
     assert bench.is_dominant(TILED_MANGLED.format(1), "tiled")
-    for args in ("256, 1, 0, false", "128, 1, 2, false", "256, 2, 1, false"):
+    for args in ("256, 1, 0, false, true", "128, 1, 2, false, false", "256, 2, 1, false, true"):
         assert not bench.is_dominant(TILED.format(args), "tiled")
     assert not bench.is_dominant(TILED_MANGLED.format(0), "tiled")
     # one kind never matches the other's kernels
     assert not bench.is_dominant(STREAM.format(1), "tiled")
-    assert not bench.is_dominant(TILED.format("256, 2, 1, true"), "stream")
+    assert not bench.is_dominant(TILED.format("256, 2, 1, true, true"), "stream")
     assert bench.dominant_kind(4) == "tiled"
     assert all(bench.dominant_kind(n) == "stream" for n in (1, 2, 3, 5))
 
@@ -65,8 +70,8 @@ def test_pmc_summary_scales_each_counter_by_the_calibration_copy(tmp_path, monke
     """A 1 GiB copy reads 1 GiB and writes 1 GiB; whatever a counter reads
     for it fixes that counter's scale (here FETCH reads half, WRITE all)."""
     gib = 1 << 30
-    dom = TILED.format("256, 2, 1, true")
-    other = TILED.format("256, 1, 0, false")
+    dom = TILED.format("256, 2, 1, true, true")
+    other = TILED.format("256, 1, 0, false, true")
     _counter_csv(tmp_path / "fetch", [
         (dom, "FETCH_SIZE", 1000.0), (dom, "FETCH_SIZE", 1004.0), (dom, "FETCH_SIZE", 990.0),
         (other, "FETCH_SIZE", 9.0e6), (COPY, "FETCH_SIZE", gib / 1024 / 2)])
@@ -152,7 +157,7 @@ def test_kernel_labels_name_each_layer_kernel():
     assert bench.kernel_label(STREAM.format(1)) == "stream_gemm_kernel gate/up"
     assert bench.kernel_label(STREAM.format(0)) == "stream_gemm_kernel down"
     assert bench.kernel_label(STREAM_F32.format(2)) == "stream_gemm_kernel router"
-    assert bench.kernel_label(TILED.format("256, 2, 1, true")) == \
+    assert bench.kernel_label(TILED.format("256, 2, 1, true, true")) == \
         "tiled_gemm_kernel gate/up (256-row tiles)"
     assert bench.kernel_label(TILED_MANGLED.format(0).replace("Li2ELi1", "Li1ELi0")) == \
         "tiled_gemm_kernel down (256-row tiles)"
@@ -163,7 +168,7 @@ def test_kernel_labels_name_each_layer_kernel():
 
 def test_pmc_summary_of_every_kernel(tmp_path, monkeypatch):
     gib = 1 << 30
-    up, down = TILED.format("256, 2, 1, true"), TILED.format("256, 1, 0, false")
+    up, down = TILED.format("256, 2, 1, true, true"), TILED.format("256, 1, 0, false, true")
     _counter_csv(tmp_path / "fetch", [(up, "FETCH_SIZE", 100.0), (up, "FETCH_SIZE", 104.0),
                                       (down, "FETCH_SIZE", 50.0), (COPY, "FETCH_SIZE", gib / 2048)])
     _counter_csv(tmp_path / "write", [(up, "WRITE_SIZE", 3.0), (down, "WRITE_SIZE", 7.0),
@@ -188,8 +193,8 @@ def test_trace_summary_splits_the_prefill_leg(tmp_path):
     rows = [(STREAM.format(1), 0, 2000, 256, 256 * 32, 258, 1),
             (STREAM.format(1), 5000, 7000, 256, 256 * 32, 258, 1),
             (STREAM.format(1), 8000, 8100, 256, 256 * 32, 2, 2),
-            (TILED.format("128, 1, 2, false"), 10000, 10080, 512, 512 * 256, 1, 1),
-            (TILED.format("256, 2, 1, true"), 11000, 12000, 512, 512 * 256, 1, 1)]
+            (TILED.format("128, 1, 2, false, false"), 10000, 10080, 512, 512 * 256, 1, 1),
+            (TILED.format("256, 2, 1, true, true"), 11000, 12000, 512, 512 * 256, 1, 1)]
     with open(d / "run_kernel_trace.csv", "w") as f:
         f.write(cols + "\n")
         for r in rows:

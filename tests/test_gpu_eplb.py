@@ -65,15 +65,18 @@ def test_double_buffered_table_swap_matches_oracle():
     offA, slotA, seA = moe.moe_eplb_slot_map(st, ecfg, rank)
     assert list(seA) == list(range(per))
 
+    # expert weights in the fragment layout: each slot packed as it is loaded
+    pk = lambda a: moe.pack_weights(torch.from_numpy(a).to(gh.DEV))  # noqa: E731
     G = torch.zeros((S, cfg.I, cfg.H), dtype=torch.float16, device=gh.DEV)
     U = torch.zeros_like(G)
     D = torch.zeros((S, cfg.H, cfg.I), dtype=torch.float16, device=gh.DEV)
     host = {}
     for s, (e, (g, u, d)) in enumerate(moe_synth.iter_experts(cfg, seA)):
-        G[s].copy_(torch.from_numpy(g)), U[s].copy_(torch.from_numpy(u))
-        D[s].copy_(torch.from_numpy(d))
+        G[s].copy_(pk(g)), U[s].copy_(pk(u))
+        D[s].copy_(pk(d))
         host[int(e)] = (g, u, d)
-    shape = moe.make_shape(hidden=cfg.H, inter=cfg.I, n_experts=E, top_k=K, n_slots=S)
+    shape = moe.make_shape(hidden=cfg.H, inter=cfg.I, n_experts=E, top_k=K, n_slots=S,
+                           w_layout=moe.MOE_W_FRAG)
     hd, wrd, bd = gh.to_dev(h), gh.to_dev(wr), gh.to_dev(bias)
     w = moe.make_weights(w_router=wrd, bias=bd, w_gate=G, w_up=U, w_down=D)
     # two device tables (the double buffer), sized for the largest table
@@ -110,8 +113,8 @@ def test_double_buffered_table_swap_matches_oracle():
     # the copy's weights first, then table B into the other buffer
     g, u, d = moe_synth.gen_expert(cfg, e_new)
     host[e_new] = (g, u, d)
-    G[per].copy_(torch.from_numpy(g)), U[per].copy_(torch.from_numpy(u))
-    D[per].copy_(torch.from_numpy(d))
+    G[per].copy_(pk(g)), U[per].copy_(pk(u))
+    D[per].copy_(pk(d))
     tab[1][0].copy_(torch.from_numpy(offB))
     tab[1][1][: len(slotB)].copy_(torch.from_numpy(slotB))
     mapB = moe.make_slot_map(tab[1][0], tab[1][1], cfg.seed)

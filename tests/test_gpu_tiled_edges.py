@@ -9,7 +9,9 @@ The x rows are read three ways: already permuted, gathered through a row
 index (as the gate/up GEMM gathers h through perm_src; direct-to-LDS loads
 from per-lane addresses) and shared (every group reads the same rows, as
 the shared experts do).  H = 512 (the down projection's output spans two
-256-feature tiles), I = 384 (gate/up: three tiles of 128 features).
+256-feature tiles), I = 384 (gate/up: three tiles of 128 features).  Both
+weight layouts: row-major (XOR-swizzled LDS rows) and the fragment layout
+(fragment-ordered LDS).
 
 Bar: |gpu - ref| <= 2e-3 + 2e-2 |ref| on hm and y (fp16 outputs, fp32
 accumulation); rows past the last group are never written.
@@ -36,8 +38,9 @@ def _device():
     torch.cuda.init()
 
 
+@pytest.mark.parametrize("layout", ["frag", "rowmajor"])
 @pytest.mark.parametrize("x_rows", ["permuted", "gather", "shared"])
-def test_tiled_expert_gemms_at_tile_edges(x_rows):
+def test_tiled_expert_gemms_at_tile_edges(x_rows, layout):
     cfg = moe_synth.scaled_config(4, T=sum(SIZES), H=512, I=384, seed=41)
     G = len(SIZES)
     offsets = np.concatenate([[0], np.cumsum(SIZES)]).astype(np.int32)
@@ -63,15 +66,19 @@ def test_tiled_expert_gemms_at_tile_edges(x_rows):
         mode = moe.MOE_X_PERMUTED
 
     # est. rows per group (cap_rows / n_experts) >= 64 selects the tiled kernel
-    shape = moe.make_shape(hidden=cfg.H, inter=cfg.I, n_experts=G, top_k=1, n_slots=G)
+    frag = layout == "frag"
+    shape = moe.make_shape(hidden=cfg.H, inter=cfg.I, n_experts=G, top_k=1, n_slots=G,
+                           w_layout=moe.MOE_W_FRAG if frag else moe.MOE_W_ROWMAJOR)
     cap = P + 64  # rows past the last group stay untouched
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     xd, wgd, wud, wdd, offd = d(x), d(wg), d(wu), d(wd), d(offsets)
+    if frag:
+        wgd, wud, wdd = (moe.pack_weights(t) for t in (wgd, wud, wdd))
     gd = d(gather) if gather is not None else None
     sentinel = torch.tensor(12345.0, dtype=torch.float16)
     hm = torch.full((cap, cfg.I), sentinel.item(), dtype=torch.float16, device="cuda")
     y = torch.full((cap, cfg.H), sentinel.item(), dtype=torch.float16, device="cuda")
-    print(f"[tiled edges] x_rows={x_rows} groups={SIZES} P={P}", flush=True)
+    print(f"[tiled edges] x_rows={x_rows} layout={layout} groups={SIZES} P={P}", flush=True)
     moe.moe_expert_ffn_up(shape, G, cap, xd, moe.MOE_F16, None, mode, gd, offd, wgd, wud, hm)
     moe.moe_expert_ffn_down(shape, G, cap, hm, offd, wdd, y)
     torch.cuda.synchronize()
