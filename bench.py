@@ -676,6 +676,43 @@ def summarize_trace(trace_dir: str):
     return out
 
 
+# ------------------------------------------------------------------ context
+
+
+def library_gemm(reps: int = 20):
+    """For scale: torch's fp16 products (hipBLASLt) on the prefill expert
+    GEMM shapes, contiguous operands: one [M, K] x [K, N] product and the
+    same flops as 32 batched groups of 512 rows.  Not part of the layer."""
+    import torch
+    dev = "cuda:0"
+    torch.manual_seed(0)
+
+    def timed(fn, flops):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        return {"us": round(ms * 1e3, 1), "tflops": round(flops / (ms / 1e3) / 1e12, 1)}
+
+    out = {}
+    for (M, K, N) in [(16384, 7168, 4096), (16384, 2048, 7168), (8192, 8192, 8192)]:
+        a = torch.randn(M, K, device=dev, dtype=torch.float16)
+        b = torch.randn(K, N, device=dev, dtype=torch.float16)
+        out[f"mm {M}x{K} @ {K}x{N}"] = timed(lambda: torch.mm(a, b), 2 * M * K * N)
+    for (G, M, K, N) in [(32, 512, 7168, 4096), (32, 512, 2048, 7168)]:
+        a = torch.randn(G, M, K, device=dev, dtype=torch.float16)
+        b = torch.randn(G, K, N, device=dev, dtype=torch.float16)
+        out[f"bmm {G}x[{M}x{K} @ {K}x{N}]"] = timed(lambda: torch.bmm(a, b), 2 * G * M * K * N)
+    print(json.dumps({"library_gemm_fp16": out}))
+    return out
+
+
 # ------------------------------------------------------------------ main
 
 
@@ -749,6 +786,8 @@ def main():
                     help="per-kernel HBM traffic of every libmoe kernel of the two PMC runs")
     ap.add_argument("--eplb", action="store_true",
                     help="also report the EPLB-lite monitor cost and rank balance")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time torch's fp16 GEMMs on the prefill expert shapes")
     ap.add_argument("--w-layout", choices=["frag", "rowmajor"], default="frag",
                     help="expert weight layout: the fragment layout (default) or row-major")
     ap.add_argument("--groups", metavar="G,M", default=None,
@@ -778,6 +817,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.library_gemm:
+        library_gemm()
+        return 0
     import expert_router_gemm_amd as moe
     moe.lib()
     want_cpu = not args.no_cpu_baseline

@@ -50,23 +50,27 @@ namespace moe {
 
 namespace {
 
-// Kernel shapes (measured best on MI355X):
+// Kernel shapes (measured best on MI355X, fragment-layout weights):
 //   kU              K chunks per register buffer (double-buffered) of the
 //                   one-wave-per-slice shapes
 //   kStoreWideRows  expected rows per group from which the plain (down
-//                   projection) GEMM takes the wide shape (measured faster
-//                   from ~8 rows per group; one subtile per wave for fewer)
+//                   projection) GEMM takes the wide shape (one subtile per
+//                   wave is faster at 4 and 8 rows per group, the wide shape
+//                   at 15)
 //   kStoreNsubWide, kStoreUWide  subtiles per wave and K chunks per buffer
 //                   of that wide shape
 //   kSwigluNsub, kSwigluU  the SwiGLU GEMM's subtiles and chunks per buffer
+//   kSwigluUFp8     chunks per buffer when x is fp8 codes (the decode VALU
+//                   work per chunk makes one chunk per buffer ~1% faster)
 // The wide store shape, the SwiGLU GEMM and the fp16 router split K over
 // the 4 waves of a block (KW = 4) when K allows it.
 constexpr int kU = 8;
-constexpr int kStoreWideRows = 6;
+constexpr int kStoreWideRows = 12;
 constexpr int kStoreNsubWide = 4;
 constexpr int kStoreUWide = 2;
 constexpr int kSwigluNsub = 4;
 constexpr int kSwigluU = 2;
+constexpr int kSwigluUFp8 = 1;
 
 // Epilogues
 enum : int { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_LOGITS = 2 };
@@ -370,7 +374,8 @@ hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int m
         if (mode == STREAM_SWIGLU) {
             constexpr int NS = kSwigluNsub, U = kSwigluU, KW = 4;
             if (x_dtype == DT_FP8)
-                return kw_ok ? launch_t<f16, DT_FP8, NS, EPI_SWIGLU, U, KW>(a, n_groups, zblocks, s)
+                return kw_ok ? launch_t<f16, DT_FP8, NS, EPI_SWIGLU, kSwigluUFp8, KW>(a, n_groups,
+                                                                                    zblocks, s)
                              : launch_t<f16, DT_FP8, 1, EPI_SWIGLU>(a, n_groups, zblocks, s);
             return kw_ok ? launch_t<f16, DT_F16, NS, EPI_SWIGLU, U, KW>(a, n_groups, zblocks, s)
                          : launch_t<f16, DT_F16, 1, EPI_SWIGLU>(a, n_groups, zblocks, s);
