@@ -177,8 +177,20 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ par
         topk_w[(size_t)t * K + lane] = expf(my_v - m) / z;
     }
     if (has_gate && shared_gate && lane == 0) {
-        float zg = l[E];
-        for (int zs = 1; zs < nsplit; ++zs) zg += l[(size_t)zs * split_stride + E];
+        // the gate column's partials, summed in slice order like the logits
+        // (all loads issued before the first add when NS is known)
+        float zg;
+        if (NS > 0) {
+            float part[NS > 0 ? NS : 1];
+#pragma unroll
+            for (int zs = 0; zs < NS; ++zs) part[zs] = l[(size_t)zs * split_stride + E];
+            zg = part[0];
+#pragma unroll
+            for (int zs = 1; zs < NS; ++zs) zg += part[zs];
+        } else {
+            zg = l[E];
+            for (int zs = 1; zs < nsplit; ++zs) zg += l[(size_t)zs * split_stride + E];
+        }
         shared_gate[t] = sigmoidf_(zg);
     }
 }
