@@ -34,7 +34,10 @@
  *     MOE_FP8_E4M3 with one fp32 scale per row (F16 layers only).
  *   - stream: a hipStream_t; NULL is the default stream.  Every call only
  *     enqueues work on it and returns; outputs are valid once the stream
- *     reaches that point.
+ *     reaches that point.  The work is kernel launches only (no copy,
+ *     memset, allocation or synchronisation), so calls may be captured
+ *     into a HIP graph and replayed (after one eager call per device, which
+ *     sets up the per-device state below).
  *   - Return value: a synchronous status from host-side validation (shapes,
  *     NULL pointers, alignment, dtype combinations, workspace size), or
  *     MOE_ERR_LAUNCH if a kernel launch was rejected.  Nothing is enqueued
