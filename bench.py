@@ -679,6 +679,33 @@ def summarize_trace(trace_dir: str):
 # ------------------------------------------------------------------ context
 
 
+def _timed(fn, flops, reps):
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"us": round(ms * 1e3, 1), "tflops": round(flops / (ms / 1e3) / 1e12, 1)}
+
+
+def library_bmm(G, M, K, N, reps=10):
+    """torch.bmm (hipBLASLt) fp16 on G groups of [M, K] x [K, N], contiguous."""
+    import torch
+    torch.manual_seed(0)
+    a = torch.randn(G, M, K, device="cuda:0", dtype=torch.float16)
+    b = torch.randn(G, K, N, device="cuda:0", dtype=torch.float16)
+    r = _timed(lambda: torch.bmm(a, b), 2 * G * M * K * N, reps)
+    del a, b
+    torch.cuda.empty_cache()
+    return r
+
+
 def library_gemm(reps: int = 20):
     """For scale: torch's fp16 products (hipBLASLt) on the prefill expert
     GEMM shapes, contiguous operands: one [M, K] x [K, N] product and the
@@ -747,6 +774,20 @@ def prefill_record(K: int, warmup: int, w_layout: str = "frag"):
            "layer": layer_record(work, t)}
     rec["layer"]["stage_ms_one_pass"] = {k: round(v, 4) for k, v in t["stage_ms"].items()}
     free_gpu(ctx)
+    # context: the vendor library on the same gate/up flops, as uniform
+    # contiguous groups (no gather, no ragged tail, no fused epilogue)
+    # (equal groups holding this step's rows, and the same groups cut to a
+    # multiple of 256 rows, the library's best case)
+    G = cfg.E // cfg.ep_size  # local experts
+    rows = -(-work["P"] // G)
+    vendor = {}
+    for key, m in (("equal_groups", rows), ("aligned_groups", rows // 256 * 256)):
+        if m <= 0:
+            continue
+        lib = library_bmm(G, m, cfg.H, 2 * cfg.I)
+        vendor[key] = dict(lib, shape=f"{G} x [{m} x {cfg.H} @ {cfg.H} x {2 * cfg.I}]",
+                           tiled_over_vendor=round(rec["roofline"]["achieved"] / lib["tflops"], 3))
+    rec["vendor_bmm_gate_up"] = vendor
     return rec
 
 
