@@ -226,13 +226,17 @@ def expert_rows(x: np.ndarray, wg, wu, wd, want_hm: bool = False):
     return (y, hm) if want_hm else y
 
 
-def combine(y, inv_pos, topk_w, shared_y=None, shared_gate_v=None):
-    """Steps 4-5: gate-weighted sum (+ gated sum of shared experts)."""
+def combine(y, inv_pos, topk_w, shared_y=None, shared_gate_v=None, H=None):
+    """Steps 4-5: gate-weighted sum (+ gated sum of shared experts).
+
+    y [P, H] (P may be 0: no local pair); H is y's row length, or that of
+    shared_y, unless given."""
     y = _c(y, np.float32)
     inv_pos = _c(inv_pos, np.int32)
     topk_w = _c(topk_w, np.float32)
     T, K = inv_pos.shape
-    H = y.shape[1] if y.ndim == 2 and y.shape[0] else (shared_y.shape[-1] if shared_y is not None else 0)
+    if H is None:
+        H = y.shape[1] if y.ndim == 2 else (shared_y.shape[-1] if shared_y is not None else 0)
     n_sh = 0 if shared_y is None else shared_y.shape[0]
     out = np.empty((T, H), np.float32)
     if y.size == 0:

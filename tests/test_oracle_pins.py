@@ -535,6 +535,15 @@ def test_combine_consistent_with_layer():
     # no local pair and no shared term: exact zeros
     z = oracle.combine(y, np.full_like(inv, -1), res["topk_w"])
     assert np.all(z == 0)
+    # a rank share that received no pair at all (P = 0 rows of y): zeros of
+    # the full [T, H] shape, the row length taken from y's columns
+    z0 = oracle.combine(np.zeros((0, cfg.H), np.float32), np.full_like(inv, -1),
+                        res["topk_w"])
+    assert z0.shape == (len(inv), cfg.H) and np.all(z0 == 0)
+    # ... or, with the shared experts, exactly their gated sum
+    zs = oracle.combine(np.zeros((0, cfg.H), np.float32), np.full_like(inv, -1),
+                        res["topk_w"], shy, gs)
+    assert np.allclose(zs, gs[:, None] * shy.sum(0), rtol=1e-6, atol=1e-7)
 
 
 def test_layer_refuses_a_token_meeting_one_slot_twice():
