@@ -255,3 +255,17 @@ def test_valid_pack_without_device_reports_no_device():
     assert L.moe_pack_weights(moe.MOE_F16, 1, 16, 32, FAKE, FAKE + 4096, None) == 6
     # 1 KB matrices 1 KB apart: adjacent, not overlapping
     assert L.moe_pack_weights(moe.MOE_F16, 1, 16, 32, FAKE, FAKE + 1024, None) == 6
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback path: without libmoe.so every entry point raises (the
+    binding refuses to load instead of computing anything elsewhere)."""
+    import expert_router_gemm_amd.binding as b
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "libmoe.so"))
+    with pytest.raises(ImportError, match="no fallback"):
+        b.lib()
+    with pytest.raises(ImportError):
+        b.moe_workspace_bytes(_shape(), 16)
+    with pytest.raises(ImportError):
+        b.moe_pack_weights(moe.MOE_F16, 0, 16, 32, FAKE, FAKE + 4096)
