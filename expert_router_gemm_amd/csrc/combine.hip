@@ -7,8 +7,8 @@
 // token with no local pair and no shared term gets exact zeros.
 //
 // One block per token with one thread per 8 consecutive features (up to
-// 1024 threads: 896 for hidden 7168), so every y row of the token is read
-// once with 16-byte loads; the token's local pairs are compacted in k order
+// 1024 threads: 896 for hidden 7168; per two chunks of 8 for large batches),
+// so every y row of the token is read once with 16-byte loads; the token's local pairs are compacted in k order
 // into LDS first (one wave, a ballot and popcounts), and each thread loads
 // them 4 at a time.
 #include "common.h"
@@ -54,8 +54,9 @@ __device__ __forceinline__ void store8<float>(float *p, const float v[8]) {
 // Rows are summed in batches of 4 whose loads are in flight together (one
 // round trip per 4 rows instead of per row, at 4 fp16 vectors of registers).
 constexpr int kMaxPairs = 16;  // top-K limit of the shape check
+constexpr int kCombineTwoChunkT = 2048;  // tokens from which a thread sums two chunks
 
-template <typename T>
+template <typename T, int CH>
 __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
     __shared__ int rows[kMaxPairs];
     __shared__ float gates[kMaxPairs];
@@ -86,35 +87,50 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
     const bool sh = shy && a.n_shared > 0;
     const float gs = sh ? a.shared_gate[t] : 0.0f;
     T *out = reinterpret_cast<T *>(a.out) + (size_t)t * a.H;
-    for (int i = threadIdx.x * 8; i < a.H; i += blockDim.x * 8) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        // batches of 4 rows: their loads are in flight together
+    for (int i0 = threadIdx.x * 8; i0 < a.H; i0 += blockDim.x * 8 * CH) {
+        float acc[CH][8];
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[c][j] = 0.f;
+        // batches of 4 rows x CH chunks: their loads are in flight together
         for (int q0 = 0; q0 < np; q0 += 4) {
-            Raw8<T> v[4];
+            Raw8<T> v[4][CH];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (q0 + q < np) v[q].load(y + (size_t)rows[q0 + q] * a.H + i);
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int i = i0 + c * blockDim.x * 8;
+                    if (q0 + q < np && i < a.H) v[q][c].load(y + (size_t)rows[q0 + q] * a.H + i);
+                }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (q0 + q < np) {
                     const float g = gates[q0 + q];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) acc[j] += g * v[q][j];
+                    for (int c = 0; c < CH; ++c)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[c][j] += g * v[q][c][j];
                 }
             }
         }
-        if (sh) {
-            float sv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < a.n_shared; ++s) {
-                Raw8<T> u;
-                u.load(shy + ((size_t)s * a.T + t) * a.H + i);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) sv[j] += u[j];
+        for (int c = 0; c < CH; ++c) {
+            const int i = i0 + c * blockDim.x * 8;
+            if (i >= a.H) continue;
+            if (sh) {
+                float sv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < a.n_shared; ++s) {
+                    Raw8<T> u;
+                    u.load(shy + ((size_t)s * a.T + t) * a.H + i);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) sv[j] += u[j];
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[c][j] += gs * sv[j];
             }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] += gs * sv[j];
+            store8<T>(out + i, acc[c]);
         }
-        store8<T>(out + i, acc);
     }
 }
 
@@ -124,12 +140,24 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
     // one thread per 8 features, up to 1024 threads (whole waves)
     if (a.K < 1 || a.K > kMaxPairs) return hipErrorInvalidValue;
-    int threads = ((a.H / 8 + 63) / 64) * 64;
+    // Batches of thousands of tokens: two chunks of 8 features per thread
+    // (their loads in flight together, half-size blocks, twice the blocks
+    // per CU): prefill combine 86 -> 72 us at T = 16384.  Decode batches keep
+    // one chunk per thread (more waves for few tokens).  Same sums either way.
+    const bool two = a.T >= kCombineTwoChunkT;
+    int threads = ((a.H / (two ? 16 : 8) + 63) / 64) * 64;
     if (threads > 1024) threads = 1024;
-    if (a.dtype == DT_F16)
-        hipLaunchKernelGGL(combine_kernel<f16>, dim3(a.T), dim3(threads), 0, s, a);
-    else
-        hipLaunchKernelGGL(combine_kernel<float>, dim3(a.T), dim3(threads), 0, s, a);
+    if (a.dtype == DT_F16) {
+        if (two)
+            hipLaunchKernelGGL((combine_kernel<f16, 2>), dim3(a.T), dim3(threads), 0, s, a);
+        else
+            hipLaunchKernelGGL((combine_kernel<f16, 1>), dim3(a.T), dim3(threads), 0, s, a);
+    } else {
+        if (two)
+            hipLaunchKernelGGL((combine_kernel<float, 2>), dim3(a.T), dim3(threads), 0, s, a);
+        else
+            hipLaunchKernelGGL((combine_kernel<float, 1>), dim3(a.T), dim3(threads), 0, s, a);
+    }
     return hipGetLastError();
 }
 
