@@ -86,9 +86,13 @@ def log(msg):
 
 
 LAYOUT_NAME = {"frag": "fragment (MOE_W_FRAG)", "rowmajor": "row-major"}
+# where the combine runs (moe_shape.flags)
+COMBINE_NAME = {False: "separate launch",
+                True: "tail of the tiled down projection where it runs (MOE_F_FUSED_COMBINE)"}
 
 
-def setup(n: int, keep_host: bool = True, groups=None, w_layout: str = "frag"):
+def setup(n: int, keep_host: bool = True, groups=None, w_layout: str = "frag",
+          fused_combine: bool = False):
     import numpy as np
     import torch
 
@@ -140,7 +144,8 @@ def setup(n: int, keep_host: bool = True, groups=None, w_layout: str = "frag"):
                            act=moe.MOE_F32 if cfg.dtype == "f32" else moe.MOE_F16,
                            dispatch=moe.MOE_FP8_E4M3 if fp8 else None, shared=cfg.n_shared > 0,
                            n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
-                           w_layout=moe.MOE_W_FRAG if w_layout == "frag" else moe.MOE_W_ROWMAJOR)
+                           w_layout=moe.MOE_W_FRAG if w_layout == "frag" else moe.MOE_W_ROWMAJOR,
+                           fused_combine=fused_combine)
     T, K = cfg.T, cfg.K
     bufs = dict(
         ws=torch.empty(moe.moe_workspace_bytes(shape, T), dtype=torch.uint8, device=dev),
@@ -751,13 +756,14 @@ def free_gpu(ctx):
     torch.cuda.empty_cache()
 
 
-def prefill_record(K: int, warmup: int, w_layout: str = "frag"):
+def prefill_record(K: int, warmup: int, w_layout: str = "frag", fused_combine: bool = False):
     """The prefill workload timed like the main one; tokens/s, the MFMA
     fraction of its gate/up launch and of the whole layer."""
     import torch
 
     import expert_router_gemm_amd as moe
-    ctx = setup(PREFILL_WORKLOAD, keep_host=False, w_layout=w_layout)
+    ctx = setup(PREFILL_WORKLOAD, keep_host=False, w_layout=w_layout,
+                fused_combine=fused_combine)
     cfg = ctx["cfg"]
     t = time_workload(ctx, K, warmup, references=False)
     prof_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
@@ -768,6 +774,7 @@ def prefill_record(K: int, warmup: int, w_layout: str = "frag"):
     work = algorithmic_work(cfg, _counts_of(ctx))
     rec = {"workload": cfg.name, "tokens": cfg.T, "local_slots": ctx["S"],
            "weight_layout": LAYOUT_NAME[w_layout],
+           "combine": COMBINE_NAME[fused_combine],
            "value": round(cfg.T / (t["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
            "steps": K, "warmup": warmup, "ms_per_step": round(t["ms_per_step"], 4),
            "roofline": kernel_roofline(cfg, work, t["up_ms"], "tiled"),
@@ -831,6 +838,9 @@ def main():
                     help="only time torch's fp16 GEMMs on the prefill expert shapes")
     ap.add_argument("--w-layout", choices=["frag", "rowmajor"], default="frag",
                     help="expert weight layout: the fragment layout (default) or row-major")
+    ap.add_argument("--fused-combine", action="store_true",
+                    help="set MOE_F_FUSED_COMBINE: the combine in the tiled down projection's "
+                         "tail (prefill batches) instead of its own launch")
     ap.add_argument("--groups", metavar="G,M", default=None,
                     help="group-limited routing: keep M of G contiguous expert groups")
     args = ap.parse_args()
@@ -864,7 +874,8 @@ def main():
     import expert_router_gemm_amd as moe
     moe.lib()
     want_cpu = not args.no_cpu_baseline
-    ctx = setup(args.workload, keep_host=want_cpu, groups=groups, w_layout=args.w_layout)
+    ctx = setup(args.workload, keep_host=want_cpu, groups=groups, w_layout=args.w_layout,
+                fused_combine=args.fused_combine)
     cfg = ctx["cfg"]
     kind = dominant_kind(args.workload)
 
@@ -911,7 +922,8 @@ def main():
                    "ep_size": cfg.ep_size, "ep_rank": cfg.ep_rank,
                    "long_tail": cfg.long_tail,
                    "group_limit": list(groups) if groups else None,
-                   "weight_layout": LAYOUT_NAME[args.w_layout]},
+                   "weight_layout": LAYOUT_NAME[args.w_layout],
+                   "combine": COMBINE_NAME[args.fused_combine]},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer": layer,
@@ -920,7 +932,8 @@ def main():
         rec["eplb"] = eplb
     free_gpu(ctx)
     if not args.no_prefill and args.workload != PREFILL_WORKLOAD:
-        rec["prefill"] = prefill_record(args.steps, args.warmup, args.w_layout)
+        rec["prefill"] = prefill_record(args.steps, args.warmup, args.w_layout,
+                                        args.fused_combine)
         log(f"[bench] prefill {rec['prefill']['workload']}: {rec['prefill']['value']:.0f} "
             f"tokens/s, gate/up {rec['prefill']['roofline']['achieved']} TFLOP/s")
     print(json.dumps(rec))

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_F16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_F_SHARED = 1
+MOE_F_FUSED_COMBINE = 2
 MOE_X_PERMUTED, MOE_X_SHARED, MOE_X_GATHER = 0, 1, 2
 MOE_W_ROWMAJOR, MOE_W_FRAG = 0, 1
 
@@ -160,10 +161,10 @@ def _check(fn: str, st: int):
 
 def make_shape(*, hidden, inter, n_experts, top_k, n_slots, n_shared=0, act=MOE_F16,
                dispatch=None, shared=False, n_groups=0, topk_groups=0,
-               w_layout=MOE_W_ROWMAJOR) -> Shape:
+               w_layout=MOE_W_ROWMAJOR, fused_combine=False) -> Shape:
+    flags = (MOE_F_SHARED if shared else 0) | (MOE_F_FUSED_COMBINE if fused_combine else 0)
     return Shape(hidden, inter, n_experts, top_k, n_slots, n_shared, act,
-                 act if dispatch is None else dispatch, MOE_F_SHARED if shared else 0,
-                 n_groups, topk_groups, w_layout)
+                 act if dispatch is None else dispatch, flags, n_groups, topk_groups, w_layout)
 
 
 def moe_workspace_bytes(shape: Shape, T: int) -> int:

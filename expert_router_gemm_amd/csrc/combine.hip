@@ -3,7 +3,9 @@
 //   out[t] = sum_k topk_w[t][k] * y[inv_pos[t][k]]  +  gate[t] * sum_j shared_y[j][t]
 // On one GPU the return trip is a gather: y rows are read through inv_pos.
 // Accumulation is fp32 in fixed k order (deterministic), rounded once to the
-// output dtype.  Pairs computed on other GPUs (inv_pos = -1) are skipped, so a
+// output dtype: acc = fma(w_k, y_k, acc) from 0 over the local pairs, then
+// acc = fma(gate, sum of shared rows, acc).  The down projection's fused
+// combine (gemm_tiled.hip) uses the same sequence, so both give the same bits.  Pairs computed on other GPUs (inv_pos = -1) are skipped, so a
 // token with no local pair and no shared term gets exact zeros.
 //
 // One block per token with one thread per 8 consecutive features (up to
@@ -40,10 +42,13 @@ template <typename T>
 __device__ __forceinline__ void store8(T *p, const float v[8]);
 template <>
 __device__ __forceinline__ void store8<f16>(f16 *p, const float v[8]) {
-    f16x8 x;
+    // 8 fp32 sums -> fp16 as one vector: v_cvt_pk_f16_f32 (round to
+    // nearest even), the rounding the fused tail in gemm_tiled.hip writes
+    // out explicitly (plain asm here costs the kernel ~2 us of branches)
+    f32x8 w;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = to_f16(v[j]);
-    *reinterpret_cast<f16x8 *>(p) = x;
+    for (int j = 0; j < 8; ++j) w[j] = v[j];
+    *reinterpret_cast<f16x8 *>(p) = __builtin_convertvector(w, f16x8);
 }
 template <>
 __device__ __forceinline__ void store8<float>(float *p, const float v[8]) {
@@ -110,7 +115,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
 #pragma unroll
                     for (int c = 0; c < CH; ++c)
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[c][j] += g * v[q][c][j];
+                        for (int j = 0; j < 8; ++j)
+                            acc[c][j] = __builtin_fmaf(g, v[q][c][j], acc[c][j]);
                 }
             }
         }
@@ -127,7 +133,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineArgs a) {
                     for (int j = 0; j < 8; ++j) sv[j] += u[j];
                 }
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[c][j] += gs * sv[j];
+                for (int j = 0; j < 8; ++j) acc[c][j] = __builtin_fmaf(gs, sv[j], acc[c][j]);
             }
             store8<T>(out + i, acc[c]);
         }

@@ -98,5 +98,19 @@ __device__ __forceinline__ float siluf_(float z) { return z / (1.0f + expf(-z));
 
 // Round-to-nearest-even conversions for outputs.
 __device__ __forceinline__ f16 to_f16(float v) { return (f16)v; }
+// The same for 8 fp32 values, two per v_cvt_pk_f16_f32 (round to nearest
+// even).  Written as the instruction itself so the compiler cannot fold the
+// conversion into the fma that produced a value (v_fma_mixlo_f16 rounds
+// the exact result once, to fp16), which it does in some contexts and not
+// in others: the combine's two code paths must round alike (the separate
+// combine kernel's 8-wide vector conversion compiles to this instruction).
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8 to_f16x8_of_f32(f32x8 v) {
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r[j]) : "v"(v[2 * j]), "v"(v[2 * j + 1]));
+    return __builtin_bit_cast(f16x8, r);
+}
 
 }  // namespace moe

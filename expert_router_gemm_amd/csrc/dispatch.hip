@@ -66,6 +66,15 @@ __device__ __forceinline__ void drop_repeated_slots(int (&sl)[KMAX], int K = KMA
     }
 }
 
+// Tickets of the down projection's fused combine: each of the token's
+// feature tiles starts at its number of local pairs (slots after
+// drop_repeated_slots, i.e. the rows it really gets).
+__device__ __forceinline__ void seed_tickets(const DispatchArgs &a, int t, int np) {
+    if (!a.tickets || t >= a.T) return;
+    int32_t *tk = a.tickets + (size_t)t * a.n_tiles;
+    for (int f = 0; f < a.n_tiles; ++f) tk[f] = np;
+}
+
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchArgs a) {
     extern __shared__ unsigned long long masks[];  // [4][S]
     const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -81,6 +90,12 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchArgs a) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) sk[k] = (t < a.T && k < a.K) ? slot_of(a, t, k) : -1;
     drop_repeated_slots<16>(sk);
+    {
+        int np = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) np += sk[k] >= 0;
+        seed_tickets(a, t, np);
+    }
 #pragma unroll
     for (int k = 0; k < 16; ++k)
         if (sk[k] >= 0) atomicOr(&m[sk[k]], bit);
@@ -291,6 +306,10 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
             sls[k] = sl;
         }
         drop_repeated_slots<KMAX>(sls, K);
+        int np = 0;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) np += k < K && sls[k] >= 0;
+        seed_tickets(a, t, np);
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
             if (k < K && sls[k] >= 0) atomicOr(&masks[wave][sls[k]], bit);

@@ -453,6 +453,241 @@ __device__ __forceinline__ void run_items_dma(const StreamArgs &a, f16 *As, f16 
     wait_vm<0>();
 }
 
+// ---- The combine in the down projection (comb.out set) ----
+// Steps 4-5 of the EP blog page (section 2.2) in this launch's tail: the page
+// lets the combine run alongside the last expert computations (section 2.3),
+// and the large-EP article (三.2) fuses the gather and the scatter around the
+// grouped GEMM.  Result, per token t and feature i:
+//   out[t][i] = sum over t's local pairs k (k order) of topk_w[t][k] * y[inv_pos[t][k]][i]
+//               + shared_gate[t] * sum_j shared_y[j][t][i]
+// with the combine kernel's arithmetic (fp32 fma from 0 in that order, one
+// rounding), so the bits equal the separate combine's.
+//
+// Dispatch set one ticket per (token, 256-feature tile) to the token's local
+// pair count.  A workgroup that has finished its items makes its y rows
+// visible at agent scope (release fence), takes the ticket of every (row,
+// feature tile) it wrote (atomic decrement), and sums the (token, tile)s
+// whose ticket it took to zero -- it wrote the last of their rows -- after
+// an acquire fence, reading the other pairs' rows from memory.  No workgroup
+// waits for another, so nothing depends on workgroups being co-resident.
+// Tokens with no local pair (their experts live on other ranks) get zeros,
+// or the shared term alone, from workgroup t mod grid.
+constexpr int kCombSub = kThreads;  // entries summed per pass (one pair list per thread)
+constexpr int kCombCap = 4096;      // list room: under kCombSub pending + one batch's 4 x kThreads
+constexpr int kCombMaxK = 16;       // top-K limit of the shape check
+static_assert(kCombCap >= kCombSub - 1 + 4 * kThreads, "list room");
+constexpr size_t kCombLds =
+    (size_t)kCombCap * 4 + (size_t)kCombSub * kCombMaxK * 8 + (size_t)kCombSub * 3 * 4;
+
+__device__ __forceinline__ f16x8 ldg16(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
+
+template <int TBM>
+__device__ void comb_tail(const StreamArgs &a, const ItemSeq &seq, const int *tstart, int n_groups,
+                          int n_ntiles, f16 *lds) {
+    const CombineArgs &c = a.comb;
+    const int tid = threadIdx.x;
+    const int K = c.K, H = a.N, T = c.T, nft = n_ntiles;
+    const bool sh = c.shared_y && c.n_shared > 0;
+    const f16 *y = reinterpret_cast<const f16 *>(a.out);
+    const f16 *shy = reinterpret_cast<const f16 *>(c.shared_y);
+    f16 *out = reinterpret_cast<f16 *>(c.out);
+    int *list = reinterpret_cast<int *>(lds);          // [kCombCap] ticket indices t*nft + f
+    int *prow = list + kCombCap;                       // [kCombSub][kCombMaxK] local rows, k order
+    float *pw = reinterpret_cast<float *>(prow + kCombSub * kCombMaxK);  // their weights
+    int *pn = reinterpret_cast<int *>(pw + kCombSub * kCombMaxK);       // local pair count
+    int *pe = pn + kCombSub;                                            // ticket index
+    float *pgs = reinterpret_cast<float *>(pe + kCombSub);              // shared gate
+    __shared__ int nlist;
+
+    // 8 features from i of token t: the pairs' rows (np of them, from LDS
+    // row-lists at rl / wl), then the shared term; stored to out.
+    // (4 units per thread, their loads in flight together)
+    auto sum_units = [&](int units, auto unit_of) {
+        for (int u0 = tid; u0 < units; u0 += 4 * kThreads) {
+            int t[4], i[4], np[4], base[4];
+            float gs[4];
+            int maxnp = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                np[q] = -1;
+                const int u = u0 + q * kThreads;
+                if (u < units) unit_of(u, t[q], i[q], np[q], base[q], gs[q]);
+                maxnp = np[q] > maxnp ? np[q] : maxnp;
+            }
+            float acc[4][8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[q][j] = 0.f;
+            for (int k0 = 0; k0 < maxnp; k0 += 4) {
+                f16x8 v[4][4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        if (k0 + kk < np[q])
+                            v[q][kk] = ldg16(y + (size_t)prow[base[q] + k0 + kk] * H + i[q]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        if (k0 + kk < np[q]) {
+                            const float g = pw[base[q] + k0 + kk];
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)
+                                acc[q][j] = __builtin_fmaf(g, (float)v[q][kk][j], acc[q][j]);
+                        }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (np[q] < 0) continue;
+                if (sh) {
+                    float sv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                    for (int s = 0; s < c.n_shared; ++s) {
+                        const f16x8 w = ldg16(shy + ((size_t)s * T + t[q]) * H + i[q]);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) sv[j] += (float)w[j];
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[q][j] = __builtin_fmaf(gs[q], sv[j], acc[q][j]);
+                }
+                f32x8 a8;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a8[j] = acc[q][j];
+                *reinterpret_cast<f16x8 *>(out + (size_t)t[q] * H + i[q]) = to_f16x8_of_f32(a8);
+            }
+        }
+    };
+
+    // sum the n (token, tile) entries of the list
+    auto flush = [&](int n) {
+        // see the rows the other producers released before their decrements
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        for (int b = 0; b < n; b += kCombSub) {
+            const int m = n - b < kCombSub ? n - b : kCombSub;
+            if (tid < m) {
+                const int e = list[b + tid];
+                const int t = e / nft;
+                // all K loads in flight together, then compacted in k order
+                int r[kCombMaxK];
+                float w[kCombMaxK];
+#pragma unroll
+                for (int k = 0; k < kCombMaxK; ++k) {
+                    r[k] = k < K ? c.inv_pos[(size_t)t * K + k] : -1;
+                    w[k] = k < K ? c.topk_w[(size_t)t * K + k] : 0.f;
+                }
+                int np = 0;
+#pragma unroll
+                for (int k = 0; k < kCombMaxK; ++k)
+                    if (r[k] >= 0) {
+                        prow[tid * kCombMaxK + np] = r[k];
+                        pw[tid * kCombMaxK + np] = w[k];
+                        ++np;
+                    }
+                pn[tid] = np;
+                pe[tid] = e;
+                pgs[tid] = sh ? c.shared_gate[t] : 0.f;
+            }
+            __syncthreads();
+            // units: (entry, 8-feature chunk), 32 chunks per 256-feature tile
+            sum_units(m * (WR / 8), [&](int u, int &t, int &i, int &np, int &base, float &gs) {
+                const int ent = u / (WR / 8);
+                const int e = pe[ent];
+                t = e / nft;
+                i = (e - t * nft) * WR + (u % (WR / 8)) * 8;
+                if (i >= H) return;  // past the last, narrower tile
+                np = pn[ent];
+                base = ent * kCombMaxK;
+                gs = pgs[ent];
+            });
+            __syncthreads();
+        }
+    };
+
+    // every wave's y stores have completed (run_items_dma waited for them)
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (tid == 0) nlist = 0;
+    __syncthreads();
+    const int nitems = seq.first < seq.end ? (seq.end - seq.first + seq.step - 1) / seq.step : 0;
+    // items in batches of 8: thread tid takes row tid % 256 of items 2q + tid / 256
+    for (int b0 = 0; b0 < nitems; b0 += 8) {
+        int row[4], ft[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            row[q] = -1;
+            ft[q] = 0;
+            const int j = b0 + 2 * q + (tid >> 8);
+            if (j < nitems) {
+                int g, mt, nt, kz;
+                decode_item(tstart, n_groups, n_ntiles, 1, seq.chunked, seq.first + j * seq.step, g,
+                            mt, nt, kz);
+                const int r0 = a.offsets ? a.offsets[g] : g * a.rows_per_group;
+                const int r1 = a.offsets ? a.offsets[g + 1] : r0 + a.rows_per_group;
+                const int r = r0 + mt * TBM + (tid & 255);
+                if (TBM == 256 && r < r1) {
+                    row[q] = r;
+                    ft[q] = nt;
+                }
+            }
+        }
+        int pair[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pair[q] = row[q] >= 0 ? c.perm_src[row[q]] : -1;
+        int tk[4], left[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            left[q] = -1;
+            tk[q] = pair[q] >= 0 ? (pair[q] / K) * nft + ft[q] : -1;
+            if (tk[q] >= 0)
+                left[q] = __hip_atomic_fetch_add(c.tickets + tk[q], -1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (tk[q] >= 0 && left[q] == 1) list[atomicAdd(&nlist, 1)] = tk[q];
+        __syncthreads();
+        const int n = nlist;
+        if (n >= kCombSub) {  // a full pass is pending: sum it now
+            flush(n);
+            if (tid == 0) nlist = 0;
+            __syncthreads();
+        }
+    }
+    __syncthreads();
+    if (nlist > 0) flush(nlist);
+
+    // tokens without a local pair: zeros, or the shared term alone
+    const int G = gridDim.x;
+    for (int t0 = blockIdx.x; t0 < T; t0 += G * kThreads) {
+        __syncthreads();
+        if (tid == 0) nlist = 0;
+        __syncthreads();
+        const int t = t0 + tid * G;
+        if (t < T) {
+            bool any = false;
+#pragma unroll
+            for (int k = 0; k < kCombMaxK; ++k)
+                if (k < K) any |= c.inv_pos[(size_t)t * K + k] >= 0;
+            if (!any) {
+                const int at = atomicAdd(&nlist, 1);
+                list[at] = t;
+                pgs[at] = sh ? c.shared_gate[t] : 0.f;
+            }
+        }
+        __syncthreads();
+        const int nz = nlist;
+        sum_units(nz * (H / 8), [&](int u, int &t, int &i, int &np, int &base, float &gs) {
+            const int ent = u / (H / 8);
+            t = list[ent];
+            i = (u % (H / 8)) * 8;
+            np = 0;
+            base = 0;
+            gs = pgs[ent];
+        });
+    }
+}
+
 constexpr int kMaxGroups = 1024;
 
 // Persistent: a fixed grid walks the real tiles.  Each workgroup first builds
@@ -471,7 +706,7 @@ constexpr size_t tile_lds_bytes() {
     return (size_t)n_stages<TBM>() * (TBM + WR) * BK * sizeof(f16);
 }
 
-template <int TBM, int NM, int EPI, bool GATHER, bool FR>
+template <int TBM, int NM, int EPI, bool GATHER, bool FR, bool CB>
 __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int n_ntiles,
                                                               int n_groups) {
     extern __shared__ __attribute__((aligned(16))) f16 lds[];
@@ -521,11 +756,16 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
         seq.chunked = false;
     }
     run_items_dma<TBM, NM, EPI, GATHER, FR>(a, As, Bs, tstart, n_groups, n_ntiles, ks, seq);
+    if constexpr (CB) {
+        static_assert(TBM == kExpertRows && NM == 1 && EPI == 0 && !GATHER, "down projection only");
+        static_assert(kCombLds <= tile_lds_bytes<TBM>(), "the combine reuses the stage buffers");
+        comb_tail<TBM>(a, seq, tstart, n_groups, n_ntiles, lds);
+    }
 }
 
 // max_tiles bounds the 128-row tiles (so also the taller ones): it only
 // sizes the grid, surplus workgroups find no item and exit.
-template <int TBM, int NM, int EPI, bool GATHER, bool FR>
+template <int TBM, int NM, int EPI, bool GATHER, bool FR, bool CB = false>
 hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream_t s) {
     if (n_groups <= 0 || n_groups > kMaxGroups) return hipErrorInvalidValue;
     const int n_ntiles = (a.N + WR / NM - 1) / (WR / NM);
@@ -539,13 +779,13 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
     int slots = dev < kMaxDevices ? resident[dev].load(std::memory_order_acquire) : 0;
     if (slots <= 0) {
-        hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR>,
+        hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR, CB>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         int cus = 256, per_cu = 1;
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR>, kThreads, lds) != hipSuccess ||
+                &per_cu, tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR, CB>, kThreads, lds) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
         slots = cus * per_cu;
@@ -555,7 +795,7 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream
     long grid = slots;
     const long items = max_tiles * n_ntiles * (EPI == 2 ? a.ksplit : 1);
     if (items < grid) grid = items > 0 ? items : 1;
-    hipLaunchKernelGGL((tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR>), dim3((unsigned)grid), dim3(kThreads),
+    hipLaunchKernelGGL((tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR, CB>), dim3((unsigned)grid), dim3(kThreads),
                        lds, s, a, n_ntiles, n_groups);
     return hipGetLastError();
 }
@@ -582,9 +822,19 @@ hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long m
         return a.gather ? launch_t<XB, 2, 1, true, false>(a, n_groups, max_tiles, s)
                         : launch_t<XB, 2, 1, false, false>(a, n_groups, max_tiles, s);
     }
-    if (mode == STREAM_STORE)
+    if (mode == STREAM_STORE) {
+        if (a.comb.out) {
+            // the combine rides in the tail (fp16 rows, top-K within the
+            // row lists' room)
+            if (a.comb.K < 1 || a.comb.K > kCombMaxK || a.comb.T < 1 || !a.comb.tickets ||
+                !a.comb.perm_src || !a.offsets)
+                return hipErrorInvalidValue;
+            return a.w_frag ? launch_t<XB, 1, 0, false, true, true>(a, n_groups, max_tiles, s)
+                            : launch_t<XB, 1, 0, false, false, true>(a, n_groups, max_tiles, s);
+        }
         return a.w_frag ? launch_t<XB, 1, 0, false, true>(a, n_groups, max_tiles, s)
                         : launch_t<XB, 1, 0, false, false>(a, n_groups, max_tiles, s);
+    }
     // router weights are row-major
     return launch_t<kTiledRouterRows, 1, 2, false, false>(a, n_groups, max_tiles, s);
 }

@@ -7,6 +7,24 @@
 
 namespace moe {
 
+// ---------------------------------------------------------------- combine
+// out[t] = sum over local k (k order) of topk_w[t][k] * y[inv_pos[t][k]]
+//          + shared_gate[t] * sum_j shared_y[j][t]       (fp32 fma from 0)
+struct CombineArgs {
+    int T, K, H, n_shared, dtype;
+    const void *y;
+    const int32_t *inv_pos;
+    const float *topk_w;
+    const void *shared_y;   // [n_shared][T][H] or NULL
+    const float *shared_gate;
+    void *out;
+    // Down projection with the combine fused (tiled kernel only): row ->
+    // pair t*K + k, and one ticket per (token, 256-feature tile) holding the
+    // token's local pair count (set by dispatch; taken to 0 by the GEMM).
+    const int32_t *perm_src;
+    int32_t *tickets;
+};
+
 // ---------------------------------------------------------------- GEMMs
 enum : int { STREAM_STORE = 0, STREAM_SWIGLU = 1, STREAM_LOGITS = 2 };
 
@@ -38,6 +56,10 @@ struct StreamArgs {
     int x2_broadcast;
     const void *w0b, *w1b;
     int rows2, row2_base;
+    // Down projection only (tiled kernel): with comb.out set, the launch
+    // also forms the layer output from the rows it writes (see
+    // gemm_tiled.hip); comb.y is not used (the rows are this launch's out).
+    CombineArgs comb;
 };
 
 // Fragment layout of a [N][K] weight matrix (N a multiple of 16, K * esize
@@ -93,6 +115,10 @@ struct DispatchArgs {
     // scratch
     int32_t *pair_code;     // [T*K]
     int32_t *chunk_counts;  // [C][S], C = ceil(T/64)
+    // optional: tickets[t][f] = local pairs of token t, f < n_tiles (the
+    // down projection's fused combine)
+    int32_t *tickets;
+    int n_tiles;
 };
 size_t dispatch_scratch_bytes(int T, int K, int S);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
@@ -103,15 +129,7 @@ hipError_t launch_expert_counts(const int32_t *topk_idx, long pairs, int E, int3
                                 hipStream_t s);
 
 // ---------------------------------------------------------------- combine
-struct CombineArgs {
-    int T, K, H, n_shared, dtype;
-    const void *y;
-    const int32_t *inv_pos;
-    const float *topk_w;
-    const void *shared_y;   // [n_shared][T][H] or NULL
-    const float *shared_gate;
-    void *out;
-};
+// The separate combine (CombineArgs above; perm_src and tickets unused).
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------- layout

@@ -82,7 +82,7 @@ size_t route_ws_bytes(const moe_shape &s, int T) {
 
 moe_status check_shape(const moe_shape *s) {
     if (!s) return MOE_ERR_INVALID_ARG;
-    if (s->flags & ~MOE_F_SHARED) return MOE_ERR_INVALID_ARG;
+    if (s->flags & ~(MOE_F_SHARED | MOE_F_FUSED_COMBINE)) return MOE_ERR_INVALID_ARG;
     if (s->w_layout != MOE_W_ROWMAJOR && s->w_layout != MOE_W_FRAG) return MOE_ERR_INVALID_ARG;
     if (s->hidden <= 0 || s->inter <= 0 || s->hidden % 128 || s->inter % 128) return MOE_ERR_SHAPE;
     if (s->hidden > kMaxDim || s->inter > kMaxDim) return MOE_ERR_SHAPE;
@@ -136,8 +136,12 @@ moe_status device_ok() {
 // Workspace carving for moe_layer_forward (every piece 256-byte aligned).
 struct Layout {
     size_t logits, topk_idx, topk_w, shared_gate, counts, offsets, perm_src, inv_pos;
-    size_t x_perm, x_scale, hm, y, shared_y, disp, total;
+    size_t x_perm, x_scale, hm, y, shared_y, disp, tickets, total;
 };
+
+// Feature tiles of the tiled down projection: one combine ticket each.
+constexpr int kCombTile = 256;
+inline int comb_tiles(const moe_shape &s) { return (s.hidden + kCombTile - 1) / kCombTile; }
 
 Layout layout(const moe_shape &s, int T) {
     Layout L;
@@ -166,6 +170,7 @@ Layout layout(const moe_shape &s, int T) {
     L.y = take((TK + nsh * T) * s.hidden * isz);
     L.shared_y = 0;  // inside y, after the routed rows
     L.disp = take(dispatch_scratch_bytes(T, s.top_k, s.n_slots));
+    L.tickets = take((size_t)T * comb_tiles(s) * 4);  // fused combine (tiled down projection)
     L.total = o;
     return L;
 }
@@ -187,6 +192,7 @@ hipError_t gemm(const StreamArgs &a, int dtype, int x_dtype, int mode, int n_gro
                 long est_rows, long cap_rows, hipStream_t st) {
     if (a.n_sec == 0 && est_rows >= kTiledMinRows && tiled_gemm_supported(a, dtype, x_dtype))
         return launch_tiled_gemm(a, mode, n_groups, cap_rows / 128 + n_groups, st);
+    if (a.comb.out) return hipErrorInvalidValue;  // the fused combine is the tiled kernel's
     return launch_stream_gemm(a, dtype, x_dtype, mode, n_groups, zblocks, est_rows, st);
 }
 
@@ -238,7 +244,7 @@ hipError_t route_impl(const moe_shape &s, int T, const void *h, const void *w_ro
 hipError_t dispatch_impl(const moe_shape &s, int T, const void *h, const int32_t *topk_idx,
                          const moe_slot_map &m, void *x_perm, float *x_scale, int32_t *counts,
                          int32_t *offsets, int32_t *perm_src, int32_t *inv_pos, void *scratch,
-                         hipStream_t st) {
+                         hipStream_t st, int32_t *tickets = nullptr) {
     DispatchArgs d{};
     d.T = T;
     d.K = s.top_k;
@@ -261,6 +267,8 @@ hipError_t dispatch_impl(const moe_shape &s, int T, const void *h, const int32_t
     d.pair_code = reinterpret_cast<int32_t *>(scratch);
     d.chunk_counts = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(scratch) +
                                                  up256((size_t)T * s.top_k * 4));
+    d.tickets = tickets;
+    d.n_tiles = comb_tiles(s);
     return launch_dispatch(d, st);
 }
 
@@ -312,9 +320,10 @@ hipError_t ffn_up_impl(const moe_shape &s, int n_groups, int zblocks, long est_r
 hipError_t ffn_down_impl(const moe_shape &s, int n_groups, int zblocks, long est_rows,
                          long cap_rows, const void *hm, const int32_t *offsets,
                          int rows_per_group, const void *w_down, void *y, hipStream_t st,
-                         const Secondary &sec = Secondary()) {
+                         const Secondary &sec = Secondary(), const CombineArgs *comb = nullptr) {
     StreamArgs a{};
     set_secondary(a, sec);
+    if (comb) a.comb = *comb;
     a.x = hm;
     a.offsets = offsets;
     a.rows_per_group = rows_per_group;
@@ -329,9 +338,9 @@ hipError_t ffn_down_impl(const moe_shape &s, int n_groups, int zblocks, long est
     return gemm(a, s.act, s.act, STREAM_STORE, n_groups, zblocks, est_rows, cap_rows, st);
 }
 
-hipError_t combine_impl(const moe_shape &s, int T, const void *y, const int32_t *inv_pos,
-                        const float *topk_w, const void *shared_y, const float *shared_gate,
-                        void *out, hipStream_t st) {
+CombineArgs combine_args(const moe_shape &s, int T, const void *y, const int32_t *inv_pos,
+                         const float *topk_w, const void *shared_y, const float *shared_gate,
+                         void *out) {
     CombineArgs c{};
     c.T = T;
     c.K = s.top_k;
@@ -344,7 +353,13 @@ hipError_t combine_impl(const moe_shape &s, int T, const void *y, const int32_t 
     c.shared_y = shared_y;
     c.shared_gate = shared_gate;
     c.out = out;
-    return launch_combine(c, st);
+    return c;
+}
+
+hipError_t combine_impl(const moe_shape &s, int T, const void *y, const int32_t *inv_pos,
+                        const float *topk_w, const void *shared_y, const float *shared_gate,
+                        void *out, hipStream_t st) {
+    return launch_combine(combine_args(s, T, y, inv_pos, topk_w, shared_y, shared_gate, out), st);
 }
 
 // Rows a group is expected to hold, used only to pick the kernel: cap_rows
@@ -633,12 +648,17 @@ moe_status layer_forward_run(const moe_shape *shape, const moe_weights *w,
     // hidden rows through perm_src and dispatch writes indices only
     const bool copy_rows = s.dispatch == MOE_FP8_E4M3;
     int32_t *perm_src = at<int32_t *>(ws, L.perm_src);
-    LAUNCH(dispatch_impl(s, T, h, topk_idx, *map, copy_rows ? at<void *>(ws, L.x_perm) : nullptr,
-                         x_scale, at<int32_t *>(ws, L.counts), offsets, perm_src, inv_pos,
-                         at<void *>(ws, L.disp), st));
-    MARK(2);
     const int z = ffn_zblocks(cap, s.n_slots);
     const long est = est_group_rows(s, cap);
+    // MOE_F_FUSED_COMBINE, where the routed down projection runs on the
+    // LDS-tiled kernel: the combine rides in its tail (tickets seeded by
+    // dispatch).  Otherwise the separate combine launch.
+    const bool fuse = (s.flags & MOE_F_FUSED_COMBINE) && use_tiled(est, s.inter, s.act, s.act);
+    int32_t *tickets = fuse ? at<int32_t *>(ws, L.tickets) : nullptr;
+    LAUNCH(dispatch_impl(s, T, h, topk_idx, *map, copy_rows ? at<void *>(ws, L.x_perm) : nullptr,
+                         x_scale, at<int32_t *>(ws, L.counts), offsets, perm_src, inv_pos,
+                         at<void *>(ws, L.disp), st, tickets));
+    MARK(2);
     void *hm = at<void *>(ws, L.hm), *y = at<void *>(ws, L.y);
     const size_t isz = act_bytes(s);
     void *shared_y = gate ? (void *)((char *)y + (size_t)cap * s.hidden * isz) : nullptr;
@@ -648,7 +668,7 @@ moe_status layer_forward_run(const moe_shape *shape, const moe_weights *w,
     const long est_sh = est_group_rows(s, cap_sh);
     // The shared experts (every token, Step 5) ride in the routed launches as
     // secondary groups when both stream their weights; rows cap.. of hm/y.
-    const bool merged = gate && !copy_rows && !use_tiled(est, s.hidden, s.act, s.act) &&
+    const bool merged = gate && !copy_rows && !fuse && !use_tiled(est, s.hidden, s.act, s.act) &&
                         !use_tiled(est_sh, s.hidden, s.act, s.act);
     if (merged) {
         Secondary up_sec, down_sec;
@@ -670,18 +690,32 @@ moe_status layer_forward_run(const moe_shape *shape, const moe_weights *w,
         LAUNCH(ffn_up_impl(s, s.n_slots, z, est, cap, x_routed, s.dispatch, x_scale, x_mode,
                            perm_src, offsets, 0, w->w_gate, w->w_up, hm, st));
         MARK(3);
-        LAUNCH(ffn_down_impl(s, s.n_slots, z, est, cap, hm, offsets, 0, w->w_down, y, st));
-        if (gate) {
+        auto shared_ffn = [&]() -> hipError_t {
             const int zs = (T + 63) / 64 < 65535 ? (T + 63) / 64 : 65535;
             void *hm_sh = (char *)hm + (size_t)cap * s.inter * isz;
-            LAUNCH(ffn_up_impl(s, s.n_shared, zs, est_sh, cap_sh, h, s.act, nullptr, MOE_X_SHARED,
-                               nullptr, nullptr, T, w->sh_gate, w->sh_up, hm_sh, st));
-            LAUNCH(ffn_down_impl(s, s.n_shared, zs, est_sh, cap_sh, hm_sh, nullptr, T,
-                                 w->sh_down, shared_y, st));
+            hipError_t e = ffn_up_impl(s, s.n_shared, zs, est_sh, cap_sh, h, s.act, nullptr,
+                                       MOE_X_SHARED, nullptr, nullptr, T, w->sh_gate, w->sh_up,
+                                       hm_sh, st);
+            if (e != hipSuccess) return e;
+            return ffn_down_impl(s, s.n_shared, zs, est_sh, cap_sh, hm_sh, nullptr, T, w->sh_down,
+                                 shared_y, st);
+        };
+        if (fuse) {
+            // the shared rows first: the routed launch's tail reads them
+            if (gate) LAUNCH(shared_ffn());
+            CombineArgs c = combine_args(s, T, y, inv_pos, topk_w, shared_y, sgate, out);
+            c.perm_src = perm_src;
+            c.tickets = tickets;
+            LAUNCH(ffn_down_impl(s, s.n_slots, z, est, cap, hm, offsets, 0, w->w_down, y, st,
+                                 Secondary(), &c));
+        } else {
+            LAUNCH(ffn_down_impl(s, s.n_slots, z, est, cap, hm, offsets, 0, w->w_down, y, st));
+            if (gate) LAUNCH(shared_ffn());
         }
     }
     MARK(4);
-    LAUNCH(combine_impl(s, T, at<void *>(ws, L.y), inv_pos, topk_w, shared_y, sgate, out, st));
+    if (!fuse)
+        LAUNCH(combine_impl(s, T, at<void *>(ws, L.y), inv_pos, topk_w, shared_y, sgate, out, st));
     MARK(5);
 #undef MARK
     return MOE_OK;

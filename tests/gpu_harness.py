@@ -148,11 +148,16 @@ def ws_for(L: Layer, T=None):
     return torch.empty(n, dtype=torch.uint8, device=DEV)
 
 
-def gpu_forward(L: Layer):
+def gpu_forward(L: Layer, fused_combine: bool = False):
+    """moe_layer_forward; fused_combine sets MOE_F_FUSED_COMBINE."""
     T, H = L.T, L.cfg.H
     out = torch.empty((T, H), dtype=L.d["h"].dtype, device=DEV)
     ws = ws_for(L)
-    moe.moe_layer_forward(L.shape, L.wmap, L.smap, T, L.d["h"], out, ws)
+    shape = L.shape
+    if fused_combine:
+        shape = type(L.shape).from_buffer_copy(L.shape)
+        shape.flags |= moe.MOE_F_FUSED_COMBINE
+    moe.moe_layer_forward(shape, L.wmap, L.smap, T, L.d["h"], out, ws)
     torch.cuda.synchronize()
     return out
 

@@ -92,6 +92,19 @@ def test_route_rejects_bad_shapes(kw, status):
     assert _route(_shape(**kw)) == status
 
 
+def test_shape_flags():
+    """MOE_F_SHARED and MOE_F_FUSED_COMBINE are the only flag bits."""
+    s = _shape()
+    s.flags = moe.MOE_F_FUSED_COMBINE
+    assert _route(s, T=0, ws=None) == 0
+    assert moe.moe_workspace_bytes(s, 16) == moe.moe_workspace_bytes(_shape(), 16)
+    assert moe.make_shape(hidden=256, inter=128, n_experts=8, top_k=2, n_slots=8,
+                          fused_combine=True).flags == moe.MOE_F_FUSED_COMBINE
+    for bad in (4, 1 << 31):
+        s.flags = bad
+        assert _route(s, T=0, ws=None) == 1  # MOE_ERR_INVALID_ARG
+
+
 def test_largest_hidden_and_inter_are_accepted():
     """65536 is the largest hidden / inter size (32-bit tile offsets)."""
     big = _shape(hidden=65536, inter=65536)

@@ -491,6 +491,9 @@ def test_tiled_feature_tiles_and_ragged_rows(T, H, I):
     _check_combine(L, st)
     ref = gh.oracle_forward(L)
     err = gh.assert_close(st["out"], ref["out"], "layer output", rows=~tie)
+    # the layer with the combine in the tiled down projection's tail
+    out = gh.gpu_forward(L, fused_combine=True).cpu().numpy()
+    assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8))
     print(f"[tiled] T={T} H={H} I={I} P={st['P']} max|d|={err:.3e}")
 
 
@@ -507,6 +510,9 @@ def test_tiled_shared_and_ragged_groups():
     _check_combine(L, st)
     ref = gh.oracle_forward(L)
     gh.assert_close(st["out"], ref["out"], "layer output", rows=~tie)
+    # combine in the routed down projection's tail (shared rows first)
+    out = gh.gpu_forward(L, fused_combine=True).cpu().numpy()
+    assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8))
 
 
 @pytest.mark.parametrize("H", [1536, 7168])
