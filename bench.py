@@ -510,14 +510,14 @@ def cpu_baseline(ctx, budget_s: float = 20.0):
 def is_dominant(kernel_name: str, kind: str) -> bool:
     """The gate/up launch of the dominant kernel, demangled or mangled.
     Stream GEMM: template arguments <TW, XM, NSUB, EPI, KW, U, FR> with EPI =
-    SwiGLU (1).  Tiled GEMM: <TBM, NM, EPI, GATHER, FR> = <256, 2, 1, true,
-    either weight layout>."""
+    SwiGLU (1).  Tiled GEMM: <TBM, NM, EPI, GATHER, FR, CB> = <256, 2, 1, true,
+    either weight layout, false>."""
     import re
     if DOMINANT[kind] not in kernel_name:
         return False
     if kind == "tiled":
         n = kernel_name.replace(" ", "")
-        return bool(re.search(r"tiled_gemm_kernel<256,2,1,true(,(true|false))?>", n)
+        return bool(re.search(r"tiled_gemm_kernel<256,2,1,true(,(true|false))*>", n)
                     or "tiled_gemm_kernelILi256ELi2ELi1ELb1E" in n)
     n = kernel_name.replace(" ", "")
     m = re.search(r"stream_gemm_kernel<[^,]+,(\d+),(\d+),(\d+),", n)
@@ -585,7 +585,11 @@ def kernel_label(name: str) -> str:
             r"tiled_gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELb([01])E", n)
         if m:
             epi = {"0": "down", "1": "gate/up", "2": "router"}[m.group(3)]
-            return f"tiled_gemm_kernel {epi} ({m.group(1)}-row tiles)"
+            # the sixth argument: the combine in the launch's tail
+            cb = re.search(r"tiled_gemm_kernel<[^>]*,(true|false),(true|false),true>", n) or \
+                re.search(r"tiled_gemm_kernelI(?:[^E]*E){3}Lb[01]ELb[01]ELb1E", n)
+            tail = " + combine in the tail" if cb else ""
+            return f"tiled_gemm_kernel {epi} ({m.group(1)}-row tiles){tail}"
     if "stream_gemm_kernel" in n:
         m = re.search(r"stream_gemm_kernel<[^,]+,(\d+),(\d+),(\d+),", n) or re.search(
             r"stream_gemm_kernelI(?:DF16_|f)Li(\d+)ELi(\d+)ELi(\d+)E", n)

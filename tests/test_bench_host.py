@@ -15,13 +15,13 @@ import moe_synth
 # kernel names as rocprofv3 prints them (PMC runs: mangled; kernel traces:
 # demangled); template arguments <weight, x, subtiles, epilogue, K waves,
 # chunks, fragment layout> and <tile rows, matrices, epilogue, gathered,
-# fragment layout>, epilogue 1 = SwiGLU
+# fragment layout, combine in the tail>, epilogue 1 = SwiGLU
 STREAM = ("_ZN3moe12_GLOBAL__N_118stream_gemm_kernelIDF16_Li1ELi4ELi{}ELi4ELi2ELb1EEEv"
           "NS_10StreamArgsE")
 STREAM_F32 = ("void moe::(anonymous namespace)::stream_gemm_kernel<float, 1, 4, {}, 4, 2, false>"
               "(moe::StreamArgs)")
 TILED = "void moe::(anonymous namespace)::tiled_gemm_kernel<{}>(moe::StreamArgs, int, int)"
-TILED_MANGLED = ("_ZN3moe12_GLOBAL__N_117tiled_gemm_kernelILi256ELi2ELi1ELb{}ELb1EEEv"
+TILED_MANGLED = ("_ZN3moe12_GLOBAL__N_117tiled_gemm_kernelILi256ELi2ELi1ELb{}ELb1ELb0EEEv"
                  "NS_10StreamArgsEii")
 COPY = ("void at::native::vectorized_elementwise_kernel<8, at::native::AUnaryFunctor<c10::Half, "
         "c10::Half, c10::Half, at::native::binary_internal::MulFunctor<float> >>(int)")
@@ -33,17 +33,32 @@ def test_dominant_kernel_is_the_swiglu_gate_up_launch():
     for epi in (0, 2):  # down projection, router logits
         assert not bench.is_dominant(STREAM.format(epi), "stream")
         assert not bench.is_dominant(STREAM_F32.format(epi), "stream")
-    assert bench.is_dominant(TILED.format("256, 2, 1, true, true"), "tiled")
-    assert bench.is_dominant(TILED.format("256, 2, 1, true, false"), "tiled")
+    assert bench.is_dominant(TILED.format("256, 2, 1, true, true, false"), "tiled")
+    assert bench.is_dominant(TILED.format("256, 2, 1, true, false, false"), "tiled")
     assert bench.is_dominant(TILED_MANGLED.format(1), "tiled")
-    for args in ("256, 1, 0, false, true", "128, 1, 2, false, false", "256, 2, 1, false, true"):
+    for args in ("256, 1, 0, false, true, false", "256, 1, 0, false, true, true",
+                 "128, 1, 2, false, false, false", "256, 2, 1, false, true, false"):
         assert not bench.is_dominant(TILED.format(args), "tiled")
     assert not bench.is_dominant(TILED_MANGLED.format(0), "tiled")
     # one kind never matches the other's kernels
     assert not bench.is_dominant(STREAM.format(1), "tiled")
-    assert not bench.is_dominant(TILED.format("256, 2, 1, true, true"), "stream")
+    assert not bench.is_dominant(TILED.format("256, 2, 1, true, true, false"), "stream")
     assert bench.dominant_kind(4) == "tiled"
     assert all(bench.dominant_kind(n) == "stream" for n in (1, 2, 3, 5))
+
+
+def test_kernel_labels():
+    assert bench.kernel_label(TILED.format("256, 2, 1, true, true, false")) == \
+        "tiled_gemm_kernel gate/up (256-row tiles)"
+    assert bench.kernel_label(TILED.format("256, 1, 0, false, true, false")) == \
+        "tiled_gemm_kernel down (256-row tiles)"
+    assert bench.kernel_label(TILED.format("256, 1, 0, false, true, true")) == \
+        "tiled_gemm_kernel down (256-row tiles) + combine in the tail"
+    assert bench.kernel_label("_ZN3moe12_GLOBAL__N_117tiled_gemm_kernelILi256ELi1ELi0ELb0ELb1ELb1EEEv"
+                              "NS_10StreamArgsEii").endswith("combine in the tail")
+    assert bench.kernel_label(TILED.format("128, 1, 2, false, false, false")) == \
+        "tiled_gemm_kernel router (128-row tiles)"
+    assert bench.kernel_label(STREAM.format(1)) == "stream_gemm_kernel gate/up"
 
 
 def test_traffic_record_is_used_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
