@@ -74,3 +74,62 @@ def test_fused_combine_equals_staged(name):
     err = gh.assert_close(out[tok], ref["out"], "layer output (sample)", rows=~tie)
     print(f"[fused combine] {name}: T={cfg.T} H={cfg.H} P={st['P']} "
           f"no-local tokens={int(none_local.sum())} max|d|={err:.3e}")
+
+
+@pytest.mark.parametrize("entry", ["noalloc", "workspace"])
+def test_fused_combine_under_graph_capture(entry):
+    """The fused path enqueues kernel launches only (dispatch seeds the
+    tickets; no memset): captured once with the flag, through the
+    no-allocation entry point and through moe_layer_forward, every replay
+    equals an eager call bit for bit, with other eager calls on the same
+    workspace between the replays."""
+    c = dict(CASES["full_shared"])
+    n = c.pop("n")
+    cfg = moe_synth.scaled_config(n, **c)
+    print(f"[case] fused combine under capture ({entry}): {cfg}", flush=True)
+    L = gh.build_layer(cfg, keep_host_weights=False)
+    shape = type(L.shape).from_buffer_copy(L.shape)
+    shape.flags |= moe.MOE_F_FUSED_COMBINE
+    T, H = L.T, cfg.H
+    ws = gh.ws_for(L)
+
+    def forward(h, out, stream=None):
+        if entry == "noalloc":
+            moe.moe_layer_forward_noalloc(shape, L.wmap, L.smap, T, h, out, stream)
+        else:
+            moe.moe_layer_forward(shape, L.wmap, L.smap, T, h, out, ws, stream)
+
+    h = L.d["h"]
+    h0 = h.clone()
+    h1 = torch.flip(h0, dims=[0]).contiguous()
+    ref = {}
+    for name, src in (("h0", h0), ("h1", h1)):
+        h.copy_(src)
+        e = torch.empty((T, H), dtype=h.dtype, device=gh.DEV)
+        forward(h, e)
+        torch.cuda.synchronize()
+        ref[name] = e.cpu().numpy().view(np.uint8)
+    out = torch.empty((T, H), dtype=h.dtype, device=gh.DEV)
+    h.copy_(h0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        forward(h, out, s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        forward(h, out)
+    torch.cuda.synchronize()
+    other = torch.empty_like(out)
+    for i, name in enumerate(["h0", "h1", "h1", "h0"]):
+        h.copy_(h1 if name == "h0" else h0)
+        forward(h, other)  # eager call on the other input: rewrites the workspace
+        torch.cuda.synchronize()
+        h.copy_(h0 if name == "h0" else h1)
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint8), ref[name]), f"replay {i}"
+    print(f"[fused combine] {entry}: 4 replays bitwise equal to eager")
