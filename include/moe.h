@@ -265,7 +265,9 @@ moe_status moe_pack_weights(int32_t dtype, int64_t n_mats, int32_t rows, int32_t
 /* Steps 1-5 for T tokens: moe_route, moe_dispatch, moe_expert_ffn on the
  * routed groups and (MOE_F_SHARED) on the shared experts, moe_combine.
  * Same kernels and order as the staged calls, so the outputs are bitwise
- * equal to the staged path.  out [T][H] (act).  Without MOE_F_SHARED the
+ * equal to the staged path (with MOE_F_FUSED_COMBINE the combine runs in
+ * the down projection's tail instead, with the same arithmetic: still
+ * bitwise equal).  out [T][H] (act).  Without MOE_F_SHARED the
  * output is this GPU's partial sum over its local pairs. */
 moe_status moe_layer_forward(const moe_shape *shape, const moe_weights *weights,
                              const moe_slot_map *map, int32_t T, const void *h, void *out,
