@@ -442,7 +442,8 @@ def test_layer_at_maximum_tokens():
     decode workload (32 local slots of 256 experts, top-8) and H = I = 128:
     the tiled router, top-K over a million tokens, dispatch through the
     single-block scan, groups of ~32 K rows in the tiled expert GEMMs and a
-    million-block combine.  Routing of a sample and the whole dispatch
+    million-block combine (and the same combine in the down projection's
+    tail, MOE_F_FUSED_COMBINE, bitwise equal).  Routing of a sample and the whole dispatch
     exact, layer outputs on the sample within the output bar."""
     cfg = moe_synth.scaled_config(2, T=1 << 20, H=128, I=128, seed=64)
     print(f"[case] maximum tokens T={cfg.T} H={cfg.H} I={cfg.I}", flush=True)
@@ -450,6 +451,10 @@ def test_layer_at_maximum_tokens():
     st = gh.gpu_stages(L)
     out = gh.gpu_forward(L).cpu().numpy()
     assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8))
+    # the combine in the down projection's tail: thousands of completed
+    # (token, tile)s per workgroup, many rounds of tokens with no local pair
+    fused = gh.gpu_forward(L, fused_combine=True).cpu().numpy()
+    assert np.array_equal(fused.view(np.uint8), out.view(np.uint8))
     tok = np.sort(np.random.default_rng(64).choice(cfg.T, 64, replace=False))
     tie = _check_routing(L, st, tokens=tok)
     _check_dispatch(L, st)
