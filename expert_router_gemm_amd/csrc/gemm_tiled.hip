@@ -484,6 +484,7 @@ __device__ __forceinline__ f16x8 ldg16(const f16 *p) { return *reinterpret_cast<
 template <int TBM>
 __device__ void comb_tail(const StreamArgs &a, const ItemSeq &seq, const int *tstart, int n_groups,
                           int n_ntiles, f16 *lds) {
+    static_assert(TBM == 256 && kThreads == 512, "one row of two items per thread");
     const CombineArgs &c = a.comb;
     const int tid = threadIdx.x;
     const int K = c.K, H = a.N, T = c.T, nft = n_ntiles;
@@ -625,7 +626,7 @@ __device__ void comb_tail(const StreamArgs &a, const ItemSeq &seq, const int *ts
                 const int r0 = a.offsets ? a.offsets[g] : g * a.rows_per_group;
                 const int r1 = a.offsets ? a.offsets[g + 1] : r0 + a.rows_per_group;
                 const int r = r0 + mt * TBM + (tid & 255);
-                if (TBM == 256 && r < r1) {
+                if (r < r1) {
                     row[q] = r;
                     ft[q] = nt;
                 }
@@ -648,6 +649,9 @@ __device__ void comb_tail(const StreamArgs &a, const ItemSeq &seq, const int *ts
             if (tk[q] >= 0 && left[q] == 1) list[atomicAdd(&nlist, 1)] = tk[q];
         __syncthreads();
         const int n = nlist;
+        // every thread has its n before any appends again: all take the
+        // same branch (flush holds barriers)
+        __syncthreads();
         if (n >= kCombSub) {  // a full pass is pending: sum it now
             flush(n);
             if (tid == 0) nlist = 0;
