@@ -331,7 +331,60 @@ def time_workload(ctx, K: int, warmup: int, references: bool = True):
     torch.cuda.synchronize()
     r["staged_ms"] = e0.elapsed_time(e1) / K
     r["same"] = bool(torch.equal(ctx["b"]["out"], ctx["b"]["out2"]))
+    r["step_dist"] = step_distribution(ctx, K)
     return r
+
+
+def percentiles(v):
+    """median, p10 and p90 (nearest rank) of a list of step times."""
+    v = sorted(v)
+
+    def rank(q):
+        return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {"median": round(statistics.median(v), 4), "p10": round(rank(0.1), 4),
+            "p90": round(rank(0.9), 4), "n": len(v)}
+
+
+def step_distribution(ctx, K: int):
+    """Per-step times of moe_layer_forward: K passes with an event between
+    consecutive passes on the launch stream (each record costs the stream a
+    few µs, so the mean here sits a little above the timed region's)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    ev[0].record()
+    for i in range(K):
+        fused_step(ctx)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return percentiles([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])
+
+
+def vendor_reference(reps: int = 20):
+    """What the vendor's own kernels reach on this GPU, beside the published
+    peaks the fractions use: torch's device copy (read + write) and sum
+    (read only) over 2 GiB of fp16, and torch.mm on an 8192^3 fp16 product
+    (hipBLASLt).  Context for roofline.frac, not a ceiling (the expert
+    weight stream moves HBM faster than the first two); not part of the
+    layer."""
+    import torch
+    n = 1 << 30  # fp16 elements: 2 GiB
+    x = torch.ones(n, device="cuda:0", dtype=torch.float16)
+    y = torch.empty_like(x)
+    cp = _timed(lambda: y.copy_(x), 0, reps)
+    rd = _timed(lambda: x.sum(dtype=torch.float32), 0, reps)
+    del x, y
+    torch.cuda.empty_cache()
+    nbytes = 2 * n
+    hbm = {"copy_gbs": round(2 * nbytes / (cp["us"] / 1e6) / 1e9, 1),
+           "read_gbs": round(nbytes / (rd["us"] / 1e6) / 1e9, 1),
+           "kernels": "torch copy_ (2 GiB read + 2 GiB written) and sum (2 GiB read), fp16"}
+    a = torch.randn(8192, 8192, device="cuda:0", dtype=torch.float16)
+    b = torch.randn(8192, 8192, device="cuda:0", dtype=torch.float16)
+    mm = _timed(lambda: torch.mm(a, b), 2 * 8192 ** 3, reps)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm": hbm, "mfma": {"tflops": mm["tflops"], "kernel": "torch.mm fp16 8192^3"},
+            "published": {"hbm_gbs": HBM_PEAK_GBS, "mfma_f16_tflops": MFMA_F16_PEAK_TFLOPS}}
 
 
 def kernel_roofline(cfg, work, up_ms, workload_kind):
@@ -366,6 +419,8 @@ def layer_record(work, t):
         rec.update(no_events_ms=round(t["plain_ms"], 4), staged_calls_ms=round(t["staged_ms"], 4),
                    staged_equals_fused=t["same"],
                    stage_ms={k: round(v, 4) for k, v in t["stage_ms"].items()})
+    if "step_dist" in t:
+        rec["step_ms"] = t["step_dist"]  # moe_layer_forward, one event per step boundary
     return rec
 
 
@@ -770,6 +825,7 @@ def prefill_record(K: int, warmup: int, w_layout: str = "frag", fused_combine: b
                 fused_combine=fused_combine)
     cfg = ctx["cfg"]
     t = time_workload(ctx, K, warmup, references=False)
+    t["step_dist"] = step_distribution(ctx, K)
     prof_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     profiled_step(ctx, moe.make_profile(prof_ev))
     torch.cuda.synchronize()
@@ -842,6 +898,8 @@ def main():
                     help="only time torch's fp16 GEMMs on the prefill expert shapes")
     ap.add_argument("--w-layout", choices=["frag", "rowmajor"], default="frag",
                     help="expert weight layout: the fragment layout (default) or row-major")
+    ap.add_argument("--no-vendor-reference", action="store_true",
+                    help="skip timing the vendor copy, sum and GEMM beside the published peaks")
     ap.add_argument("--fused-combine", action="store_true",
                     help="set MOE_F_FUSED_COMBINE: the combine in the tiled down projection's "
                          "tail (prefill batches) instead of its own launch")
@@ -940,6 +998,11 @@ def main():
                                         args.fused_combine)
         log(f"[bench] prefill {rec['prefill']['workload']}: {rec['prefill']['value']:.0f} "
             f"tokens/s, gate/up {rec['prefill']['roofline']['achieved']} TFLOP/s")
+    if not args.no_vendor_reference:
+        rec["vendor_reference"] = vendor_reference()
+        a = rec["vendor_reference"]
+        log(f"[bench] vendor kernels: copy {a['hbm']['copy_gbs']} GB/s, sum {a['hbm']['read_gbs']} "
+            f"GB/s, fp16 GEMM {a['mfma']['tflops']} TFLOP/s")
     print(json.dumps(rec))
     return 0
 

@@ -221,3 +221,11 @@ def test_trace_summary_splits_the_prefill_leg(tmp_path):
     assert ("stream_gemm_kernel gate/up", (32, 2, 2)) in main
     pre = [k["kernel"] for k in out["prefill"]]
     assert pre == ["tiled_gemm_kernel gate/up (256-row tiles)", "tiled_gemm_kernel router (128-row tiles)"]
+
+
+def test_step_percentiles_nearest_rank():
+    p = bench.percentiles([float(v) for v in range(10, 0, -1)])  # order does not matter
+    assert p == {"median": 5.5, "p10": 2.0, "p90": 9.0, "n": 10}
+    assert bench.percentiles([3.0]) == {"median": 3.0, "p10": 3.0, "p90": 3.0, "n": 1}
+    q = bench.percentiles([1.0, 100.0, 2.0])
+    assert q["p10"] == 1.0 and q["p90"] == 100.0 and q["median"] == 2.0
