@@ -698,6 +698,28 @@ def summarize_pmc_all(fetch_dir: str, write_dir: str, workload: str, copy_bytes:
     print(json.dumps(rec, indent=2))
 
 
+def summarize_counters(pmc_dir: str):
+    """Any rocprofv3 --pmc run: per libmoe kernel (kernel_label) and
+    counter, the median value per launch and the launch count.  Used for
+    the MFMA counters (MfmaFlopsF16 = SQ_INSTS_VALU_MFMA_MOPS_F16 x 512,
+    MfmaUtil), which check the FLOPs the GEMMs execute against the
+    algorithmic count."""
+    import csv
+    import collections
+    vals = collections.defaultdict(list)
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                lab = kernel_label(r.get("Kernel_Name", ""))
+                if lab:
+                    vals[(lab, r.get("Counter_Name", ""))].append(float(r["Counter_Value"]))
+    out = collections.defaultdict(dict)
+    for (lab, counter), v in sorted(vals.items()):
+        out[lab][counter] = {"median_per_launch": statistics.median(v), "launches": len(v)}
+    print(json.dumps(out, indent=1))
+    return dict(out)
+
+
 def summarize_trace(trace_dir: str):
     """Per-kernel launch statistics of a rocprofv3 --kernel-trace run of
     this script: libmoe kernels grouped by name and grid (the same kernel
@@ -890,6 +912,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="per-kernel launch statistics of a rocprofv3 --kernel-trace run")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="median per launch of every counter of a rocprofv3 --pmc run, per kernel")
     ap.add_argument("--summarize-pmc-all", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="per-kernel HBM traffic of every libmoe kernel of the two PMC runs")
     ap.add_argument("--eplb", action="store_true",
@@ -910,6 +934,9 @@ def main():
 
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return 0
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return 0
     if args.summarize_pmc_all:
         import moe_synth

@@ -229,3 +229,24 @@ def test_step_percentiles_nearest_rank():
     assert bench.percentiles([3.0]) == {"median": 3.0, "p10": 3.0, "p90": 3.0, "n": 1}
     q = bench.percentiles([1.0, 100.0, 2.0])
     assert q["p10"] == 1.0 and q["p90"] == 100.0 and q["median"] == 2.0
+
+
+def test_summarize_counters_groups_by_kernel_and_counter(tmp_path):
+    d = tmp_path / "pmc" / "host"
+    d.mkdir(parents=True)
+    rows = [("Kernel_Name", "Counter_Name", "Counter_Value")]
+    gate = TILED.format("256, 2, 1, true, true, false")
+    down = TILED.format("256, 1, 0, false, true, false")
+    for v in (10.0, 30.0, 20.0):
+        rows.append((gate, "MfmaFlopsF16", v))
+    rows.append((down, "MfmaFlopsF16", 5.0))
+    rows.append((down, "MfmaUtil", 40.0))
+    rows.append(("some_other_kernel", "MfmaFlopsF16", 99.0))
+    with open(d / "run_counter_collection.csv", "w") as f:
+        for r in rows:
+            f.write(",".join(f'"{x}"' for x in r) + "\n")
+    out = bench.summarize_counters(str(tmp_path / "pmc"))
+    g = out["tiled_gemm_kernel gate/up (256-row tiles)"]["MfmaFlopsF16"]
+    assert g == {"median_per_launch": 20.0, "launches": 3}
+    assert out["tiled_gemm_kernel down (256-row tiles)"]["MfmaUtil"]["median_per_launch"] == 40.0
+    assert all("other" not in k for k in out)
