@@ -359,13 +359,59 @@ def step_distribution(ctx, K: int):
     return percentiles([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])
 
 
-def vendor_reference(reps: int = 20):
-    """What the vendor's own kernels reach on this GPU, beside the published
-    peaks the fractions use: torch's device copy (read + write) and sum
-    (read only) over 2 GiB of fp16, and torch.mm on an 8192^3 fp16 product
-    (hipBLASLt).  Context for roofline.frac, not a ceiling (the expert
-    weight stream moves HBM faster than the first two); not part of the
-    layer."""
+def probe_read_rate(gib: int = 8, reps: int = 5):
+    """Best HBM read rate of libmoe_probe.so's slab reader (contiguous 1 KB
+    nontemporal wave loads, the decode weight stream's access pattern) over
+    a few launch shapes: the measured counterpart of the 8 TB/s peak."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "expert_router_gemm_amd", "libmoe_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.moe_probe_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    nbytes, slab = gib << 30, 1 << 20
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    shapes = [(b, u) for b in (1024, 2048, 4096) for u in (4, 8)]
+    out = torch.empty(max(b for b, _ in shapes) * 256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for blocks, unroll in shapes:
+        def launch():
+            rc = fn(buf.data_ptr(), nbytes, slab, blocks, unroll, out.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"moe_probe_read returned {rc}")
+        launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ms = []
+        for _ in range(reps):
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        gbs = nbytes / (min(ms) / 1e3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 1), "blocks": blocks, "unroll": unroll}
+    del buf, out
+    torch.cuda.empty_cache()
+    best.update(bytes=nbytes, slab=slab,
+                kernel="libmoe_probe.so read_slabs_kernel (best of blocks 1024/2048/4096 x 4/8 "
+                       "1 KB pieces in flight per wave)")
+    return best
+
+
+def reference_rates(reps: int = 20):
+    """Measured rates beside the published peaks the fractions use: the
+    HBM read probe (probe_read_rate), what the vendor's own kernels reach --
+    torch's device copy (read + write) and sum (read only) over 2 GiB of
+    fp16, torch.mm on an 8192^3 fp16 product (hipBLASLt).  Context for
+    roofline.frac; not part of the layer."""
     import torch
     n = 1 << 30  # fp16 elements: 2 GiB
     x = torch.ones(n, device="cuda:0", dtype=torch.float16)
@@ -383,7 +429,8 @@ def vendor_reference(reps: int = 20):
     mm = _timed(lambda: torch.mm(a, b), 2 * 8192 ** 3, reps)
     del a, b
     torch.cuda.empty_cache()
-    return {"hbm": hbm, "mfma": {"tflops": mm["tflops"], "kernel": "torch.mm fp16 8192^3"},
+    return {"hbm": hbm, "hbm_read_probe": probe_read_rate(),
+            "mfma": {"tflops": mm["tflops"], "kernel": "torch.mm fp16 8192^3"},
             "published": {"hbm_gbs": HBM_PEAK_GBS, "mfma_f16_tflops": MFMA_F16_PEAK_TFLOPS}}
 
 
@@ -922,8 +969,9 @@ def main():
                     help="only time torch's fp16 GEMMs on the prefill expert shapes")
     ap.add_argument("--w-layout", choices=["frag", "rowmajor"], default="frag",
                     help="expert weight layout: the fragment layout (default) or row-major")
-    ap.add_argument("--no-vendor-reference", action="store_true",
-                    help="skip timing the vendor copy, sum and GEMM beside the published peaks")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the read probe and the vendor copy, sum and GEMM timed beside "
+                         "the published peaks")
     ap.add_argument("--fused-combine", action="store_true",
                     help="set MOE_F_FUSED_COMBINE: the combine in the tiled down projection's "
                          "tail (prefill batches) instead of its own launch")
@@ -1025,11 +1073,13 @@ def main():
                                         args.fused_combine)
         log(f"[bench] prefill {rec['prefill']['workload']}: {rec['prefill']['value']:.0f} "
             f"tokens/s, gate/up {rec['prefill']['roofline']['achieved']} TFLOP/s")
-    if not args.no_vendor_reference:
-        rec["vendor_reference"] = vendor_reference()
-        a = rec["vendor_reference"]
+    if not args.no_reference:
+        rec["reference"] = reference_rates()
+        a = rec["reference"]
+        probe = a["hbm_read_probe"]
         log(f"[bench] vendor kernels: copy {a['hbm']['copy_gbs']} GB/s, sum {a['hbm']['read_gbs']} "
-            f"GB/s, fp16 GEMM {a['mfma']['tflops']} TFLOP/s")
+            f"GB/s, fp16 GEMM {a['mfma']['tflops']} TFLOP/s; read probe "
+            f"{probe['gbs'] if probe else 'not built'} GB/s")
     print(json.dumps(rec))
     return 0
 

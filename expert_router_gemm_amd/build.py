@@ -74,6 +74,26 @@ def build(verbose: bool = False, out: str = None, defines=(), build_dir: str = N
     return lib
 
 
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """libmoe_probe.so: the HBM read-rate probe the benchmark reports beside
+    the published peak (csrc/probe_read.hip; not part of libmoe)."""
+    os.makedirs(BUILD, exist_ok=True)
+    obj = _compile("probe_read.hip", BUILD, [])
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)
     sys.exit(0)

@@ -4,6 +4,7 @@ summary's calibration arithmetic, and the decode workload's algorithmic
 bytes against the EP blog's per-expert figure (section 6.3: 88 MB per
 expert = 3 matrices of 7168 x 2048 fp16)."""
 import json
+import os
 
 import numpy as np
 import pytest
@@ -250,3 +251,22 @@ def test_summarize_counters_groups_by_kernel_and_counter(tmp_path):
     assert g == {"median_per_launch": 20.0, "launches": 3}
     assert out["tiled_gemm_kernel down (256-row tiles)"]["MfmaUtil"]["median_per_launch"] == 40.0
     assert all("other" not in k for k in out)
+
+
+def test_read_probe_library_validates_before_launch():
+    """libmoe_probe.so (built by build()): bad arguments return -1 and
+    launch nothing (no device needed)."""
+    import ctypes
+    path = os.path.join(bench.ROOT, "expert_router_gemm_amd", "libmoe_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libmoe_probe.so not built")
+    fn = ctypes.CDLL(path).moe_probe_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    fake = 0x100000
+    good = dict(buf=fake, nbytes=1 << 20, slab=1 << 16, blocks=4, unroll=8, out=fake)
+    for bad in (dict(buf=None), dict(out=None), dict(blocks=0), dict(unroll=3), dict(slab=1000),
+                dict(slab=3 << 10), dict(nbytes=(1 << 20) + 1024)):
+        a = dict(good, **bad)
+        assert fn(a["buf"], a["nbytes"], a["slab"], a["blocks"], a["unroll"], a["out"], None) == -1
