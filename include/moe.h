@@ -297,7 +297,7 @@ moe_status moe_layer_forward_profiled(const moe_shape *shape, const moe_weights 
  * process ends and looked up on the first call on each device.  Nothing is
  * allocated or freed.  Shapes whose moe_workspace_bytes(shape, T) exceeds
  * the array return MOE_ERR_WORKSPACE with nothing enqueued (64 MiB holds
- * DeepSeek-V3 decode batches up to 256 tokens: 39.5 MiB for one EP=8
+ * DeepSeek-V3 decode batches up to 256 tokens: 39.6 MiB for one EP=8
  * rank's 32 experts, 48.6 MiB for the whole layer with 2 shared experts).
  * Every call on one device uses the same array: calls that overlap on a
  * GPU (other streams, other threads) race and must be ordered by the
