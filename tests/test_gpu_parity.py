@@ -155,7 +155,7 @@ def _check_combine(L, st):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("seed_off", [0, 100])
+@pytest.mark.parametrize("seed_off", [0, 100, 200])
 def test_stages_and_layer_small(n, seed_off):
     cfg = small_cfg(n, seed=moe_synth.config(n).seed + seed_off)
     print(f"[case] workload {n} {cfg}", flush=True)
