@@ -89,8 +89,8 @@ typedef enum { MOE_F32 = 0, MOE_F16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
  * (agent-scope release, atomic decrement, acquire) sums the token's rows in
  * k order with the combine's arithmetic, so the output is bitwise the same.
  * Off by default: on MI355X at 16,384 tokens (EP=8 share) the layer takes
- * 2.00 ms with it against 1.71 ms with the separate combine -- the sums of
- * the last-completed tiles fall on the workgroups that finish last, while
+ * about 2.0 ms with it against 1.7 ms with the separate combine -- the sums
+ * of the last-completed tiles fall on the workgroups that finish last, while
  * the matrix cores idle.  Ignored by the staged entry points. */
 #define MOE_F_FUSED_COMBINE 2u
 
