@@ -827,6 +827,40 @@ def _timed(fn, flops, reps):
     return {"us": round(ms * 1e3, 1), "tflops": round(flops / (ms / 1e3) / 1e12, 1)}
 
 
+def tiled_equal_groups(G, M, H, I, T, K, E, reps=10):
+    """The library's own gate/up launch (moe_expert_ffn_up: the LDS-tiled
+    kernel, rows gathered from h, SwiGLU epilogue, fragment-layout weights)
+    on G equal groups of M rows -- the same flops and groups as the vendor
+    comparison, without the ragged tails of routed groups.  Random operands
+    (timing only)."""
+    import numpy as np
+    import torch
+
+    import expert_router_gemm_amd as moe
+    dev = "cuda:0"
+    torch.manual_seed(0)
+    rng = np.random.default_rng(0)
+    wg = moe.pack_weights((torch.randn(G, I, H, device=dev) * 0.02).half())
+    wu = moe.pack_weights((torch.randn(G, I, H, device=dev) * 0.02).half())
+    h = torch.randn(T, H, device=dev).half()
+    # each group gathers M distinct tokens in ascending order (as dispatch
+    # orders a slot's rows); perm codes t * K + k
+    gat = np.concatenate([np.sort(rng.choice(T, M, replace=False)) * K + (g % K)
+                          for g in range(G)]).astype(np.int32)
+    off = (np.arange(G + 1) * M).astype(np.int32)
+    gather, offsets = torch.from_numpy(gat).to(dev), torch.from_numpy(off).to(dev)
+    cap = T * K  # the layer's capacity (sizes the launch as in the layer)
+    hm = torch.empty(cap, I, dtype=torch.float16, device=dev)
+    shape = moe.make_shape(hidden=H, inter=I, n_experts=E, top_k=K, n_slots=G, act=moe.MOE_F16,
+                           w_layout=moe.MOE_W_FRAG)
+    r = _timed(lambda: moe.moe_expert_ffn_up(shape, G, cap, h, moe.MOE_F16, None,
+                                             moe.MOE_X_GATHER, gather, offsets, wg, wu, hm),
+               4 * G * M * H * I, reps)
+    del wg, wu, h, hm
+    torch.cuda.empty_cache()
+    return r
+
+
 def library_bmm(G, M, K, N, reps=10):
     """torch.bmm (hipBLASLt) fp16 on G groups of [M, K] x [K, N], contiguous."""
     import torch
@@ -916,14 +950,20 @@ def prefill_record(K: int, warmup: int, w_layout: str = "frag", fused_combine: b
     # multiple of 256 rows, the library's best case)
     G = cfg.E // cfg.ep_size  # local experts
     rows = -(-work["P"] // G)
-    vendor = {}
+    vendor, own = {}, {}
     for key, m in (("equal_groups", rows), ("aligned_groups", rows // 256 * 256)):
         if m <= 0:
             continue
         lib = library_bmm(G, m, cfg.H, 2 * cfg.I)
         vendor[key] = dict(lib, shape=f"{G} x [{m} x {cfg.H} @ {cfg.H} x {2 * cfg.I}]",
                            tiled_over_vendor=round(rec["roofline"]["achieved"] / lib["tflops"], 3))
+        # and this library's gate/up launch on the same equal groups
+        mine = tiled_equal_groups(G, m, cfg.H, cfg.I, cfg.T, cfg.K, cfg.E)
+        own[key] = dict(mine, shape=vendor[key]["shape"],
+                        frac_of_peak=round(mine["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                        over_vendor=round(mine["tflops"] / lib["tflops"], 3))
     rec["vendor_bmm_gate_up"] = vendor
+    rec["tiled_gate_up_equal_groups"] = own
     return rec
 
 
