@@ -107,3 +107,40 @@ def test_prefill_layer_repeats_bit_for_bit():
     for _ in range(4):
         again = gh.gpu_forward(L).cpu().numpy()
         assert np.array_equal(first.view(np.uint8), again.view(np.uint8))
+
+
+def test_tiled_more_groups_than_threads():
+    """1,024 expert slots, the most the tiled kernels take: every workgroup
+    builds its prefix of row tiles per group over two chunks of 512 groups
+    (one per thread), carrying the first chunk's total into the second.  A
+    full 1024-expert top-16 layer with a shared expert at T = 19200 (300
+    rows per slot on average, 124-517: one to three row tiles, most with a
+    tail), H = I = 128, on the
+    tiled router and expert GEMMs: routing on a token sample, the whole
+    dispatch, hm and y on rows covering every (slot, row tile), the combine
+    on every token, the layer on the sample against the oracle and equal to
+    the staged calls, with the combine as its own launch and in the down
+    projection's tail."""
+    import test_gpu_parity as tp
+    cfg = moe_synth.scaled_config(3, T=19200, H=128, I=128, E=1024, K=16, n_shared=1,
+                                  long_tail=False, seed=71)
+    print(f"[case] tiled, 1024 groups: {cfg}", flush=True)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    c = st["counts"]
+    assert len(c) == 1024 and c.min() < 256 < c.max(), "slots of one and of several row tiles"
+    rng = np.random.default_rng(cfg.seed)
+    tok = np.sort(rng.choice(cfg.T, 48, replace=False))
+    tie = tp._check_routing(L, st, tokens=tok)
+    tp._check_dispatch(L, st)
+    rows = tp._strata_rows(st["offsets"], rng)
+    dy = tp._check_ffn_rows(L, st, rows)
+    tp._check_combine(L, st)
+    out = gh.gpu_forward(L).cpu().numpy()
+    assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8)), "layer != staged"
+    fused = gh.gpu_forward(L, fused_combine=True).cpu().numpy()
+    assert np.array_equal(fused.view(np.uint8), out.view(np.uint8)), "fused combine differs"
+    ref = gh.oracle_forward(L, tokens=tok)
+    err = gh.assert_close(out[tok], ref["out"], "layer output (sample)", rows=~tie)
+    print(f"[tiled, 1024 groups] P={st['P']} rows/slot {int(st['counts'].min())}.."
+          f"{int(st['counts'].max())} ffn rows={len(rows)} (max |dy| {dy:.2e}) max|d|={err:.2e}")
