@@ -330,11 +330,14 @@ def test_maximum_experts_top_k_slots_and_shared():
     assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8))
 
 
-def test_single_expert_is_a_plain_swiglu_ffn():
+@pytest.mark.parametrize("T", [70, 40000])
+def test_single_expert_is_a_plain_swiglu_ffn(T):
     """E = K = S = 1: every token's gate is softmax over one logit = 1, so
     the layer is the textbook SwiGLU FFN y = W_d (SiLU(W_g h) * W_u h),
-    checked against torch on the CPU in float64."""
-    cfg = moe_synth.scaled_config(2, T=70, H=256, I=128, E=1, K=1, ep_size=1, seed=62)
+    checked against torch on the CPU in float64.  T = 70 runs the weight
+    stream; T = 40000 the tiled router (one valid logit column) and tiled
+    expert GEMMs on one group of 157 row tiles, split over the XCDs."""
+    cfg = moe_synth.scaled_config(2, T=T, H=256, I=128, E=1, K=1, ep_size=1, seed=62)
     L = gh.build_layer(cfg)
     out = gh.gpu_forward(L).cpu().numpy().astype(np.float64)
     g, u, d = (torch.from_numpy(m.astype(np.float64)) for m in L.expert(0))
