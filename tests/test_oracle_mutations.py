@@ -44,6 +44,14 @@ MUTANTS = {
     "group_tie_to_higher_id": ("if (bg < 0 || sc > bs)", "if (bg < 0 || sc >= bs)"),
     "group_score_first_expert": ("                            sc = l[e];", "                            sc = sc;"),
     "group_mask_wrong_group": ("if (!gsel[e / gs])", "if (!gsel[e % G])"),
+    "replica_mod_off_by_one": ("(uint64_t)n);", "(uint64_t)(n + 1));"),
+    "replica_hash_only_above_two": ("if (n > 1)", "if (n > 2)"),
+    "combine_weight_of_next_k": ("acc += (double)topk_w[(size_t)t * K + k] * (double)y[(size_t)r * H + o];",
+                                 "acc += (double)topk_w[(size_t)t * K + (k + 1) % K] * (double)y[(size_t)r * H + o];"),
+    "expert_input_wrong_token": ("            int t = pair[r] / K;\n            if (d->fp8_dispatch) {",
+                                 "            int t = pair[r] % K;\n            if (d->fp8_dispatch) {"),
+    "dispatch_offsets_skip_first_slot": ("offsets[s + 1] = offsets[s] + counts[s];",
+                                         "offsets[s + 1] = offsets[s] + (s ? counts[s] : 0);"),
     "combine_skips_last_k": ("            for (int k = 0; k < K; ++k) {\n                int r = inv_pos",
                              "            for (int k = 0; k < K - 1; ++k) {\n                int r = inv_pos"),
 }
