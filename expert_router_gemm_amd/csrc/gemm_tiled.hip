@@ -767,40 +767,51 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(StreamArgs a, int 
     }
 }
 
+// Per kernel and device, once: allow the kernel's dynamic LDS size and
+// count the workgroups that are resident at once (cached; a race only
+// repeats the queries; the release store orders the attribute call before
+// any thread that reads the cached count launches).
+template <int TBM, int NM, int EPI, bool GATHER, bool FR, bool CB>
+hipError_t resident_slots(int dev, int &slots) {
+    static std::atomic<int> resident[kMaxDevices];
+    slots = dev < kMaxDevices ? resident[dev].load(std::memory_order_acquire) : 0;
+    if (slots > 0) return hipSuccess;
+    const size_t lds = tile_lds_bytes<TBM>();
+    hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR, CB>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int cus = 256, per_cu = 1;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR, CB>, kThreads, lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    slots = cus * per_cu;
+    if (dev < kMaxDevices) resident[dev].store(slots, std::memory_order_release);
+    return hipSuccess;
+}
+
+int current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    return dev;
+}
+
 // max_tiles bounds the 128-row tiles (so also the taller ones): it only
 // sizes the grid, surplus workgroups find no item and exit.
 template <int TBM, int NM, int EPI, bool GATHER, bool FR, bool CB = false>
 hipError_t launch_t(const StreamArgs &a, int n_groups, long max_tiles, hipStream_t s) {
     if (n_groups <= 0 || n_groups > kMaxGroups) return hipErrorInvalidValue;
     const int n_ntiles = (a.N + WR / NM - 1) / (WR / NM);
-    const size_t lds = tile_lds_bytes<TBM>();
-    // Per device, once: allow the dynamic LDS size and count the workgroups
-    // that are resident at once (cached; a race only repeats the queries; the
-    // release store orders the attribute call before any thread that reads
-    // the cached count launches).
-    static std::atomic<int> resident[kMaxDevices];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-    int slots = dev < kMaxDevices ? resident[dev].load(std::memory_order_acquire) : 0;
-    if (slots <= 0) {
-        hipError_t e = hipFuncSetAttribute((const void *)tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR, CB>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        int cus = 256, per_cu = 1;
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR, CB>, kThreads, lds) != hipSuccess ||
-            per_cu < 1)
-            per_cu = 1;
-        slots = cus * per_cu;
-        if (dev < kMaxDevices) resident[dev].store(slots, std::memory_order_release);
-    }
+    int slots = 0;
+    const hipError_t e = resident_slots<TBM, NM, EPI, GATHER, FR, CB>(current_device(), slots);
+    if (e != hipSuccess) return e;
     // every resident workgroup slot, never more than the items
     long grid = slots;
     const long items = max_tiles * n_ntiles * (EPI == 2 ? a.ksplit : 1);
     if (items < grid) grid = items > 0 ? items : 1;
     hipLaunchKernelGGL((tiled_gemm_kernel<TBM, NM, EPI, GATHER, FR, CB>), dim3((unsigned)grid), dim3(kThreads),
-                       lds, s, a, n_ntiles, n_groups);
+                       tile_lds_bytes<TBM>(), s, a, n_ntiles, n_groups);
     return hipGetLastError();
 }
 
@@ -813,6 +824,30 @@ bool tiled_gemm_supported_shape(int K, int dtype, int x_dtype) {
 bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype) {
     return a.ksplit >= 1 && a.K % (2 * BK * a.ksplit) == 0 && a.n_sec == 0 &&
            tiled_gemm_supported_shape(a.K, dtype, x_dtype);
+}
+
+hipError_t tiled_gemm_prepare() {
+    static std::atomic<bool> ready[kMaxDevices];
+    const int dev = current_device();
+    if (dev < kMaxDevices && ready[dev].load(std::memory_order_acquire)) return hipSuccess;
+    constexpr int XB = kExpertRows;
+    int n = 0;
+    hipError_t e = hipSuccess;
+    // every kernel launch_tiled_gemm can pick
+    auto step = [&](hipError_t r) {
+        if (e == hipSuccess) e = r;
+    };
+    step(resident_slots<XB, 2, 1, true, true, false>(dev, n));
+    step(resident_slots<XB, 2, 1, false, true, false>(dev, n));
+    step(resident_slots<XB, 2, 1, true, false, false>(dev, n));
+    step(resident_slots<XB, 2, 1, false, false, false>(dev, n));
+    step(resident_slots<XB, 1, 0, false, true, true>(dev, n));
+    step(resident_slots<XB, 1, 0, false, false, true>(dev, n));
+    step(resident_slots<XB, 1, 0, false, true, false>(dev, n));
+    step(resident_slots<XB, 1, 0, false, false, false>(dev, n));
+    step(resident_slots<kTiledRouterRows, 1, 2, false, false, false>(dev, n));
+    if (e == hipSuccess && dev < kMaxDevices) ready[dev].store(true, std::memory_order_release);
+    return e;
 }
 
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,

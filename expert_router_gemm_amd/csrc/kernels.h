@@ -88,6 +88,11 @@ bool tiled_gemm_supported(const StreamArgs &a, int dtype, int x_dtype);
 bool tiled_gemm_supported_shape(int K, int dtype, int x_dtype);
 hipError_t launch_tiled_gemm(const StreamArgs &a, int mode, int n_groups, long max_tiles,
                              hipStream_t s);
+// Sets up every tiled kernel on the current device (dynamic LDS limit,
+// resident workgroup count), once per device; later calls return at once.
+// Not a stream operation: the entry points call it before enqueueing, so
+// their first call on a device sets the state that captured calls use.
+hipError_t tiled_gemm_prepare();
 
 // ---------------------------------------------------------------- routing
 // Partial logits parts[z][T][ld] fp32, z < nsplit (E expert columns, then

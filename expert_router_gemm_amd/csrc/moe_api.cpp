@@ -127,9 +127,12 @@ moe_status need4_opt(const void *p) { return (p && ((uintptr_t)p & 3u)) ? MOE_ER
         if ((x) != hipSuccess) return MOE_ERR_LAUNCH; \
     } while (0)
 
+// A current device, with the tiled kernels set up on it (once per device:
+// every later call, also under graph capture, only reads that state).
 moe_status device_ok() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_NO_DEVICE;
+    if (tiled_gemm_prepare() != hipSuccess) return MOE_ERR_LAUNCH;
     return MOE_OK;
 }
 

@@ -17,12 +17,13 @@
  *   - Pointers are DEVICE memory unless marked (host).  The caller allocates
  *     and owns every buffer; the library never allocates, frees or
  *     synchronises.  State it keeps across calls, per device: the number of
- *     resident workgroups of each LDS-tiled GEMM kernel (counted, after
- *     raising the kernel's dynamic LDS limit with hipFuncSetAttribute, on
- *     the first launch of that kernel on the device; later calls read it),
- *     and the device address of moe_layer_forward_noalloc's static
- *     workspace array.  Both are set up race-free; every entry point may be
- *     called from several host threads.
+ *     resident workgroups of each LDS-tiled GEMM kernel (counted for every
+ *     such kernel at once, after raising its dynamic LDS limit with
+ *     hipFuncSetAttribute, on the first call of any entry point on the
+ *     device; later calls read it), and the device address of
+ *     moe_layer_forward_noalloc's static workspace array (looked up on that
+ *     entry point's first call on the device).  Both are set up race-free;
+ *     every entry point may be called from several host threads.
  *   - Matrices are row-major and "out-major": a weight that maps an input of
  *     length n to m outputs is stored [m][n], i.e. the transpose of the
  *     page's [in, out] math shapes (router [7168, 256], gate/up
@@ -36,8 +37,9 @@
  *     enqueues work on it and returns; outputs are valid once the stream
  *     reaches that point.  The work is kernel launches only (no copy,
  *     memset, allocation or synchronisation), so calls may be captured
- *     into a HIP graph and replayed (after one eager call per device, which
- *     sets up the per-device state below).
+ *     into a HIP graph and replayed, after one eager call per device that
+ *     sets up the per-device state above (any entry point; for
+ *     moe_layer_forward_noalloc, that entry point itself).
  *   - Return value: a synchronous status from host-side validation (shapes,
  *     NULL pointers, alignment, dtype combinations, workspace size), or
  *     MOE_ERR_LAUNCH if a kernel launch was rejected.  Nothing is enqueued
