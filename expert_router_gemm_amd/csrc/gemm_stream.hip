@@ -364,6 +364,12 @@ hipError_t launch_t(const StreamArgs &a, int n_groups, int zblocks, hipStream_t 
 
 }  // namespace
 
+bool stream_gemm_same_kernel(int dtype, int mode, long est_a, long est_b) {
+    // only the fp16 down projection picks its shape from the estimate
+    if (dtype != DT_F16 || mode != STREAM_STORE) return true;
+    return (est_a >= kStoreWideRows) == (est_b >= kStoreWideRows);
+}
+
 hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int mode,
                               int n_groups, int zblocks, long est_rows, hipStream_t s) {
     if (n_groups + a.n_sec <= 0 || zblocks <= 0) return hipSuccess;

@@ -79,6 +79,9 @@ __host__ __device__ inline size_t frag_offset(size_t n, size_t b, size_t row_byt
 // est_rows: expected rows per group (host estimate), picks the kernel shape.
 hipError_t launch_stream_gemm(const StreamArgs &a, int dtype, int x_dtype, int mode,
                               int n_groups, int zblocks, long est_rows, hipStream_t s);
+// Whether launch_stream_gemm picks the same kernel (so the same summation
+// order) for expected group sizes est_a and est_b.
+bool stream_gemm_same_kernel(int dtype, int mode, long est_a, long est_b);
 
 // LDS-tiled persistent variant for groups of many rows (fp16 only; K split
 // for router logits).  max_tiles bounds the total 128-row tiles (sizes the

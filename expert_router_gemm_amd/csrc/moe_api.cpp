@@ -670,9 +670,12 @@ moe_status layer_forward_run(const moe_shape *shape, const moe_weights *w,
     const long cap_sh = (long)s.n_shared * T;
     const long est_sh = est_group_rows(s, cap_sh);
     // The shared experts (every token, Step 5) ride in the routed launches as
-    // secondary groups when both stream their weights; rows cap.. of hm/y.
+    // secondary groups when both stream their weights with the kernels the
+    // separate calls would pick for each (so the sums, and the output, are
+    // bitwise those of the staged calls); rows cap.. of hm/y.
     const bool merged = gate && !copy_rows && !fuse && !use_tiled(est, s.hidden, s.act, s.act) &&
-                        !use_tiled(est_sh, s.hidden, s.act, s.act);
+                        !use_tiled(est_sh, s.hidden, s.act, s.act) &&
+                        stream_gemm_same_kernel(s.act, STREAM_STORE, est, est_sh);
     if (merged) {
         Secondary up_sec, down_sec;
         up_sec.n = down_sec.n = s.n_shared;

@@ -346,6 +346,31 @@ def test_single_expert_is_a_plain_swiglu_ffn(T):
     gh.assert_close(out, ref.numpy(), "single-expert layer")
 
 
+@pytest.mark.parametrize("T,H,E,K,n_shared,groups", [
+    (500, 128, 256, 12, 1, (2, 1)),
+    (33, 256, 8, 5, 1, None),
+    (64, 256, 16, 13, 2, None),
+])
+def test_layer_equals_staged_when_shared_and_routed_sizes_differ(T, H, E, K, n_shared, groups):
+    """Decode-sized full layers whose routed groups expect 12 or more rows
+    and whose shared experts, estimated as n_shared * T / E rows, fewer:
+    the two sides of the size at which the down projection's weight stream
+    changes shape (inter 512, where the two shapes sum K in different
+    orders).  The layer must equal the staged calls bit for bit (it runs
+    the shared experts in their own launches here instead of inside the
+    routed ones) and the oracle within the bar."""
+    kw = dict(n_groups=groups[0], topk_groups=groups[1]) if groups else {}
+    cfg = moe_synth.scaled_config(3, T=T, H=H, I=512, E=E, K=K, n_shared=n_shared, ep_size=1,
+                                  long_tail=False, seed=64 + T, **kw)
+    L = gh.build_layer(cfg)
+    st = gh.gpu_stages(L)
+    tie = _check_routing(L, st)
+    out = gh.gpu_forward(L).cpu().numpy()
+    assert np.array_equal(out.view(np.uint8), st["out"].view(np.uint8)), "layer != staged"
+    ref = gh.oracle_forward(L)
+    gh.assert_close(out, ref["out"], "layer output", rows=~tie)
+
+
 @pytest.mark.parametrize("groups", [None, (10, 3)])
 def test_expert_count_not_a_multiple_of_the_wave(groups):
     """E = 100 (lanes past E hold no expert in the top-K kernel), K = 5, full
