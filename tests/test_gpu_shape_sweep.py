@@ -38,7 +38,7 @@ def _shapes(n=16, seed=2024):
         ep = int(rng.choice([d for d in (1, 2, 4, 8) if E % d == 0]))
         cfg = moe_synth.config(
             2, name=f"sweep{i}", T=int(rng.choice([1, 5, 64, 130, 300])),
-            H=128 * int(rng.integers(1, 6)), I=128 * int(rng.integers(1, 4)), E=E,
+            H=128 * int(rng.integers(1, 6)), I=128 * int(rng.integers(1, 5)), E=E,
             K=int(rng.integers(1, min(E, 8) + 1)),
             n_shared=int(rng.choice([0, 1, 2])) if ep == 1 else 0, dtype=dtype,
             dispatch="fp8" if dtype == "f16" and rng.random() < 0.3 else "same",
