@@ -2,8 +2,9 @@
 layouts.
 
 Sixteen shapes drawn once from a fixed seed: hidden 128..640 and inter
-128..384 (multiples of 128, so 1-5 K tiles of the weight stream and 1-3
-gate/up feature tiles), 1..64 experts, top-k 1..8, full layer or a rank
+128..512 (multiples of 128, so 1-5 K tiles of the weight stream and 1-4
+gate/up feature tiles; inter 512 is where the down projection's weight
+stream can split K over the waves), 1..64 experts, top-k 1..8, full layer or a rank
 share of an EP group of 2, 4 or 8 (with or without a replica of a remote
 hot expert), shared experts on the full layer, fp32 / fp16, fp8 dispatch,
 long-tail bias, and 1..300 tokens.  Each shape runs the staged entry points
